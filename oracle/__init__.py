@@ -1,0 +1,170 @@
+"""Plain CPU oracle for the DSA path (lightning indexer -> top-k -> sparse MLA attention).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the CPU-baseline leg of
+the benchmark, never by the product library.  It shares no code with the HIP path; the arithmetic
+lives in ``dsa_oracle.c`` (plain C, built with gcc) and this module only marshals numpy arrays.
+
+Sources (web pages on DeepSeek-V3.2):
+  * velog summary "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models",
+    section 1.1 (lightning indexer equation for I_{t,s}, ReLU, FP8, previous tokens),
+    section 1.2 (top-k retrieval and u_t = Attn(h_t, {c_s})), section 1.3 (MQA mode: each
+    latent KV entry shared by all query heads), Continued Pre-Training stage 2 (k = 2048).
+  * notes.yuuk.io page of the same title, section "DeepSeek Sparse Attention (DSA)".
+
+``forward`` composes the three steps in the pages' order.  Every function is pinned by
+``tests/test_oracle_pins.py`` against closed forms, library routines, invariants and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile dsa_oracle.c with gcc into oracle/liboracle.so (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+        lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        lib.oracle_decode_e4m3.argtypes = [P, I64, P]
+        lib.oracle_decode_bf16.argtypes = [P, I64, P]
+        lib.oracle_dequant_e4m3.argtypes = [P, P, I64, I64, P]
+        lib.oracle_indexer.argtypes = [P, P, P, I64, P, I, I, P, I64, P]
+        lib.oracle_topk.argtypes = [P, I64, I64, P, I, P, P]
+        lib.oracle_sparse_attn.argtypes = [P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
+        lib.oracle_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def threads() -> int:
+    """Number of host threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
+
+
+def e4m3_to_f32(codes: np.ndarray) -> np.ndarray:
+    """Decode OCP e4m3fn byte codes to float32 (exact)."""
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float32)
+    _load().oracle_decode_e4m3(_p(codes), codes.size, _p(out))
+    return out
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 (exact)."""
+    bits = _c(bits, np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    _load().oracle_decode_bf16(_p(bits), bits.size, _p(out))
+    return out
+
+
+def dequant_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp32(e4m3(code) * scale) with one scale per leading-row: codes [..., C], scales [...]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    cols = codes.shape[-1]
+    rows = codes.size // cols
+    assert scales.size == rows, (scales.shape, codes.shape)
+    out = np.empty(codes.shape, np.float32)
+    _load().oracle_dequant_e4m3(_p(codes), _p(scales), rows, cols, _p(out))
+    return out
+
+
+def indexer(q: np.ndarray, w: np.ndarray, k: np.ndarray, pos: np.ndarray, ld: int | None = None,
+            with_mag: bool = False):
+    """Index scores I[r, s] = sum_j w[r, j] * ReLU(q[r, j, :] . k[s, :]) for s <= pos[r].
+
+    q [R, H, d] float32, w [R, H] float32, k [S, d] float32, pos [R] int64.
+    Returns scores [R, ld] float32 with -inf where s > pos[r] (and mag [R, ld] if asked)."""
+    q = _c(q, np.float32)
+    w = _c(w, np.float32)
+    k = _c(k, np.float32)
+    pos = _c(pos, np.int64)
+    R, H, d = q.shape
+    assert w.shape == (R, H) and k.shape[1] == d and pos.shape == (R,)
+    assert R == 0 or pos.max() < k.shape[0]
+    if ld is None:
+        ld = int(pos.max()) + 1 if R else 1
+    scores = np.full((R, ld), -np.inf, np.float32)
+    mag = np.zeros((R, ld), np.float32) if with_mag else None
+    _load().oracle_indexer(_p(q), _p(w), _p(k), R, _p(pos), H, d, _p(scores), ld,
+                           _p(mag) if with_mag else None)
+    return (scores, mag) if with_mag else scores
+
+
+def topk(scores: np.ndarray, pos: np.ndarray, k: int):
+    """Per row: the k largest of scores[r, 0..pos[r]] (ties -> lower index), ascending, -1 padded.
+
+    Returns (idx [R, k] int32, kth [R] float32 = k-th largest score or -inf if <= k candidates)."""
+    scores = _c(scores, np.float32)
+    pos = _c(pos, np.int64)
+    R = scores.shape[0]
+    assert pos.shape == (R,) and (R == 0 or pos.max() < scores.shape[1])
+    idx = np.empty((R, k), np.int32)
+    kth = np.empty((R,), np.float32)
+    _load().oracle_topk(_p(scores), scores.shape[1], R, _p(pos), int(k), _p(idx), _p(kth))
+    return idx, kth
+
+
+def sparse_attn(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, d_v: int, sm_scale: float):
+    """MQA-mode attention over the selected latent rows (all in double).
+
+    q [R, H, d_qk] float32, kv [S, d_qk] float32 (shared by all heads), idx [R, k] int32 (-1 skipped).
+    Returns (out [R, H, d_v] float64, lse [R, H] float64)."""
+    q = _c(q, np.float32)
+    kv = _c(kv, np.float32)
+    idx = _c(idx, np.int32)
+    R, H, d_qk = q.shape
+    k = idx.shape[1]
+    assert idx.shape[0] == R and kv.shape[1] == d_qk and 0 < d_v <= d_qk
+    assert idx.size == 0 or idx.max() < kv.shape[0]
+    out = np.empty((R, H, d_v), np.float64)
+    lse = np.empty((R, H), np.float64)
+    _load().oracle_sparse_attn(_p(q), _p(kv), _p(idx), R, H, d_qk, d_v, k, float(sm_scale),
+                               _p(out), _p(lse))
+    return out, lse
+
+
+def forward(q_i: np.ndarray, w: np.ndarray, k_i: np.ndarray, q: np.ndarray, kv: np.ndarray,
+            pos: np.ndarray, k: int, d_v: int, sm_scale: float):
+    """The whole path for the query rows given by ``pos``: indexer -> top-k -> sparse attention.
+
+    q_i [R, H_I, d_I], w [R, H_I], k_i [S, d_I] fp32 (dequantised); q [R, H, d_qk], kv [S, d_qk] fp32.
+    Returns dict(scores, kth, idx, out, lse)."""
+    scores = indexer(q_i, w, k_i, pos)
+    idx, kth = topk(scores, pos, k)
+    out, lse = sparse_attn(q, kv, idx, d_v, sm_scale)
+    return dict(scores=scores, kth=kth, idx=idx, out=out, lse=lse)
