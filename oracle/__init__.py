@@ -54,7 +54,7 @@ def _load():
         lib.oracle_decode_e4m3.argtypes = [P, I64, P]
         lib.oracle_decode_bf16.argtypes = [P, I64, P]
         lib.oracle_dequant_e4m3.argtypes = [P, P, I64, I64, P]
-        lib.oracle_indexer.argtypes = [P, P, P, I64, P, I, I, P, I64, P]
+        lib.oracle_indexer.argtypes = [P, P, P, I64, P, I, I, P, I64, P, P]
         lib.oracle_topk.argtypes = [P, I64, I64, P, I, P, P]
         lib.oracle_sparse_attn.argtypes = [P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
         lib.oracle_threads.restype = I
@@ -108,7 +108,8 @@ def indexer(q: np.ndarray, w: np.ndarray, k: np.ndarray, pos: np.ndarray, ld: in
     """Index scores I[r, s] = sum_j w[r, j] * ReLU(q[r, j, :] . k[s, :]) for s <= pos[r].
 
     q [R, H, d] float32, w [R, H] float32, k [S, d] float32, pos [R] int64.
-    Returns scores [R, ld] float32 with -inf where s > pos[r] (and mag [R, ld] if asked)."""
+    Returns scores [R, ld] float32 with -inf where s > pos[r]; with_mag=True returns
+    (scores, mag, absmag): mag = sum_j |w| ReLU(q.k), absmag = sum_j |w| sum_i |q_i k_i|."""
     q = _c(q, np.float32)
     w = _c(w, np.float32)
     k = _c(k, np.float32)
@@ -120,9 +121,10 @@ def indexer(q: np.ndarray, w: np.ndarray, k: np.ndarray, pos: np.ndarray, ld: in
         ld = int(pos.max()) + 1 if R else 1
     scores = np.full((R, ld), -np.inf, np.float32)
     mag = np.zeros((R, ld), np.float32) if with_mag else None
+    absmag = np.zeros((R, ld), np.float32) if with_mag else None
     _load().oracle_indexer(_p(q), _p(w), _p(k), R, _p(pos), H, d, _p(scores), ld,
-                           _p(mag) if with_mag else None)
-    return (scores, mag) if with_mag else scores
+                           _p(mag) if with_mag else None, _p(absmag) if with_mag else None)
+    return (scores, mag, absmag) if with_mag else scores
 
 
 def topk(scores: np.ndarray, pos: np.ndarray, k: int):

@@ -98,26 +98,34 @@ int oracle_threads(void) {
  *   pos    [n_rows]         position of each query token; keys s = 0..pos[r] are scored
  *   scores [n_rows][ld]     out: I[r][s] for s <= pos[r] (fp32); other entries untouched
  *   mag    [n_rows][ld]     out (nullable): sum_j |w| * ReLU(q.k), the magnitude the sum is made of
+ *   absmag [n_rows][ld]     out (nullable): sum_j |w| * sum_i |q_i k_i|, the magnitude of every product
+ *                           (bounds the rounding of the dot products, which can cancel)
  * I = sum_j w_j * max(q_j . k, 0), with the dot and the head sum in double, one final fp32 rounding.
  */
 void oracle_indexer(const float* q, const float* w, const float* k, int64_t n_rows, const int64_t* pos,
-                    int H, int d, float* scores, int64_t ld, float* mag) {
+                    int H, int d, float* scores, int64_t ld, float* mag, float* absmag) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; r++) {
     const float* qr = q + r * (int64_t)H * d;
     const float* wr = w + r * (int64_t)H;
     for (int64_t s = 0; s <= pos[r]; s++) {
       const float* ks = k + s * (int64_t)d;
-      double acc = 0.0, amag = 0.0;
+      double acc = 0.0, amag = 0.0, pmag = 0.0;
       for (int j = 0; j < H; j++) {
-        double dot = 0.0;
-        for (int i = 0; i < d; i++) dot += (double)qr[j * d + i] * (double)ks[i];
+        double dot = 0.0, dabs = 0.0;
+        for (int i = 0; i < d; i++) {
+          double prod = (double)qr[j * d + i] * (double)ks[i];
+          dot += prod;
+          dabs += fabs(prod);
+        }
         double relu = dot > 0.0 ? dot : 0.0;
         acc += (double)wr[j] * relu;
         amag += fabs((double)wr[j]) * relu;
+        pmag += fabs((double)wr[j]) * dabs;
       }
       scores[r * ld + s] = (float)acc + 0.0f; /* + 0.0f maps -0 to +0 */
       if (mag) mag[r * ld + s] = (float)amag;
+      if (absmag) absmag[r * ld + s] = (float)pmag;
     }
   }
 }

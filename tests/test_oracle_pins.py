@@ -135,8 +135,14 @@ def test_indexer_invariants(orc):
     for r in range(R):
         assert np.all(np.isneginf(base[r, pos[r] + 1:])) and np.all(np.isfinite(base[r, : pos[r] + 1]))
     # mag bounds the score
-    sc, mag = orc.indexer(q, w, k, pos, ld=S, with_mag=True)
+    sc, mag, absmag = orc.indexer(q, w, k, pos, ld=S, with_mag=True)
     assert np.all(np.abs(sc[fin]) <= mag[fin] * (1 + 1e-6) + 1e-30)
+    assert np.all(mag[fin] <= absmag[fin] * (1 + 1e-6) + 1e-30)
+    # absmag is the same sum with |w| and |q_i k_i|: for non-negative inputs it equals the score
+    qa, ka, wa = np.abs(q), np.abs(k), np.abs(w)
+    sa, ma, aa = orc.indexer(qa, wa, ka, pos, ld=S, with_mag=True)
+    np.testing.assert_allclose(aa[fin], sa[fin], rtol=1e-6)
+    np.testing.assert_allclose(ma[fin], sa[fin], rtol=1e-6)
 
 
 def test_indexer_no_negative_zero(orc):
