@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one pass of the whole path over each workload the headline metric names:
+  * prefill, 1 sequence of 32768 tokens (all tokens are queries), indexer H_I=64 x d_I=128 in fp8,
+    top-2048 selection, sparse MLA (128 heads, 576/512) in bf16;
+  * decode, 64 sequences x one query against 131072 cached tokens, same shapes.
+Each workload runs its three stages (indexer -> top-k -> sparse attention) on one stream through the
+C ABI, with HIP events between the stages; inputs are generated on the GPU before the timed region.
+
+Prints ONE JSON line: value = prefill tokens/s at 32K (whole job, one GPU); decode queries/s, per-stage
+times and roofline fractions are in the same line.  The oracle (plain C on the host cores) is timed on a
+bounded sample of rows and extrapolated with the per-row work model.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense)
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+IDX_FLOP_PER_PAIR = 2 * 64 * 128          # one causal (query, key) pair: 64 heads x 128-dim dot
+ATT_FLOP_PER_ENTRY = 2 * 128 * (576 + 512)  # one selected entry: QK (576) and PV (512) for 128 heads
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-len", type=int, default=32768)
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-len", type=int, default=131072)
+    ap.add_argument("--k", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    return ap.parse_args()
+
+
+def causal_work(L: int, n_q: int, k: int):
+    """(indexer causal pairs, selected entries, score reads) for the last n_q queries of L tokens."""
+    pairs, entries = 0, 0
+    for t in range(L - n_q, L):
+        pairs += t + 1
+        entries += min(k, t + 1)
+    return pairs, entries
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    k = args.k
+    sm = 1.0 / math.sqrt(576)
+    result = {}
+
+    def timed(stages, steps):
+        """Run `stages` (list of (name, fn)) `steps` times with events between them; per-stage mean ms."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        acc = [0.0] * len(stages)
+        for _ in range(steps):
+            ev[0].record(stream)
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            for i in range(len(stages)):
+                acc[i] += ev[i].elapsed_time(ev[i + 1])
+        return {name: acc[i] / steps for i, (name, _) in enumerate(stages)}
+
+    # ------------------------------------------------------------------ prefill workload
+    pre = None
+    if args.only in (None, "prefill"):
+        L = args.prefill_len
+        print(f"[bench] generating prefill inputs L={L}", file=sys.stderr, flush=True)
+        x = synth.prefill(L, seed=0, device=dev, n_needles=256, needle_layout="random")
+        ld = ((L + 63) // 64) * 64
+        scores = torch.empty((1, L, ld), dtype=torch.float32, device=dev)
+        idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
+        out = torch.empty((1, L, 128, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16)
+        ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+        q8, qs, k8, ks, w = (x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None])
+        q, kv = x["q"][None], x["kv"][None]
+        pre_stages = [
+            ("indexer", lambda: dsa.indexer_scores(q8, qs, k8, ks, w, scores)),
+            ("topk", lambda: dsa.topk(scores, L, k, idx=idx)),
+            ("sparse_mla", lambda: dsa.sparse_mla_attn(q, kv, idx, 512, sm, out=out, lse=lse, workspace=ws)),
+        ]
+        pre = dict(L=L, stages=pre_stages, x=x, idx=idx, out=out, lse=lse)
+
+    # ------------------------------------------------------------------ decode workload
+    dec = None
+    if args.only in (None, "decode"):
+        B, S = args.decode_batch, args.decode_len
+        print(f"[bench] generating decode inputs B={B} S={S}", file=sys.stderr, flush=True)
+        y = synth.decode(B, S, seed=0, device=dev)
+        ld = ((S + 63) // 64) * 64
+        d_scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
+        d_idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+        d_out = torch.empty((B, 1, 128, 512), dtype=torch.bfloat16, device=dev)
+        d_lse = torch.empty((B, 1, 128), dtype=torch.float32, device=dev)
+        ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(B, 1, S, 128, 576, 512, k, dsa.DSA_BF16)
+        d_ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+        yq8, yqs, yk8, yks, yw = (y["q8"][:, None], y["q_scale"][:, None], y["k8"], y["k_scale"], y["w"][:, None])
+        yq, ykv = y["q"][:, None], y["kv"]
+        dec_stages = [
+            ("indexer", lambda: dsa.indexer_scores(yq8, yqs, yk8, yks, yw, d_scores)),
+            ("topk", lambda: dsa.topk(d_scores, S, k, idx=d_idx)),
+            ("sparse_mla", lambda: dsa.sparse_mla_attn(yq, ykv, d_idx, 512, sm, out=d_out, lse=d_lse, workspace=d_ws)),
+        ]
+        dec = dict(B=B, S=S, stages=dec_stages, y=y, idx=d_idx, out=d_out, lse=d_lse)
+
+    stages_all = (pre["stages"] if pre else []) + (dec["stages"] if dec else [])
+    names = [("prefill." if pre and i < 3 else "decode.") + n for i, (n, _) in enumerate(stages_all)]
+    stages_named = list(zip(names, [f for _, f in stages_all]))
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    timed(stages_named, max(args.warmup, 0)) if args.warmup > 0 else None
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    st = timed(stages_named, args.steps)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+
+    out = {"metric": "DSA prefill tokens/s at 32K ctx + decode queries/s at 128K ctx; % roofline",
+           "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(sum(st.values()), 4), "wall_ms_per_step": round(wall, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16",
+           "data": "synthetic (seeded; N(0,1) inputs, fp8 e4m3 indexer with amax scales, needles)",
+           "config": {"workload": ("prefill 1x32768 tokens (all queries) + decode 64x1 query over 131072 "
+                                   "cached tokens; H_I=64 d_I=128 fp8, k=2048, 128 heads d_qk=576 d_v=512 bf16")}}
+    rooflines = {}
+    if pre:
+        L = pre["L"]
+        pairs, entries = causal_work(L, L, k)
+        t_i, t_k, t_a = st["prefill.indexer"], st["prefill.topk"], st["prefill.sparse_mla"]
+        t_tot = t_i + t_k + t_a
+        idx_tf = pairs * IDX_FLOP_PER_PAIR / (t_i * 1e-3) / 1e12
+        tk_bytes = pairs * 4 + L * k * 4
+        tk_gbs = tk_bytes / (t_k * 1e-3) / 1e9
+        att_tf = entries * ATT_FLOP_PER_ENTRY / (t_a * 1e-3) / 1e12
+        roof_ms = (pairs * IDX_FLOP_PER_PAIR / (PEAK_FP8_TFLOPS * 1e12) + tk_bytes / (PEAK_HBM_GBS * 1e9)
+                   + entries * ATT_FLOP_PER_ENTRY / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
+        out["value"] = round(L / (t_tot * 1e-3), 1)
+        out["prefill"] = {"tokens_per_s": out["value"], "ms": round(t_tot, 4),
+                          "roofline_ms": round(roof_ms, 4), "frac_of_roofline": round(roof_ms / t_tot, 4),
+                          "stages_ms": {"indexer": round(t_i, 4), "topk": round(t_k, 4), "sparse_mla": round(t_a, 4)},
+                          "indexer": {"TFLOP/s": round(idx_tf, 1), "frac_fp8_peak": round(idx_tf / PEAK_FP8_TFLOPS, 4)},
+                          "topk": {"GB/s": round(tk_gbs, 1), "frac_hbm": round(tk_gbs / PEAK_HBM_GBS, 4)},
+                          "sparse_mla": {"TFLOP/s": round(att_tf, 1),
+                                         "frac_bf16_peak": round(att_tf / PEAK_BF16_TFLOPS, 4)}}
+        rooflines["prefill.indexer"] = (t_i, {"bound": "mfma", "achieved": round(idx_tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                              "unit": "TFLOP/s", "frac": round(idx_tf / PEAK_FP8_TFLOPS, 4),
+                                              "traffic": None})
+        rooflines["prefill.topk"] = (t_k, {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": PEAK_HBM_GBS,
+                                           "unit": "GB/s", "frac": round(tk_gbs / PEAK_HBM_GBS, 4), "traffic": None})
+        rooflines["prefill.sparse_mla"] = (t_a, {"bound": "mfma", "achieved": round(att_tf, 2),
+                                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                                 "frac": round(att_tf / PEAK_BF16_TFLOPS, 4), "traffic": None})
+    if dec:
+        B, S = dec["B"], dec["S"]
+        t_i, t_k, t_a = st["decode.indexer"], st["decode.topk"], st["decode.sparse_mla"]
+        t_tot = t_i + t_k + t_a
+        i_bytes = B * S * (128 + 4 + 4) + B * 64 * (128 + 8)
+        k_bytes = B * S * 4 + B * k * 4
+        a_bytes = B * k * 1152 + B * 128 * 576 * 2 + B * 128 * 512 * 2 + B * k * 4
+        roof_ms = (i_bytes + k_bytes + a_bytes) / (PEAK_HBM_GBS * 1e9) * 1e3
+        i_gbs = i_bytes / (t_i * 1e-3) / 1e9
+        a_gbs = a_bytes / (t_a * 1e-3) / 1e9
+        out["decode"] = {"queries_per_s": round(B / (t_tot * 1e-3), 1), "unit": "queries/s", "ms": round(t_tot, 4),
+                         "roofline_ms": round(roof_ms, 4), "frac_of_hbm_roofline": round(roof_ms / t_tot, 4),
+                         "stages_ms": {"indexer": round(t_i, 4), "topk": round(t_k, 4), "sparse_mla": round(t_a, 4)},
+                         "indexer": {"GB/s": round(i_gbs, 1), "frac_hbm": round(i_gbs / PEAK_HBM_GBS, 4)},
+                         "topk": {"GB/s": round(k_bytes / (t_k * 1e-3) / 1e9, 1)},
+                         "sparse_mla": {"GB/s": round(a_gbs, 1), "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4)}}
+        rooflines["decode.indexer"] = (t_i, {"bound": "hbm", "achieved": round(i_gbs, 1), "peak": PEAK_HBM_GBS,
+                                             "unit": "GB/s", "frac": round(i_gbs / PEAK_HBM_GBS, 4), "traffic": None})
+        if out["value"] is None:
+            out["value"] = out["decode"]["queries_per_s"]
+            out["unit"] = "queries/s"
+    # dominant kernel = the stage with the largest time in the step
+    dom = max(rooflines.items(), key=lambda kv: kv[1][0]) if rooflines else None
+    if dom:
+        out["roofline"] = dict(dom[1][1], kernel=dom[0])
+
+    # ------------------------------------------------------------------ CPU oracle baseline (bounded sample)
+    if not args.no_cpu_baseline and pre:
+        out["cpu_baseline"] = cpu_baseline_prefill(pre, k, sm)
+        if dec:
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, k, sm)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_prefill(pre, k, sm):
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_attention_13_amd import synth
+    L, x = pre["L"], pre["x"]
+    gen = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(k - 4, k + 4), np.arange(L - 8, L),
+                                     gen.choice(L, 40, replace=False)])).astype(np.int64)
+    rsel = torch.from_numpy(rows).to(x["q8"].device)
+    q_i = oracle.dequant_e4m3(synth.u8(x["q8"][rsel]), x["q_scale"][rsel].cpu().numpy())
+    w = x["w"][rsel].cpu().numpy()
+    k_i = oracle.dequant_e4m3(synth.u8(x["k8"]), x["k_scale"].cpu().numpy())
+    qb = oracle.bf16_to_f32(synth.bf16_bits(x["q"][rsel]))
+    kvb = oracle.bf16_to_f32(synth.bf16_bits(x["kv"]))
+    t0 = time.perf_counter()
+    oracle.forward(q_i, w, k_i, qb, kvb, rows, k, 512, sm)
+    t = time.perf_counter() - t0
+    work = lambda p: IDX_FLOP_PER_PAIR * (p + 1) + ATT_FLOP_PER_ENTRY * min(k, p + 1)
+    w_sample = sum(work(int(p)) for p in rows)
+    w_total = sum(work(p) for p in range(L))
+    full_s = t * w_total / w_sample
+    return {"value": round(L / full_s, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": (f"{len(rows)} of {L} query rows (first, around position k-1, last, uniform), "
+                       f"{t:.1f} s, extrapolated to all rows by the per-row work model"),
+            "sample_seconds": round(t, 2)}
+
+
+def cpu_baseline_decode(dec, k, sm):
+    import numpy as np
+
+    import oracle
+    from sparse_attention_13_amd import synth
+    y, S = dec["y"], dec["S"]
+    nb = 2
+    t_total = 0.0
+    for b in range(nb):
+        q_i = oracle.dequant_e4m3(synth.u8(y["q8"][b:b + 1]), y["q_scale"][b:b + 1].cpu().numpy())
+        k_i = oracle.dequant_e4m3(synth.u8(y["k8"][b]), y["k_scale"][b].cpu().numpy())
+        qb = oracle.bf16_to_f32(synth.bf16_bits(y["q"][b:b + 1]))
+        kvb = oracle.bf16_to_f32(synth.bf16_bits(y["kv"][b]))
+        t0 = time.perf_counter()
+        oracle.forward(q_i, y["w"][b:b + 1].cpu().numpy(), k_i, qb, kvb, np.array([S - 1], np.int64), k, 512, sm)
+        t_total += time.perf_counter() - t0
+    return {"value": round(nb / t_total, 4), "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{nb} of {dec['B']} sequences, full path, {t_total:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

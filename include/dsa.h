@@ -1,0 +1,162 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path on one AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps, each an entry point, plus two entry points that run all three:
+ *
+ *   1. dsa_indexer_scores   lightning-indexer scores   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s])
+ *   2. dsa_topk             per-query selection of the k keys with the largest I[t,:]
+ *   3. dsa_sparse_mla_attn  attention of every query head over the selected latent rows only,
+ *                           each latent row shared by all heads (MLA in MQA mode)
+ *   dsa_forward_prefill / dsa_forward_decode   1 -> 2 -> 3 on one stream
+ *
+ * Definitions: velog summary "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models",
+ * section 1.1 (the index score equation, ReLU, few FP8 indexer heads, scores against the preceding
+ * tokens), section 1.2 (top-k retrieval of key/value entries and u_t = Attn(h_t, {c_s})), section
+ * 1.3 (MQA mode, every latent KV entry shared by all query heads), Continued Pre-Training stage 2
+ * (2048 selected tokens per query); notes.yuuk.io page of the same title, section on DSA.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Sequences.  A call covers B independent sequences.  Each has n_kv visible tokens and carries its
+ *   last n_q tokens as queries: query t (0 <= t < n_q) sits at position pos_t = n_kv - n_q + t and
+ *   sees keys s = 0..pos_t (the causal domain includes the query's own token).  Decode is n_q = 1.
+ * Memory.  Every pointer is a device pointer unless stated otherwise; all tensors are dense,
+ *   row-major, with the batch as the outermost dimension.  The caller owns all memory; the library
+ *   never allocates, frees or synchronises.  Fast paths need 16-byte aligned base pointers.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *   enqueued asynchronously; a kernel fault surfaces at the caller's next synchronisation.
+ * Errors.  Arguments are validated before anything is enqueued; on failure nothing is enqueued
+ *   and a status other than DSA_OK is returned.  dsa_last_error() returns a text of the last
+ *   failure on the calling thread.  No C++ exception crosses the ABI.
+ * fp8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities).  Row scales must be finite and > 0.
+ * Threading.  All entry points are reentrant; the only mutable global state is the thread-local
+ *   error text.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, n_q > n_kv, bad leading dimension ... */
+  DSA_ERR_UNSUPPORTED = 2, /* valid arguments no kernel here implements (dtype / shape combination) */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned                          */
+  DSA_ERR_HIP = 4          /* the HIP runtime refused a launch                                    */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,      /* IEEE binary32                                   */
+  DSA_BF16 = 1,     /* bfloat16                                        */
+  DSA_FP8_E4M3 = 2  /* OCP e4m3fn codes (uint8) with fp32 row scales   */
+} dsa_dtype_t;
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int dsa_version(void);
+
+/* Constant text for a status code (never NULL). */
+const char* dsa_status_string(dsa_status_t status);
+
+/* Text describing the last failure on the calling thread ("" if none).  Valid until the next call
+ * into the library from the same thread. */
+const char* dsa_last_error(void);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_indexer_scores -- lightning-indexer scores (section 1.1 of the velog summary).
+ *
+ *   scores[b][t][s] = sum_{j<H_I} w[b][t][j] * ReLU( qhat[b][t][j][:] . khat[b][s][:] ),  s <= pos_t
+ *
+ * dtype = DSA_FP8_E4M3: q is uint8 codes [B][n_q][H_I][d_I] with q_scale [B][n_q][H_I] (fp32), k is
+ *   uint8 codes [B][n_kv][d_I] with k_scale [B][n_kv]; qhat = e4m3(q) * q_scale, khat = e4m3(k) *
+ *   k_scale.  Because scales are positive, the kernel evaluates
+ *   k_scale[s] * sum_j (w * q_scale)[t][j] * ReLU(e4m3(q) . e4m3(k)) with fp32 accumulation.
+ * dtype = DSA_F32: q [B][n_q][H_I][d_I] and k [B][n_kv][d_I] are float; q_scale, k_scale must be NULL.
+ * w is [B][n_q][H_I] fp32 (any sign).  scores is [B][n_q][ld_scores] fp32, ld_scores >= n_kv; only
+ *   entries s <= pos_t are written, the rest of each row is left untouched.
+ * Fast path: FP8 with H_I = 64, d_I = 128 (CDNA4 FP8 matrix cores).  Other shapes: a generic kernel
+ *   (H_I <= 64, d_I <= 256, d_I % 4 == 0); anything else returns DSA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_indexer_scores(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                const float* w, int B, int n_q, int n_kv, int H_I, int d_I,
+                                dsa_dtype_t dtype, float* scores, int64_t ld_scores, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_topk -- fine-grained token selection (section 1.2 of the velog summary; k = 2048 in stage 2).
+ *
+ * For each query row: the min(k, pos_t + 1) positions s <= pos_t with the largest scores[b][t][s],
+ * preferring the higher score and, among equal scores, the lower s; -0.0 equals +0.0.  Written to
+ * idx[b][t][0..k) in ascending s, padded with -1.  scores is read only at s <= pos_t.
+ * scores [B][n_q][ld_scores] fp32 (ld_scores >= n_kv), idx [B][n_q][k] int32.  1 <= k <= 65536.
+ * Non-finite scores: NaN is not allowed (result unspecified); +-inf are ordered as usual.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int B, int n_q, int n_kv, int k,
+                      int32_t* idx, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_sparse_mla_attn -- attention over the selected latent rows (sections 1.2 and 1.3 of the
+ * velog summary).  For every query t and head h:
+ *
+ *   z_i   = sm_scale * q[b][t][h][:] . kv[b][s_i][:]     over s_i = idx[b][t][i] != -1
+ *   out   = sum_i softmax(z)_i * kv[b][s_i][0:d_v]        (V = the first d_v columns of the row)
+ *   lse   = log sum_i exp(z_i)                            (natural log)
+ *
+ * q [B][n_q][H][d_qk], kv [B][n_kv][d_qk] (one latent row per token, shared by all H heads),
+ * idx [B][n_q][k] int32 with entries -1 (skipped) or in [0, n_kv) (entries outside are skipped too),
+ * out [B][n_q][H][d_v] in `dtype`, lse [B][n_q][H] fp32 or NULL.  A row with no valid entry gets
+ * out = 0 and lse = -inf.
+ * dtype = DSA_BF16: q, kv, out are bf16 (fp32 accumulation).  Fast path H = 128, d_qk = 576,
+ *   d_v = 512 (CDNA4 bf16 matrix cores).
+ * dtype = DSA_F32: q, kv, out fp32 (generic kernel: H <= 64, d_qk <= 256, d_v <= d_qk).
+ * workspace: device memory of at least dsa_sparse_mla_attn_workspace_size(...) bytes, 256-byte
+ *   aligned (may be NULL when that size is 0).
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx, int B, int n_q,
+                                 int n_kv, int H, int d_qk, int d_v, int k, float sm_scale,
+                                 dsa_dtype_t dtype, void* out, float* lse, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+size_t dsa_sparse_mla_attn_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
+                                          dsa_dtype_t dtype);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_forward_prefill -- the whole path for B sequences of n_kv tokens whose last n_q tokens are
+ * queries: dsa_indexer_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.  Chunked prefill
+ * is one call per chunk with n_kv growing by the chunk length (all state is in the caller's caches).
+ *
+ * Indexer inputs as in dsa_indexer_scores (idx_dtype, q_i, q_i_scale, k_i, k_i_scale, w, H_I, d_I);
+ * attention inputs as in dsa_sparse_mla_attn (attn_dtype, q, kv, H, d_qk, d_v, sm_scale, out, lse).
+ * idx_out: NULL, or [B][n_q][k] int32 that receives the selection (else it stays in the workspace).
+ * workspace: at least dsa_forward_workspace_size(...) bytes, 256-byte aligned.  It holds the score
+ *   rows ([B][n_q][ld] fp32, ld = n_kv rounded up to 64), the selection and the attention scratch.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_forward_prefill(const void* q_i, const float* q_i_scale, const void* k_i,
+                                 const float* k_i_scale, const float* w, const void* q, const void* kv,
+                                 int B, int n_q, int n_kv, int H_I, int d_I, int H, int d_qk, int d_v,
+                                 int k, float sm_scale, dsa_dtype_t idx_dtype, dsa_dtype_t attn_dtype,
+                                 void* out, float* lse, int32_t* idx_out, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/* dsa_forward_decode -- the whole path for B sequences with one new query each (n_q = 1) at position
+ * n_kv - 1, whose own key is already in the caches.  Same arguments as dsa_forward_prefill without
+ * n_q; kernels tuned for few long rows (keys split over many workgroups, split-k attention). */
+dsa_status_t dsa_forward_decode(const void* q_i, const float* q_i_scale, const void* k_i,
+                                const float* k_i_scale, const float* w, const void* q, const void* kv,
+                                int B, int n_kv, int H_I, int d_I, int H, int d_qk, int d_v, int k,
+                                float sm_scale, dsa_dtype_t idx_dtype, dsa_dtype_t attn_dtype,
+                                void* out, float* lse, int32_t* idx_out, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/* Workspace bytes for dsa_forward_prefill (n_q queries) or dsa_forward_decode (n_q = 1). */
+size_t dsa_forward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
+                                  dsa_dtype_t attn_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

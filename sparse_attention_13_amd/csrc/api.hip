@@ -1,0 +1,276 @@
+// api.hip -- the C ABI declared in include/dsa.h: argument validation, kernel selection, workspace
+// layout.  Nothing here allocates, frees or synchronises; every failure is reported before any work
+// is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status_t ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kMaxTopK = 65536;
+
+// ---------------------------------------------------------------------------------------- indexer
+dsa_status_t check_indexer(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
+                           int B, int n_q, int n_kv, int H_I, int d_I, dsa_dtype_t dtype, const float* scores,
+                           int64_t ld, bool* fast) {
+  if (!q || !k || !w || !scores) return fail(DSA_ERR_INVALID_ARG, "indexer: null q, k, w or scores");
+  if (B < 1 || n_q < 1 || n_kv < 1 || H_I < 1 || d_I < 1)
+    return fail(DSA_ERR_INVALID_ARG, "indexer: sizes must be positive (B=%d n_q=%d n_kv=%d H_I=%d d_I=%d)", B, n_q,
+                n_kv, H_I, d_I);
+  if (n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "indexer: n_q=%d exceeds n_kv=%d", n_q, n_kv);
+  if (ld < n_kv) return fail(DSA_ERR_INVALID_ARG, "indexer: ld_scores=%lld < n_kv=%d", (long long)ld, n_kv);
+  if (dtype == DSA_FP8_E4M3) {
+    if (!q_scale || !k_scale) return fail(DSA_ERR_INVALID_ARG, "indexer: fp8 inputs need q_scale and k_scale");
+  } else if (dtype == DSA_F32) {
+    if (q_scale || k_scale) return fail(DSA_ERR_INVALID_ARG, "indexer: fp32 inputs take no scales (pass NULL)");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: dtype %d not supported (fp8 e4m3 or fp32)", (int)dtype);
+  }
+  *fast = dtype == DSA_FP8_E4M3 && H_I == 64 && d_I == 128 && aligned(q, 16) && aligned(k, 16);
+  if (!*fast && !(H_I <= 64 && d_I <= 256 && d_I % 4 == 0 && (size_t)(H_I * d_I + H_I) * 4 <= 65536))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: H_I=%d d_I=%d not supported (fast path 64x128 fp8; generic H_I<=64, "
+                "d_I<=256, d_I%%4==0)", H_I, d_I);
+  return DSA_OK;
+}
+
+dsa_status_t run_indexer(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
+                         int B, int n_q, int n_kv, int H_I, int d_I, dsa_dtype_t dtype, float* scores, int64_t ld,
+                         bool fast, hipStream_t stream) {
+  hipError_t e;
+  if (fast)
+    e = dsa::launch_indexer_fp8((const uint8_t*)q, q_scale, (const uint8_t*)k, k_scale, w, B, n_q, n_kv, scores, ld, 0,
+                                stream);
+  else
+    e = dsa::launch_indexer_generic(q, q_scale, k, k_scale, w, B, n_q, n_kv, H_I, d_I, dtype == DSA_FP8_E4M3, scores,
+                                    ld, stream);
+  return hip_status(e, "dsa_indexer_scores");
+}
+
+// ------------------------------------------------------------------------------------------- top-k
+dsa_status_t check_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, const int32_t* idx) {
+  if (!scores || !idx) return fail(DSA_ERR_INVALID_ARG, "topk: null scores or idx");
+  if (B < 1 || n_q < 1 || n_kv < 1) return fail(DSA_ERR_INVALID_ARG, "topk: sizes must be positive");
+  if (n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "topk: n_q=%d exceeds n_kv=%d", n_q, n_kv);
+  if (ld < n_kv) return fail(DSA_ERR_INVALID_ARG, "topk: ld_scores=%lld < n_kv=%d", (long long)ld, n_kv);
+  if (k < 1 || k > kMaxTopK) return fail(DSA_ERR_INVALID_ARG, "topk: k=%d outside [1, %d]", k, kMaxTopK);
+  if (n_q > 65535 * 1024 || B > 65535) return fail(DSA_ERR_UNSUPPORTED, "topk: grid too large");
+  return DSA_OK;
+}
+
+// ------------------------------------------------------------------------------------------- attention
+struct AttnPlan {
+  bool fast = false;
+  int n_split = 1;
+  size_t ws = 0;
+};
+
+dsa_status_t plan_attn(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k, dsa_dtype_t dtype, AttnPlan* p) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || H < 1 || d_qk < 1 || d_v < 1 || k < 1)
+    return fail(DSA_ERR_INVALID_ARG, "attn: sizes must be positive");
+  if (d_v > d_qk) return fail(DSA_ERR_INVALID_ARG, "attn: d_v=%d exceeds d_qk=%d", d_v, d_qk);
+  if (k > kMaxTopK) return fail(DSA_ERR_INVALID_ARG, "attn: k=%d exceeds %d", k, kMaxTopK);
+  if (dtype == DSA_BF16) {
+    if (!(H == 128 && d_qk == 576 && d_v == 512))
+      return fail(DSA_ERR_UNSUPPORTED, "attn: bf16 supports H=128, d_qk=576, d_v=512 (got %d, %d, %d)", H, d_qk, d_v);
+    p->fast = true;
+    p->n_split = dsa::mla_bf16_pick_split(B, n_q, k);
+    p->ws = dsa::mla_bf16_workspace_bytes(B, n_q, p->n_split);
+  } else if (dtype == DSA_F32) {
+    if (!(d_qk <= 256 && (size_t)(d_qk + k + 4) * 4 <= 65536 && H <= 65535))
+      return fail(DSA_ERR_UNSUPPORTED, "attn: fp32 generic kernel needs d_qk<=256 and (d_qk+k)*4 <= 64 KiB");
+    p->fast = false;
+    p->n_split = 1;
+    p->ws = 0;
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "attn: dtype %d not supported (bf16 or fp32)", (int)dtype);
+  }
+  if (n_q > 65535 * 64 || B > 65535) return fail(DSA_ERR_UNSUPPORTED, "attn: grid too large");
+  return DSA_OK;
+}
+
+dsa_status_t check_attn_ptrs(const void* q, const void* kv, const int32_t* idx, const void* out, float sm_scale,
+                             const AttnPlan& p, const void* ws, size_t ws_bytes) {
+  if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "attn: null q, kv, idx or out");
+  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "attn: sm_scale must be finite");
+  if (p.fast && !(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "attn: bf16 path needs 16-byte aligned q, kv and out");
+  if (p.ws > 0) {
+    if (!ws) return fail(DSA_ERR_WORKSPACE, "attn: workspace of %zu bytes required", p.ws);
+    if (!aligned(ws, 256)) return fail(DSA_ERR_WORKSPACE, "attn: workspace must be 256-byte aligned");
+    if (ws_bytes < p.ws) return fail(DSA_ERR_WORKSPACE, "attn: workspace %zu < %zu bytes", ws_bytes, p.ws);
+  }
+  return DSA_OK;
+}
+
+dsa_status_t run_attn(const void* q, const void* kv, const int32_t* idx, int B, int n_q, int n_kv, int H, int d_qk,
+                      int d_v, int k, float sm_scale, void* out, float* lse, const AttnPlan& p, void* ws,
+                      hipStream_t stream) {
+  hipError_t e;
+  if (p.fast)
+    e = dsa::launch_mla_bf16((const uint16_t*)q, (const uint16_t*)kv, idx, B, n_q, n_kv, k, sm_scale, (uint16_t*)out,
+                             lse, p.n_split, ws, stream);
+  else
+    e = dsa::launch_attn_generic((const float*)q, (const float*)kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale,
+                                 (float*)out, lse, stream);
+  return hip_status(e, "dsa_sparse_mla_attn");
+}
+
+// ------------------------------------------------------------------------------------------- forward
+struct FwdLayout {
+  int64_t ld = 0;
+  size_t off_scores = 0, off_idx = 0, off_attn = 0, total = 0;
+  AttnPlan attn;
+};
+
+dsa_status_t plan_forward(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k, dsa_dtype_t attn_dtype,
+                          FwdLayout* L) {
+  dsa_status_t st = plan_attn(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype, &L->attn);
+  if (st != DSA_OK) return st;
+  if (n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "forward: n_q=%d exceeds n_kv=%d", n_q, n_kv);
+  L->ld = (int64_t)align_up((size_t)n_kv, 64);
+  L->off_scores = 0;
+  L->off_idx = align_up((size_t)B * n_q * L->ld * sizeof(float), 256);
+  L->off_attn = align_up(L->off_idx + (size_t)B * n_q * k * sizeof(int32_t), 256);
+  L->total = L->off_attn + align_up(L->attn.ws, 256);
+  return DSA_OK;
+}
+
+dsa_status_t forward(const void* q_i, const float* q_i_scale, const void* k_i, const float* k_i_scale, const float* w,
+                     const void* q, const void* kv, int B, int n_q, int n_kv, int H_I, int d_I, int H, int d_qk,
+                     int d_v, int k, float sm_scale, dsa_dtype_t idx_dtype, dsa_dtype_t attn_dtype, void* out,
+                     float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream_) {
+  FwdLayout L;
+  dsa_status_t st = plan_forward(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype, &L);
+  if (st != DSA_OK) return st;
+  if (!workspace) return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes required", L.total);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_WORKSPACE, "forward: workspace must be 256-byte aligned");
+  if (ws_bytes < L.total) return fail(DSA_ERR_WORKSPACE, "forward: workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* ws = (char*)workspace;
+  float* scores = (float*)(ws + L.off_scores);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + L.off_idx);
+  bool fast_idx = false;
+  st = check_indexer(q_i, q_i_scale, k_i, k_i_scale, w, B, n_q, n_kv, H_I, d_I, idx_dtype, scores, L.ld, &fast_idx);
+  if (st != DSA_OK) return st;
+  st = check_topk(scores, L.ld, B, n_q, n_kv, k, idx);
+  if (st != DSA_OK) return st;
+  st = check_attn_ptrs(q, kv, idx, out, sm_scale, L.attn, L.attn.ws ? ws + L.off_attn : nullptr, L.attn.ws);
+  if (st != DSA_OK) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  st = run_indexer(q_i, q_i_scale, k_i, k_i_scale, w, B, n_q, n_kv, H_I, d_I, idx_dtype, scores, L.ld, fast_idx,
+                   stream);
+  if (st != DSA_OK) return st;
+  st = hip_status(dsa::launch_topk(scores, L.ld, B, n_q, n_kv, k, idx, stream), "dsa_topk");
+  if (st != DSA_OK) return st;
+  return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, L.attn,
+                  L.attn.ws ? ws + L.off_attn : nullptr, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return 100; }
+
+const char* dsa_status_string(dsa_status_t s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: no kernel for this dtype/shape";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown dsa_status_t";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status_t dsa_indexer_scores(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                const float* w, int B, int n_q, int n_kv, int H_I, int d_I, dsa_dtype_t dtype,
+                                float* scores, int64_t ld_scores, void* stream) {
+  bool fast = false;
+  dsa_status_t st = check_indexer(q, q_scale, k, k_scale, w, B, n_q, n_kv, H_I, d_I, dtype, scores, ld_scores, &fast);
+  if (st != DSA_OK) return st;
+  return run_indexer(q, q_scale, k, k_scale, w, B, n_q, n_kv, H_I, d_I, dtype, scores, ld_scores, fast,
+                     (hipStream_t)stream);
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int B, int n_q, int n_kv, int k, int32_t* idx,
+                      void* stream) {
+  dsa_status_t st = check_topk(scores, ld_scores, B, n_q, n_kv, k, idx);
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_topk(scores, ld_scores, B, n_q, n_kv, k, idx, (hipStream_t)stream), "dsa_topk");
+}
+
+size_t dsa_sparse_mla_attn_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
+                                          dsa_dtype_t dtype) {
+  AttnPlan p;
+  if (plan_attn(B, n_q, n_kv, H, d_qk, d_v, k, dtype, &p) != DSA_OK) return 0;
+  return p.ws;
+}
+
+dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* idx, int B, int n_q, int n_kv, int H,
+                                 int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t dtype, void* out, float* lse,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  AttnPlan p;
+  dsa_status_t st = plan_attn(B, n_q, n_kv, H, d_qk, d_v, k, dtype, &p);
+  if (st != DSA_OK) return st;
+  st = check_attn_ptrs(q, kv, idx, out, sm_scale, p, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, p, workspace, (hipStream_t)stream);
+}
+
+size_t dsa_forward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
+                                  dsa_dtype_t attn_dtype) {
+  FwdLayout L;
+  if (plan_forward(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype, &L) != DSA_OK) return 0;
+  return L.total;
+}
+
+dsa_status_t dsa_forward_prefill(const void* q_i, const float* q_i_scale, const void* k_i, const float* k_i_scale,
+                                 const float* w, const void* q, const void* kv, int B, int n_q, int n_kv, int H_I,
+                                 int d_I, int H, int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t idx_dtype,
+                                 dsa_dtype_t attn_dtype, void* out, float* lse, int32_t* idx_out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  return forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, B, n_q, n_kv, H_I, d_I, H, d_qk, d_v, k, sm_scale,
+                 idx_dtype, attn_dtype, out, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+dsa_status_t dsa_forward_decode(const void* q_i, const float* q_i_scale, const void* k_i, const float* k_i_scale,
+                                const float* w, const void* q, const void* kv, int B, int n_kv, int H_I, int d_I,
+                                int H, int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t idx_dtype,
+                                dsa_dtype_t attn_dtype, void* out, float* lse, int32_t* idx_out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  return forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, B, 1, n_kv, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype,
+                 attn_dtype, out, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// dsa_internal.h -- shared definitions of the gfx950 kernels behind include/dsa.h.
+// Internal to the library: kernels, launch helpers and the vector types used with the CDNA4
+// matrix-core builtins.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even (inputs here are finite).
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
+  return __uint_as_float(((unsigned int)b) << 16);
+}
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned int u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+  return (unsigned int)f32_to_bf16_bits(a) | ((unsigned int)f32_to_bf16_bits(b) << 16);
+}
+
+// OCP e4m3fn byte -> fp32 through the hardware converter.
+__device__ __forceinline__ float e4m3_to_f32(unsigned int byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Sum of x over the lane pair (l, l ^ 32).
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum of x over the lane pair (l, l ^ 16).
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace dsa
+
+// ---------------------------------------------------------------------------------------------
+// Launch helpers (host side), one per kernel family.  They assume arguments already validated by
+// the C-ABI layer and return the HIP launch status.
+// ---------------------------------------------------------------------------------------------
+namespace dsa {
+
+hipError_t launch_indexer_generic(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                  const float* w, int B, int n_q, int n_kv, int H_I, int d_I, bool fp8,
+                                  float* scores, int64_t ld, hipStream_t stream);
+
+// FP8 matrix-core indexer, H_I = 64, d_I = 128.  keys_per_wave <= 0 means "whole causal row".
+hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint8_t* k, const float* k_scale,
+                              const float* w, int B, int n_q, int n_kv, float* scores, int64_t ld,
+                              int keys_per_wave, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,
+                       hipStream_t stream);
+
+hipError_t launch_attn_generic(const float* q, const float* kv, const int32_t* idx, int B, int n_q, int n_kv,
+                               int H, int d_qk, int d_v, int k, float sm_scale, float* out, float* lse,
+                               hipStream_t stream);
+
+// bf16 matrix-core sparse MLA, H = 128, d_qk = 576, d_v = 512.  n_split > 1 splits each query's
+// selection into n_split contiguous parts whose partial results go to `partial` (fp32) and are
+// merged by a second kernel.
+size_t mla_bf16_workspace_bytes(int B, int n_q, int n_split);
+int mla_bf16_pick_split(int B, int n_q, int k);
+hipError_t launch_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int n_q, int n_kv,
+                           int k, float sm_scale, uint16_t* out, float* lse, int n_split, void* partial,
+                           hipStream_t stream);
+
+}  // namespace dsa

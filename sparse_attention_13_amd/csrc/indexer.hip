@@ -1,0 +1,229 @@
+// indexer.hip -- lightning-indexer scores on gfx950.
+//
+// I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) over s <= pos_t (velog summary "DeepSeek-V3.2:
+// Pushing the Frontier of Open Large Language Models", section 1.1; few indexer heads in FP8).
+//
+// Fast path (H_I = 64, d_I = 128, e4m3 inputs): the 64 heads of one query form the M dimension of
+// the 16x16x128 FP8 matrix-core instruction (4 row blocks of 16 heads), 16 keys form N, and the
+// whole d_I = 128 is one instruction's K.  With scales positive, ReLU commutes with them, so the
+// epilogue is  k_scale[s] * sum_h (w * q_scale)[h] * max(acc[h,s], 0).  Each lane owns 4 heads of
+// every row block for one key column, so the head sum is 16 lane-local FMAs followed by two
+// cross-lane adds (lane ^ 16, lane ^ 32).  The per-head [H_I, T, S] products are never stored.
+//
+// Work decomposition: one wave = QW consecutive queries x a range of keys, streamed in groups of
+// 64 keys (4 MFMA column blocks) with the next group's keys loaded while the current one is
+// computed.  Prefill: one range = the whole causal row, longest rows dispatched first.  Decode
+// (one query per sequence): the row is split into chunks so that thousands of waves stream keys.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+// ------------------------------------------------------------------------------------------------
+// Generic kernel: any H_I <= 64, d_I <= 256; fp32 or e4m3 inputs.  One workgroup per query row; the
+// query (dequantised exactly like the definition: fp32(e4m3 * scale)) and its weights sit in LDS.
+// ------------------------------------------------------------------------------------------------
+template <bool FP8>
+__global__ __launch_bounds__(256) void indexer_generic_kernel(const void* __restrict__ q_,
+                                                              const float* __restrict__ q_scale,
+                                                              const void* __restrict__ k_,
+                                                              const float* __restrict__ k_scale,
+                                                              const float* __restrict__ w, int n_q, int n_kv,
+                                                              int H_I, int d_I, float* __restrict__ scores,
+                                                              int64_t ld) {
+  extern __shared__ float smem[];
+  float* qs = smem;              // [H_I][d_I]
+  float* ws = smem + H_I * d_I;  // [H_I]
+  const int t = blockIdx.x, b = blockIdx.y;
+  const size_t qrow = (size_t)b * n_q + t;
+  for (int e = threadIdx.x; e < H_I * d_I; e += blockDim.x) {
+    float v;
+    if (FP8) {
+      const uint8_t* q8 = (const uint8_t*)q_ + qrow * H_I * d_I;
+      v = e4m3_to_f32(q8[e]) * q_scale[qrow * H_I + e / d_I];
+    } else {
+      v = ((const float*)q_)[qrow * H_I * d_I + e];
+    }
+    qs[e] = v;
+  }
+  for (int j = threadIdx.x; j < H_I; j += blockDim.x) ws[j] = w[qrow * H_I + j];
+  __syncthreads();
+  const int pos = n_kv - n_q + t;
+  for (int s = threadIdx.x; s <= pos; s += blockDim.x) {
+    const size_t krow = (size_t)b * n_kv + s;
+    float kscale = FP8 ? k_scale[krow] : 1.0f;
+    float acc = 0.0f;
+    for (int j = 0; j < H_I; j++) {
+      float dot = 0.0f;
+      for (int i = 0; i < d_I; i++) {
+        float kv;
+        if (FP8)
+          kv = e4m3_to_f32(((const uint8_t*)k_)[krow * d_I + i]) * kscale;
+        else
+          kv = ((const float*)k_)[krow * d_I + i];
+        dot = fmaf(qs[j * d_I + i], kv, dot);
+      }
+      acc = fmaf(ws[j], fmaxf(dot, 0.0f), acc);
+    }
+    scores[qrow * ld + s] = acc + 0.0f;
+  }
+}
+
+hipError_t launch_indexer_generic(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                  const float* w, int B, int n_q, int n_kv, int H_I, int d_I, bool fp8,
+                                  float* scores, int64_t ld, hipStream_t stream) {
+  dim3 grid(n_q, B);
+  size_t lds = (size_t)(H_I * d_I + H_I) * sizeof(float);
+  if (fp8)
+    hipLaunchKernelGGL(indexer_generic_kernel<true>, grid, dim3(256), lds, stream, q, q_scale, k, k_scale, w,
+                       n_q, n_kv, H_I, d_I, scores, ld);
+  else
+    hipLaunchKernelGGL(indexer_generic_kernel<false>, grid, dim3(256), lds, stream, q, q_scale, k, k_scale, w,
+                       n_q, n_kv, H_I, d_I, scores, ld);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// FP8 matrix-core kernel, H_I = 64, d_I = 128.
+// ------------------------------------------------------------------------------------------------
+constexpr int kHI = 64;
+constexpr int kDI = 128;
+
+__device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b) {
+  v4f c = {0.f, 0.f, 0.f, 0.f};
+  // Scale operands 0 select the unscaled instruction (v_mfma_f32_16x16x128_f8f6f4, e4m3 x e4m3).
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// One group = 64 keys = 4 column blocks of 16.  Lane l loads key (16*j + l%16), bytes 32*(l/16)..+32
+// of column block j: the matrix-core B-operand layout.  Keys past the end are clamped (never stored).
+__device__ __forceinline__ void load_key_group(const uint8_t* __restrict__ kb, int g0, int n_kv, int lane,
+                                               v8i (&kf)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    int s = min(g0 + 16 * j + (lane & 15), n_kv - 1);
+    kf[j] = *(const v8i*)(kb + (size_t)s * kDI + (lane >> 4) * 32);
+  }
+}
+
+template <int QW>
+__global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __restrict__ q8,
+                                                             const float* __restrict__ q_scale,
+                                                             const float* __restrict__ w,
+                                                             const uint8_t* __restrict__ k8,
+                                                             const float* __restrict__ k_scale,
+                                                             float* __restrict__ scores, int64_t ld, int B,
+                                                             int n_q, int n_kv, int n_qgroups, int n_chunks,
+                                                             int chunk_keys, int n_items) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n_items) return;
+  const int kc = item % n_chunks;
+  const int rest = item / n_chunks;
+  const int b = rest % B;
+  const int qg = n_qgroups - 1 - rest / B;  // longest rows first
+  const int t0 = qg * QW;
+  const int nq_here = min(QW, n_q - t0);
+  const int pos0 = n_kv - n_q + t0;
+  const int pos_last = pos0 + nq_here - 1;
+  const int s_begin = kc * chunk_keys;
+  if (s_begin > pos_last) return;
+  const int s_end = min(pos_last + 1, s_begin + chunk_keys);
+
+  // A operands: row block mb holds heads 16*mb .. 16*mb+15; lane l supplies head 16*mb + l%16,
+  // bytes 32*(l/16) .. +32 of that head's 128-byte query.
+  v8i qa[QW][4];
+  float ww[QW][4][4];  // (w * q_scale) of head 16*mb + 4*(l/16) + r: the accumulator rows lane l owns
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) {
+    const int t = t0 + min(qi, nq_here - 1);
+    const size_t qrow = (size_t)b * n_q + t;
+    const uint8_t* qp = q8 + qrow * kHI * kDI;
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) qa[qi][mb] = *(const v8i*)(qp + (16 * mb + (lane & 15)) * kDI + (lane >> 4) * 32);
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int h = 16 * mb + 4 * (lane >> 4) + r;
+        ww[qi][mb][r] = w[qrow * kHI + h] * q_scale[qrow * kHI + h];
+      }
+  }
+
+  const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
+  const float* ksb = k_scale + (size_t)b * n_kv;
+  float* srow = scores + ((size_t)b * n_q + t0) * ld;
+
+  v8i kcur[4], knext[4];
+  load_key_group(kb, s_begin, n_kv, lane, kcur);
+  for (int g0 = s_begin; g0 < s_end; g0 += 64) {
+    if (g0 + 64 < s_end) load_key_group(kb, g0 + 64, n_kv, lane, knext);
+    const int s = g0 + lane;
+    const float ksc = ksb[min(s, n_kv - 1)];
+    float out[QW];
+#pragma unroll
+    for (int qi = 0; qi < QW; qi++) out[qi] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v4f acc[QW][4];
+#pragma unroll
+      for (int qi = 0; qi < QW; qi++)
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) acc[qi][mb] = mfma_f8_16x16x128(qa[qi][mb], kcur[j]);
+#pragma unroll
+      for (int qi = 0; qi < QW; qi++) {
+        float v = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], fmaxf(acc[qi][mb][r], 0.0f), v);
+        v = xor16_sum(v);
+        v = xor32_sum(v);
+        out[qi] = ((lane >> 4) == j) ? v : out[qi];
+      }
+    }
+    // lane l now holds the score of key g0 + l for every query of the wave
+    if (s < s_end) {
+#pragma unroll
+      for (int qi = 0; qi < QW; qi++)
+        if (qi < nq_here && s <= pos0 + qi) srow[(size_t)qi * ld + s] = out[qi] * ksc + 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) kcur[j] = knext[j];
+  }
+}
+
+hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint8_t* k, const float* k_scale,
+                              const float* w, int B, int n_q, int n_kv, float* scores, int64_t ld,
+                              int keys_per_wave, hipStream_t stream) {
+  if (n_q >= 2) {
+    constexpr int QW = 2;
+    const int n_qgroups = (n_q + QW - 1) / QW;
+    const int chunk = keys_per_wave > 0 ? ((keys_per_wave + 63) / 64) * 64 : ((n_kv + 63) / 64) * 64;
+    const int n_chunks = (n_kv + chunk - 1) / chunk;
+    const long long items = (long long)B * n_qgroups * n_chunks;
+    if (items > (1LL << 30)) return hipErrorInvalidValue;
+    const int blocks = (int)((items + 3) / 4);
+    hipLaunchKernelGGL(indexer_fp8_kernel<QW>, dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k, k_scale,
+                       scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
+  } else {
+    constexpr int QW = 1;
+    const int n_qgroups = n_q;
+    int chunk = keys_per_wave;
+    if (chunk <= 0) {
+      // enough waves to stream the keys from every CU: aim for >= 4096 waves in total
+      long long waves_per_row = (4096 + (long long)B * n_q - 1) / ((long long)B * n_q);
+      chunk = (int)((n_kv + waves_per_row - 1) / waves_per_row);
+      chunk = chunk < 512 ? 512 : chunk;
+    }
+    chunk = ((chunk + 63) / 64) * 64;
+    const int n_chunks = (n_kv + chunk - 1) / chunk;
+    const long long items = (long long)B * n_qgroups * n_chunks;
+    if (items > (1LL << 30)) return hipErrorInvalidValue;
+    const int blocks = (int)((items + 3) / 4);
+    hipLaunchKernelGGL(indexer_fp8_kernel<QW>, dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k, k_scale,
+                       scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

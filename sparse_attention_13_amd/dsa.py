@@ -1,0 +1,193 @@
+"""Python binding of libdsa.so (include/dsa.h): argument marshalling only.
+
+Every computation runs in the library's HIP kernels on the GPU; torch tensors are used only as
+device memory and the current HIP stream.  If the library is missing this module raises on load:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+
+# Every entry point of include/dsa.h, with its ctypes signature.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "dsa_version": ([], _I),
+    "dsa_status_string": ([_I], ctypes.c_char_p),
+    "dsa_last_error": ([], ctypes.c_char_p),
+    "dsa_indexer_scores": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
+    "dsa_topk": ([_P, _I64, _I, _I, _I, _I, _P, _P], _I),
+    "dsa_sparse_mla_attn": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
+    "dsa_sparse_mla_attn_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "dsa_forward_prefill": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P,
+                             _P, _P, _SZ, _P], _I),
+    "dsa_forward_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P,
+                            _P, _SZ, _P], _I),
+    "dsa_forward_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+}
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+def _status_name(st: int) -> str:
+    return ["DSA_OK", "DSA_ERR_INVALID_ARG", "DSA_ERR_UNSUPPORTED", "DSA_ERR_WORKSPACE", "DSA_ERR_HIP"][st] \
+        if 0 <= st <= 4 else f"status {st}"
+
+
+def lib():
+    """The loaded library (raises if libdsa.so has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build it with sparse_attention_13_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != DSA_OK:
+        raise DSAError(st, lib().dsa_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def version() -> int:
+    return lib().dsa_version()
+
+
+def indexer_scores(q, q_scale, k, k_scale, w, scores, n_q=None, stream=None):
+    """scores[b, t, s] for s <= n_kv - n_q + t.  q [B, n_q, H_I, d_I] (uint8 e4m3 codes or f32),
+    k [B, n_kv, d_I], w [B, n_q, H_I], scores [B, n_q, ld] f32 (written in place)."""
+    _dev(q, q_scale, k, k_scale, w, scores)
+    B, nq, H_I, d_I = q.shape
+    n_kv = k.shape[1]
+    _check(lib().dsa_indexer_scores(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), B, nq, n_kv, H_I, d_I,
+                                    _dtype_code(q), _ptr(scores), scores.shape[-1], _stream(stream)))
+    return scores
+
+
+def topk(scores, n_kv: int, k: int, idx=None, stream=None):
+    """Per row the k best s <= pos_t (ascending, -1 padded).  scores [B, n_q, ld] f32 -> idx [B, n_q, k] int32."""
+    _dev(scores, idx)
+    B, nq, ld = scores.shape
+    if idx is None:
+        idx = torch.empty((B, nq, k), dtype=torch.int32, device=scores.device)
+    _check(lib().dsa_topk(_ptr(scores), ld, B, nq, n_kv, k, _ptr(idx), _stream(stream)))
+    return idx
+
+
+def sparse_mla_attn(q, kv, idx, d_v: int, sm_scale: float, out=None, lse=None, workspace=None, stream=None):
+    """MQA-mode attention over the selected latent rows.  q [B, n_q, H, d_qk], kv [B, n_kv, d_qk],
+    idx [B, n_q, k] int32 -> out [B, n_q, H, d_v] (q's dtype), lse [B, n_q, H] f32."""
+    _dev(q, kv, idx, out, lse, workspace)
+    B, nq, H, d_qk = q.shape
+    n_kv = kv.shape[1]
+    k = idx.shape[-1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, nq, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq, H), dtype=torch.float32, device=q.device)
+    ws = lib().dsa_sparse_mla_attn_workspace_size(B, nq, n_kv, H, d_qk, d_v, k, dt)
+    if ws and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_sparse_mla_attn(_ptr(q), _ptr(kv), _ptr(idx), B, nq, n_kv, H, d_qk, d_v, k, float(sm_scale), dt,
+                                     _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
+    return out, lse
+
+
+def forward_workspace_size(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype) -> int:
+    return int(lib().dsa_forward_workspace_size(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype))
+
+
+def forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, k: int, d_v: int, sm_scale: float, decode: bool = False,
+            out=None, lse=None, idx_out=None, workspace=None, stream=None):
+    """Indexer -> top-k -> sparse attention on one stream.
+
+    Prefill: q_i [B, n_q, H_I, d_I], w [B, n_q, H_I], q [B, n_q, H, d_qk].  Decode (decode=True):
+    q_i [B, H_I, d_I], w [B, H_I], q [B, H, d_qk] (one query per sequence at position n_kv - 1).
+    k_i [B, n_kv, d_I], kv [B, n_kv, d_qk].  Returns (out, lse, idx_out)."""
+    _dev(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, out, lse, idx_out, workspace)
+    if decode:
+        B, H_I, d_I = q_i.shape
+        n_q = 1
+        H, d_qk = q.shape[1], q.shape[2]
+    else:
+        B, n_q, H_I, d_I = q_i.shape
+        H, d_qk = q.shape[2], q.shape[3]
+    n_kv = k_i.shape[1]
+    adt = _dtype_code(q)
+    idt = _dtype_code(q_i)
+    if out is None:
+        out = torch.empty((B, n_q, H, d_v) if not decode else (B, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, n_q, H) if not decode else (B, H), dtype=torch.float32, device=q.device)
+    ws = forward_workspace_size(B, n_q, n_kv, H, d_qk, d_v, k, adt)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    L = lib()
+    if decode:
+        st = L.dsa_forward_decode(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w), _ptr(q), _ptr(kv),
+                                  B, n_kv, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), idt, adt, _ptr(out),
+                                  _ptr(lse), _ptr(idx_out), _ptr(workspace), wsz, _stream(stream))
+    else:
+        st = L.dsa_forward_prefill(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w), _ptr(q),
+                                   _ptr(kv), B, n_q, n_kv, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), idt, adt,
+                                   _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace), wsz, _stream(stream))
+    _check(st)
+    return out, lse, idx_out

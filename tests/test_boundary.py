@@ -1,0 +1,150 @@
+"""The C-ABI library: it loads, exports every entry point include/dsa.h declares, and rejects bad
+arguments before touching the device (these calls never reach a kernel, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# These calls pass fake device pointers that validation must reject; on a machine with a GPU a
+# validation bug would instead launch a kernel on them, so the module only runs where there is none.
+import torch  # noqa: E402
+
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake-pointer validation tests run only on hosts without a GPU")
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_13_amd import dsa
+    if not os.path.exists(dsa.LIB_PATH):
+        from sparse_attention_13_amd import build
+        build.build()
+    return dsa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ["dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward_prefill", "dsa_forward_decode",
+              "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
+              "dsa_last_error", "dsa_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from sparse_attention_13_amd import dsa
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in dsa.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_status_strings(L):
+    assert L.dsa_version() >= 100
+    for st in range(5):
+        s = L.dsa_status_string(st).decode()
+        assert s.startswith("DSA_")
+    assert b"unknown" in L.dsa_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000)
+
+
+def test_topk_validation(L):
+    from sparse_attention_13_amd.dsa import DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED
+    assert L.dsa_topk(None, 10, 1, 1, 10, 4, FAKE, None) == DSA_ERR_INVALID_ARG
+    assert b"null" in L.dsa_last_error()
+    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 0, FAKE2, None) == DSA_ERR_INVALID_ARG  # k = 0
+    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 70000, FAKE2, None) == DSA_ERR_INVALID_ARG  # k too large
+    assert L.dsa_topk(FAKE, 9, 1, 1, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # ld < n_kv
+    assert L.dsa_topk(FAKE, 10, 1, 11, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # n_q > n_kv
+    assert L.dsa_topk(FAKE, 10, 0, 1, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # B = 0
+    assert L.dsa_topk(FAKE, 10, 70000, 1, 10, 4, FAKE2, None) == DSA_ERR_UNSUPPORTED  # grid limit
+
+
+def test_indexer_validation(L):
+    from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_F32,
+                                             DSA_FP8_E4M3)
+    f = L.dsa_indexer_scores
+    ok_args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 8, 64, 128, DSA_FP8_E4M3, FAKE2, 8, None]
+    bad = list(ok_args); bad[0] = None
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = list(ok_args); bad[1] = None  # fp8 without q_scale
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = list(ok_args); bad[10] = DSA_F32  # fp32 with scales
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = list(ok_args); bad[10] = DSA_BF16
+    assert f(*bad) == DSA_ERR_UNSUPPORTED
+    bad = list(ok_args); bad[12] = 7  # ld < n_kv
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = list(ok_args); bad[7] = 3  # n_kv < n_q
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = list(ok_args); bad[8], bad[9] = 65, 128  # too many heads for any kernel
+    assert f(*bad) == DSA_ERR_UNSUPPORTED
+    bad = list(ok_args); bad[8], bad[9] = 64, 254  # generic kernel needs d_I % 4 == 0
+    assert f(*bad) == DSA_ERR_UNSUPPORTED
+
+
+def test_attention_validation_and_workspace(L):
+    from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE,
+                                             DSA_F32, DSA_FP8_E4M3)
+    f = L.dsa_sparse_mla_attn
+    # decode-like shape needs a split-k workspace
+    ws = L.dsa_sparse_mla_attn_workspace_size(4, 1, 4096, 128, 576, 512, 2048, DSA_BF16)
+    assert ws > 0
+    args = [FAKE, FAKE, FAKE, 4, 1, 4096, 128, 576, 512, 2048, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
+    assert f(*args) == DSA_ERR_WORKSPACE
+    args[14], args[15] = ctypes.c_void_p(0x30000 + 8), ws  # misaligned
+    assert f(*args) == DSA_ERR_WORKSPACE
+    args[14], args[15] = ctypes.c_void_p(0x30000), ws - 1  # too small
+    assert f(*args) == DSA_ERR_WORKSPACE
+    # many queries: no workspace needed
+    assert L.dsa_sparse_mla_attn_workspace_size(1, 4096, 4096, 128, 576, 512, 2048, DSA_BF16) == 0
+    bad = [FAKE, FAKE, None, 1, 1, 10, 128, 576, 512, 8, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
+    assert f(*bad) == DSA_ERR_INVALID_ARG
+    bad = [FAKE, FAKE, FAKE, 1, 1, 10, 64, 576, 512, 8, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
+    assert f(*bad) == DSA_ERR_UNSUPPORTED  # bf16 path is H=128 only
+    bad = [FAKE, FAKE, FAKE, 1, 1, 10, 8, 80, 96, 8, 0.1, DSA_F32, FAKE2, None, None, 0, None]
+    assert f(*bad) == DSA_ERR_INVALID_ARG  # d_v > d_qk
+    bad = [FAKE, FAKE, FAKE, 1, 1, 10, 8, 80, 64, 8, float("nan"), DSA_F32, FAKE2, None, None, 0, None]
+    assert f(*bad) == DSA_ERR_INVALID_ARG  # non-finite scale
+    bad = [FAKE, FAKE, FAKE, 1, 1, 10, 8, 80, 64, 8, 0.1, DSA_FP8_E4M3, FAKE2, None, None, 0, None]
+    assert f(*bad) == DSA_ERR_UNSUPPORTED
+    bad = [ctypes.c_void_p(0x10002), FAKE, FAKE, 1, 1, 10, 128, 576, 512, 8, 0.1, DSA_BF16, FAKE2, None, None, 0,
+           None]
+    assert f(*bad) == DSA_ERR_INVALID_ARG  # misaligned q on the bf16 path
+
+
+def test_forward_validation(L):
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_WORKSPACE, DSA_FP8_E4M3
+    n_q, n_kv, k = 64, 100, 32
+    ws = L.dsa_forward_workspace_size(1, n_q, n_kv, 128, 576, 512, k, DSA_BF16)
+    # scores rows are padded to 128 floats, the selection follows 256-byte aligned
+    assert ws >= n_q * 128 * 4 + n_q * k * 4
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, n_q, n_kv, 64, 128, 128, 576, 512, k, 0.04, DSA_FP8_E4M3,
+            DSA_BF16, FAKE2, None, None, ctypes.c_void_p(0x40000), ws - 256, None]
+    assert L.dsa_forward_prefill(*args) == DSA_ERR_WORKSPACE
+    args[23] = ws
+    args[0] = None
+    assert L.dsa_forward_prefill(*args) == DSA_ERR_INVALID_ARG
+    dargs = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, n_kv, 64, 128, 128, 576, 512, 0, 0.04, DSA_FP8_E4M3,
+             DSA_BF16, FAKE2, None, None, ctypes.c_void_p(0x40000), 1 << 30, None]
+    assert L.dsa_forward_decode(*dargs) == DSA_ERR_INVALID_ARG  # k = 0
+    assert L.dsa_forward_workspace_size(1, 10, 5, 128, 576, 512, k, DSA_BF16) == 0  # n_q > n_kv: invalid
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from sparse_attention_13_amd import dsa
+    monkeypatch.setattr(dsa, "_lib", None)
+    monkeypatch.setattr(dsa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        dsa.lib()

@@ -1,0 +1,428 @@
+"""HIP path vs the CPU oracle, through the C ABI, on the GPU.
+
+Small cases compare every element; the full-size workloads (prefill 8K and 32K, decode 64 x 131072,
+chunked 16 x 8192) are run in the launch configuration the benchmark times and compared on sampled
+rows plus properties that hold at any size.  Rules and tolerances: tests/parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from sparse_attention_13_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_13_amd import dsa as d
+    d.lib()
+    return d
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def deq_q(x, rows=None):
+    """Dequantised indexer queries (fp32) of the given query rows, via the oracle's decoder."""
+    import oracle
+    q8, qs = x["q8"], x["q_scale"]
+    if rows is not None:
+        q8, qs = q8[rows], qs[rows]
+    return oracle.dequant_e4m3(synth.u8(q8), qs.cpu().numpy())
+
+
+def deq_k(x):
+    import oracle
+    return oracle.dequant_e4m3(synth.u8(x["k8"]), x["k_scale"].cpu().numpy())
+
+
+def bf16_np(t):
+    import oracle
+    return oracle.bf16_to_f32(synth.bf16_bits(t))
+
+
+def stack_prefill(B, L, n_q, seed, n_needles=0, with_mla=False, **kw):
+    xs = [synth.prefill(L, seed=seed + b, device=DEV, n_needles=n_needles, n_q=n_q, with_mla=with_mla, **kw)
+          for b in range(B)]
+    keys = ["q8", "q_scale", "k8", "k_scale", "w"] + (["q", "kv"] if with_mla else [])
+    out = {k: torch.stack([x[k] for x in xs]).contiguous() for k in keys}
+    out["per_seq"] = xs
+    return out
+
+
+# ------------------------------------------------------------------------------------------ indexer
+
+def test_indexer_tiny_f32(orc, dsa):
+    x = synth.tiny(seed=0, device=DEV)
+    L = x["L"]
+    ld = L + 5
+    scores = torch.full((1, L, ld), float("nan"), device=DEV)
+    dsa.indexer_scores(x["q_i"][None].contiguous(), None, x["k_i"][None].contiguous(), None, x["w"][None].contiguous(),
+                       scores)
+    torch.cuda.synchronize()
+    g = np32(scores)[0]
+    pos = np.arange(L, dtype=np.int64)
+    o, mag, absmag = orc.indexer(np32(x["q_i"]), np32(x["w"]), np32(x["k_i"]), pos, ld=ld, with_mag=True)
+    e_mag, e_rel, n = parity.indexer_errors(g, o, mag, absmag, pos)
+    assert e_mag <= 1.0, (e_mag, e_rel)
+    for t in range(L):
+        assert np.all(np.isnan(g[t, t + 1:])), "entries beyond the query position must stay untouched"
+
+
+@pytest.mark.parametrize("B,L,n_q,needles", [(2, 1000, 300, 8), (1, 77, 77, 0), (1, 4099, 130, 16), (3, 515, 1, 0)])
+def test_indexer_fp8_vs_oracle(orc, dsa, B, L, n_q, needles):
+    x = stack_prefill(B, L, n_q, seed=11, n_needles=needles)
+    ld = L + 3
+    scores = torch.full((B, n_q, ld), float("nan"), device=DEV)
+    dsa.indexer_scores(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], scores)
+    torch.cuda.synchronize()
+    g = np32(scores)
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    for b, xb in enumerate(x["per_seq"]):
+        o, mag, absmag = orc.indexer(deq_q(xb), np32(xb["w"]), deq_k(xb), pos, ld=ld, with_mag=True)
+        e_mag, e_rel, n = parity.indexer_errors(g[b], o, mag, absmag, pos)
+        assert e_mag <= 1.0, (b, e_mag, e_rel)
+        for r, p in enumerate(pos):
+            assert np.all(np.isnan(g[b, r, p + 1:]))
+
+
+def test_indexer_fp8_exact_integers(orc, dsa):
+    """Integer-valued e4m3 inputs with power-of-two scales: every partial sum is an exact integer
+    below 2^24 on both sides, so the scores must agree bit for bit whatever the summation order."""
+    g = torch.Generator().manual_seed(5)
+    B, L, n_q, H, d = 2, 700, 200, 64, 128
+    qi = torch.randint(-4, 5, (B, n_q, H, d), generator=g).float()
+    ki = torch.randint(-4, 5, (B, L, d), generator=g).float()
+    wi = torch.randint(-3, 4, (B, n_q, H), generator=g).float()
+    q8 = (qi * 4).to(torch.float8_e4m3fn).view(torch.uint8)
+    k8 = (ki / 2).to(torch.float8_e4m3fn).view(torch.uint8)
+    qs = torch.full((B, n_q, H), 0.25)
+    ks = torch.full((B, L), 2.0)
+    scores = torch.zeros((B, n_q, L), device=DEV)
+    dsa.indexer_scores(q8.to(DEV), qs.to(DEV), k8.to(DEV), ks.to(DEV), wi.to(DEV), scores)
+    torch.cuda.synchronize()
+    gs = np32(scores)
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    for b in range(B):
+        o = orc.indexer(orc.dequant_e4m3(q8[b].numpy(), qs[b].numpy()), wi[b].numpy(),
+                        orc.dequant_e4m3(k8[b].numpy(), ks[b].numpy()), pos, ld=L)
+        for r, p in enumerate(pos):
+            assert np.array_equal(gs[b, r, : p + 1], o[r, : p + 1]), (b, r)
+
+
+# ------------------------------------------------------------------------------------------ top-k
+
+@pytest.mark.parametrize("n_kv,n_q,k,extra_ld", [(300, 300, 32, 0), (5000, 64, 2048, 7), (2048, 16, 2048, 1),
+                                                  (40000, 3, 2048, 0), (131072, 2, 2048, 64), (100, 100, 1, 0),
+                                                  (36736, 2, 4096, 0), (36737, 2, 4096, 0)])
+def test_topk_identical_scores_bit_exact(orc, dsa, n_kv, n_q, k, extra_ld):
+    gen = np.random.default_rng(n_kv + k)
+    ld = n_kv + extra_ld
+    s = gen.standard_normal((1, n_q, ld)).astype(np.float32)
+    pos = np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    for r, p in enumerate(pos):
+        s[0, r, p + 1:] = np.inf  # never to be read
+    idx = dsa.topk(torch.from_numpy(s).to(DEV), n_kv, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    oi, _ = orc.topk(s[0], pos, k)
+    assert np.array_equal(gi, oi)
+
+
+def test_topk_adversarial_rows(orc, dsa):
+    n_kv, n_q, k = 6000, 8, 2048
+    pos = np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    gen = np.random.default_rng(3)
+    s = np.zeros((1, n_q, n_kv), np.float32)
+    s[0, 0] = 1.5                                                       # all equal
+    s[0, 1] = np.where(gen.random(n_kv) < 0.5, -0.0, 0.0)              # signed zeros only
+    s[0, 2] = gen.choice(np.array([-1.0, 0.0, 2.0, 2.0, 7.0], np.float32), n_kv)  # long runs of ties
+    s[0, 3] = (gen.standard_normal(n_kv) * 1e-39).astype(np.float32)   # denormals
+    s[0, 4] = -np.inf
+    s[0, 4, ::3] = gen.standard_normal(len(range(0, n_kv, 3)))          # -inf mixed in
+    s[0, 5] = np.inf
+    s[0, 5, 100:200] = 1.0                                              # +inf ties
+    s[0, 6] = np.arange(n_kv, dtype=np.float32)                        # strictly increasing
+    s[0, 7] = -np.arange(n_kv, dtype=np.float32)                       # strictly decreasing
+    idx = dsa.topk(torch.from_numpy(s).to(DEV), n_kv, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    oi, _ = orc.topk(s[0], pos, k)
+    for r in range(n_q):
+        assert np.array_equal(gi[r], oi[r]), r
+    assert gi[0].tolist() == list(range(k))
+
+
+# ------------------------------------------------------------------------------------------ attention
+
+def _rand_idx(gen, n_kv, k, n_valid, interleave=False):
+    sel = np.sort(gen.choice(n_kv, size=n_valid, replace=False)).astype(np.int32)
+    row = np.full(k, -1, np.int32)
+    row[:n_valid] = sel
+    if interleave:
+        gen.shuffle(row)
+    return row
+
+
+def _attn_case(orc, dsa, B, n_q, n_kv, k, valid_counts, interleave, seed, peaked=False):
+    gen = np.random.default_rng(seed)
+    q = torch.randn((B, n_q, 128, 576), device=DEV).to(torch.bfloat16)
+    kv = torch.randn((B, n_kv, 576), device=DEV).to(torch.bfloat16)
+    idx = np.stack([np.stack([_rand_idx(gen, n_kv, k, valid_counts[(b * n_q + t) % len(valid_counts)], interleave)
+                              for t in range(n_q)]) for b in range(B)])
+    if peaked:  # one selected row dominates every head's softmax
+        for b in range(B):
+            for t in range(n_q):
+                s = int(idx[b, t][idx[b, t] >= 0][0])
+                q[b, t] = (kv[b, s].float() * 0.5).to(torch.bfloat16)
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx).to(DEV), 512, 1.0 / math.sqrt(576))
+    torch.cuda.synchronize()
+    go, gl = np32(out), np32(lse)
+    worst = (0.0, 0.0, 0.0)
+    for b in range(B):
+        o_out, o_lse = orc.sparse_attn(bf16_np(q[b]), bf16_np(kv[b]), idx[b], 512, 1.0 / math.sqrt(576))
+        r = parity.attention_errors(go[b], o_out, gl[b], o_lse)
+        worst = tuple(max(a, c) for a, c in zip(worst, r))
+    return worst
+
+
+def test_attention_bf16_split_path(orc, dsa):
+    # few query rows -> the selection is split across workgroups and merged
+    ratio, mx, lse_err = _attn_case(orc, dsa, B=2, n_q=3, n_kv=3000, k=2048, valid_counts=[2048, 1500, 33, 1, 2000, 64],
+                                    interleave=False, seed=1)
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
+
+
+def test_attention_bf16_interleaved_invalid(orc, dsa):
+    ratio, mx, lse_err = _attn_case(orc, dsa, B=1, n_q=4, n_kv=2500, k=2048, valid_counts=[1000, 2048, 7, 300],
+                                    interleave=True, seed=2)
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
+
+
+def test_attention_bf16_one_workgroup_per_query(orc, dsa):
+    # >= 512 query rows -> one workgroup per query, no split; short selections keep the oracle fast
+    ratio, mx, lse_err = _attn_case(orc, dsa, B=1, n_q=520, n_kv=4096, k=2048, valid_counts=[40, 70, 1, 33, 96],
+                                    interleave=False, seed=3)
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
+
+
+def test_attention_bf16_peaked(orc, dsa):
+    ratio, mx, lse_err = _attn_case(orc, dsa, B=1, n_q=2, n_kv=1000, k=256, valid_counts=[200, 37],
+                                    interleave=False, seed=4, peaked=True)
+    assert ratio <= 1.0 and lse_err <= 50 * parity.LSE_ABS, (ratio, mx, lse_err)
+
+
+def test_attention_f32_tiny(orc, dsa):
+    x = synth.tiny(seed=0, device=DEV)
+    L, k = x["L"], x["k"]
+    pos = np.arange(L, dtype=np.int64)
+    s = orc.indexer(np32(x["q_i"]), np32(x["w"]), np32(x["k_i"]), pos, ld=L)
+    oi, _ = orc.topk(s, pos, k)
+    out, lse = dsa.sparse_mla_attn(x["q"][None].contiguous(), x["kv"][None].contiguous(),
+                                   torch.from_numpy(oi[None]).to(DEV), x["d_v"], x["sm_scale"])
+    torch.cuda.synchronize()
+    o_out, o_lse = orc.sparse_attn(np32(x["q"]), np32(x["kv"]), oi, x["d_v"], x["sm_scale"])
+    assert np.abs(np32(out)[0] - o_out).max() <= 1e-5
+    assert np.abs(np32(lse)[0] - o_lse).max() <= 1e-5
+
+
+# ------------------------------------------------------------------------------------------ end to end
+
+def test_forward_tiny_f32_all_rows(orc, dsa):
+    x = synth.tiny(seed=0, device=DEV)
+    L, k = x["L"], x["k"]
+    idx_out = torch.empty((1, L, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q_i"][None].contiguous(), None, x["k_i"][None].contiguous(), None,
+                              x["w"][None].contiguous(), x["q"][None].contiguous(), x["kv"][None].contiguous(), k,
+                              x["d_v"], x["sm_scale"], idx_out=idx_out)
+    torch.cuda.synchronize()
+    pos = np.arange(L, dtype=np.int64)
+    res = orc.forward(np32(x["q_i"]), np32(x["w"]), np32(x["k_i"]), np32(x["q"]), np32(x["kv"]), pos, k, x["d_v"],
+                      x["sm_scale"])
+    gi = idx_out.cpu().numpy()[0]
+    ok, exact = parity.topk_band_match(gi, res["idx"], res["scores"], res["kth"], pos)
+    assert ok == L, (ok, exact)
+    o_out, o_lse = orc.sparse_attn(np32(x["q"]), np32(x["kv"]), gi, x["d_v"], x["sm_scale"])
+    assert np.abs(np32(out)[0] - o_out).max() <= 1e-5
+    assert np.abs(np32(lse)[0] - o_lse).max() <= 1e-5
+
+
+def _sample_rows(n_q, L, k, n, gen):
+    """First rows, rows around position k-1, last rows, and uniform others (query row indices)."""
+    base = L - n_q
+    cand = set(range(min(4, n_q))) | set(range(max(0, n_q - 4), n_q))
+    t_k = k - 1 - base
+    cand |= {t for t in range(t_k - 2, t_k + 3) if 0 <= t < n_q}
+    rest = n - len(cand)
+    if rest > 0:
+        cand |= set(int(v) for v in gen.choice(n_q, size=min(rest, n_q), replace=False))
+    return np.array(sorted(cand), dtype=np.int64)
+
+
+def check_forward_rows(orc, x, gpu_idx, gpu_out, gpu_lse, rows, L, n_q, k):
+    """Band-rule selection parity on `rows`, attention parity on the GPU's own selection."""
+    pos = (L - n_q + rows).astype(np.int64)
+    q_i = deq_q(x, torch.from_numpy(rows).to(x["q8"].device))
+    w = np32(x["w"][torch.from_numpy(rows).to(x["w"].device)])
+    k_i = deq_k(x)
+    sc = orc.indexer(q_i, w, k_i, pos, ld=L)
+    oi, kth = orc.topk(sc, pos, k)
+    gi = gpu_idx[rows]
+    parity.assert_idx_wellformed(gi, pos, k)
+    ok, exact = parity.topk_band_match(gi, oi, sc, kth, pos)
+    assert ok == len(rows), (ok, exact, len(rows))
+    qb = bf16_np(x["q"][torch.from_numpy(rows).to(x["q"].device)])
+    kvb = bf16_np(x["kv"])
+    o_out, o_lse = orc.sparse_attn(qb, kvb, gi, 512, 1.0 / math.sqrt(576))
+    ratio, mx, lse_err = parity.attention_errors(gpu_out[rows], o_out, gpu_lse[rows], o_lse)
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
+    return exact, oi, sc
+
+
+def run_prefill(dsa, x, k=2048, n_q=None):
+    L = x["L"]
+    n_q = x["n_q"] if n_q is None else n_q
+    idx = torch.empty((1, n_q, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None],
+                              x["q"][None], x["kv"][None], k, 512, 1.0 / math.sqrt(576), idx_out=idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()[0], np32(out)[0], np32(lse)[0]
+
+
+def test_forward_prefill_small_all_rows_selection(orc, dsa):
+    L, k = 2600, 2048
+    x = synth.prefill(L, seed=7, device=DEV, n_needles=16)
+    gi, go, gl = run_prefill(dsa, x, k)
+    pos = np.arange(L, dtype=np.int64)
+    sc = orc.indexer(deq_q(x), np32(x["w"]), deq_k(x), pos, ld=L)
+    oi, kth = orc.topk(sc, pos, k)
+    parity.assert_idx_wellformed(gi, pos, k)
+    ok, exact = parity.topk_band_match(gi, oi, sc, kth, pos)
+    assert ok == L, (ok, exact)
+    rows = _sample_rows(L, L, k, 24, np.random.default_rng(0))
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+
+
+def test_decode_equals_last_prefill_row(orc, dsa):
+    """Decode of a sequence == the last row of a prefill over the same caches (selection exactly)."""
+    L, k = 3000, 2048
+    x = synth.prefill(L, seed=8, device=DEV, n_needles=4, n_q=2)
+    gi_p, go_p, gl_p = run_prefill(dsa, x, k)
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"][-1:].contiguous(), x["q_scale"][-1:].contiguous(), x["k8"][None],
+                              x["k_scale"][None], x["w"][-1:].contiguous(), x["q"][-1:].contiguous(), x["kv"][None], k,
+                              512, 1.0 / math.sqrt(576), decode=True, idx_out=idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy()[0, 0], gi_p[-1])
+    d = np.abs(np32(out)[0] - go_p[-1])
+    assert d.max() <= 2e-2, d.max()
+    assert np.abs(np32(lse)[0] - gl_p[-1]).max() <= parity.LSE_ABS
+
+
+@pytest.mark.parametrize("B,S", [(4, 9000), (2, 40000)])
+def test_forward_decode_vs_oracle(orc, dsa, B, S):
+    x = synth.decode(B, S, seed=100, device=DEV)
+    k = 2048
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
+                              x["sm_scale"], decode=True, idx_out=idx)
+    torch.cuda.synchronize()
+    gi, go, gl = idx.cpu().numpy()[:, 0], np32(out), np32(lse)
+    pos = np.array([S - 1], np.int64)
+    for b in range(B):
+        q_i = orc.dequant_e4m3(synth.u8(x["q8"][b:b + 1]), x["q_scale"][b:b + 1].cpu().numpy())
+        k_i = orc.dequant_e4m3(synth.u8(x["k8"][b]), x["k_scale"][b].cpu().numpy())
+        sc = orc.indexer(q_i, np32(x["w"][b:b + 1]), k_i, pos, ld=S)
+        oi, kth = orc.topk(sc, pos, k)
+        ok, _ = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
+        assert ok == 1, b
+        o_out, o_lse = orc.sparse_attn(bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], 512, x["sm_scale"])
+        ratio, mx, lse_err = parity.attention_errors(go[b:b + 1], o_out, gl[b:b + 1], o_lse)
+        assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (b, ratio, mx, lse_err)
+
+
+# ------------------------------------------------------------------------------------------ full-size workloads
+
+def test_full_prefill_8k(orc, dsa):
+    L, k = 8192, 2048
+    x = synth.prefill(L, seed=0, device=DEV, n_needles=64, needle_layout="random")
+    gi, go, gl = run_prefill(dsa, x, k)
+    pos = np.arange(L, dtype=np.int64)
+    parity.assert_idx_wellformed(gi, pos, k)
+    rows = _sample_rows(L, L, k, 40, np.random.default_rng(1))
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+    # needle recall (sanity statistic): planted keys are selected by every later query
+    needles = x["needles"].numpy()
+    late = gi[-64:]
+    hit = np.mean([np.isin(needles[needles <= L - 64 + r], late[r]).mean() for r in range(64)])
+    assert hit > 0.99, hit
+
+
+def test_full_prefill_32k(orc, dsa):
+    L, k = 32768, 2048
+    x = synth.prefill(L, seed=0, device=DEV, n_needles=256, needle_layout="random")
+    gi, go, gl = run_prefill(dsa, x, k)
+    pos = np.arange(L, dtype=np.int64)
+    parity.assert_idx_wellformed(gi, pos, k)
+    rows = _sample_rows(L, L, k, 24, np.random.default_rng(2))
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+
+
+def test_full_decode_64x128k(orc, dsa):
+    B, S, k = 64, 131072, 2048
+    x = synth.decode(B, S, seed=0, device=DEV)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
+                              x["sm_scale"], decode=True, idx_out=idx)
+    torch.cuda.synchronize()
+    gi, go, gl = idx.cpu().numpy()[:, 0], np32(out), np32(lse)
+    parity.assert_idx_wellformed(gi, np.full(B, S - 1, np.int64), k)
+    pos = np.array([S - 1], np.int64)
+    for b in (0, 17, 63):
+        q_i = orc.dequant_e4m3(synth.u8(x["q8"][b:b + 1]), x["q_scale"][b:b + 1].cpu().numpy())
+        k_i = orc.dequant_e4m3(synth.u8(x["k8"][b]), x["k_scale"][b].cpu().numpy())
+        sc = orc.indexer(q_i, np32(x["w"][b:b + 1]), k_i, pos, ld=S)
+        oi, kth = orc.topk(sc, pos, k)
+        ok, _ = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
+        assert ok == 1, b
+        o_out, o_lse = orc.sparse_attn(bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], 512, x["sm_scale"])
+        ratio, mx, lse_err = parity.attention_errors(go[b:b + 1], o_out, gl[b:b + 1], o_lse)
+        assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (b, ratio, mx, lse_err)
+
+
+def test_full_chunked_128k_last_chunks(orc, dsa):
+    """16 chunks of 8192 queries over a 131072-token context: the last chunk against the oracle on sampled
+    rows, and chunking-invariance (two half chunks give bit-identical rows)."""
+    L, C, k = 131072, 8192, 2048
+    x = synth.prefill(L, seed=0, device=DEV, n_needles=1024, needle_layout="even", with_mla=True)
+    last = slice(L - C, L)
+
+    def chunk(lo, hi):
+        n_kv = hi
+        idx = torch.empty((1, hi - lo, k), dtype=torch.int32, device=DEV)
+        out, lse, _ = dsa.forward(x["q8"][None, lo:hi], x["q_scale"][None, lo:hi], x["k8"][None, :n_kv],
+                                  x["k_scale"][None, :n_kv], x["w"][None, lo:hi], x["q"][None, lo:hi],
+                                  x["kv"][None, :n_kv], k, 512, 1.0 / math.sqrt(576), idx_out=idx)
+        return idx, out, lse
+
+    for c in range(L // C):  # the whole chunked prefill runs, as in the workload
+        i_c, o_c, l_c = chunk(c * C, (c + 1) * C)
+    torch.cuda.synchronize()
+    gi, go, gl = i_c.cpu().numpy()[0], np32(o_c)[0], np32(l_c)[0]
+    i_a, o_a, l_a = chunk(L - C, L - C // 2)
+    i_b, o_b, l_b = chunk(L - C // 2, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.concatenate([i_a.cpu().numpy()[0], i_b.cpu().numpy()[0]]), gi)
+    assert np.array_equal(np.concatenate([np32(o_a)[0], np32(o_b)[0]]), go)
+    rows = np.array(sorted(set([0, 1, C - 1] + list(np.random.default_rng(3).choice(C, 9, replace=False)))),
+                    dtype=np.int64)
+    xs = {kk: x[kk] for kk in ["k8", "k_scale", "kv"]}
+    xs.update({kk: x[kk][last] for kk in ["q8", "q_scale", "w", "q"]})
+    check_forward_rows(orc, xs, gi, go, gl, rows, L, C, k)
