@@ -22,10 +22,8 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The sparse-MLA kernel keeps a 128x512 fp32 accumulator plus the query in
-# registers; the VGPR form of the matrix-core instructions lets the allocator split that state between
-# the VGPR and AGPR files without spilling.
-EXTRA = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none at present).
+EXTRA = {}
 
 
 def _compile(src: str, obj_dir: str) -> str:

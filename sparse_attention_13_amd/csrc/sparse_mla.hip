@@ -110,12 +110,15 @@ constexpr int kNB = 32;                        // selected rows per step
 constexpr int kRowChunks = kDQK * 2 / 16;      // 72 chunks of 16 B per latent row
 constexpr int kTileChunks = kRowChunks + 1;    // padded row: 73 chunks = 1168 B
 constexpr int kTileRowBytes = kTileChunks * 16;
-constexpr int kGatherInstr = (kNB * kTileChunks + 63) / 64;  // 37 wave-wide copies per step
-constexpr int kBufBytes = kGatherInstr * 64 * 16;            // 37888 B (the tail absorbs the last copy)
-constexpr int kOffBuf0 = 0;
-constexpr int kOffBuf1 = kBufBytes;
-constexpr int kOffP = 2 * kBufBytes;                // [4 head blocks][2 k-steps][64 lanes][16 B]
-constexpr int kOffAlpha = kOffP + 4 * 2 * 64 * 16;  // [128] f32
+constexpr int kGatherPerWave = 10;             // wave-wide 1 KiB copies per wave and step
+constexpr int kGatherInstr = 4 * kGatherPerWave;   // 40 >= 32 rows * 73 chunks / 64
+constexpr int kBufBytes = kGatherInstr * 1024;     // 40960 B (the tail absorbs the last copies)
+constexpr int kNBuf = 3;                           // steps in flight: the current one and two ahead
+constexpr int kMaxSel = 2048;                      // selection entries handled by one workgroup
+constexpr int kOffBuf = 0;
+constexpr int kOffP = kNBuf * kBufBytes;            // [4 head blocks][2 k-steps][64 lanes][16 B]
+constexpr int kOffSel = kOffP + 4 * 2 * 64 * 16;    // [kMaxSel] i32, the workgroup's selection
+constexpr int kOffAlpha = kOffSel + kMaxSel * 4;    // [128] f32
 constexpr int kOffRFlag = kOffAlpha + kH * 4;       // [4] u32 per-wave "rescaled" bits
 constexpr int kOffL = kOffRFlag + 64;               // [128] f32
 constexpr int kOffM = kOffL + kH * 4;               // [128] f32
@@ -124,36 +127,58 @@ constexpr int kLdsBytes = kOffMisc + 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+static_assert(kGatherInstr * 64 >= kNB * kTileChunks, "gather covers the tile");
+static_assert(kLdsBytes <= 163840, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bool valid_entry(int s, int n_kv) { return s >= 0 && s < n_kv; }
 
-// Copy the 32 rows of one step into an LDS buffer: wave-wide copy number c covers tile chunks
-// 64c .. 64c+63 (row = chunk / 73, column = chunk % 73; column 72 is padding, chunks past the
-// tile go to the buffer's tail).  Invalid selections copy row 0 (their scores are masked).
-__device__ __forceinline__ void gather_step(const char* __restrict__ kvb, const int32_t* __restrict__ sel,
-                                            int e0, int e_end, int n_kv, char* buf, int wave, int lane) {
-  for (int c = wave; c < kGatherInstr; c += 4) {
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait for this wave's LDS operations, then meet the other waves.  No vector-memory wait: copies
+// into other LDS buffers stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy the 32 rows of one step into an LDS buffer: wave-wide copy c (c = wave + 4j) covers tile
+// chunks 64c .. 64c+63 (row = chunk / 73, column = chunk % 73; column 72 is padding, chunks past the
+// tile land in the buffer's tail).  Row indices come from the LDS copy of the selection (-1 =
+// invalid, which copies row 0: its scores are masked).  Exactly kGatherPerWave copies per wave.
+__device__ __forceinline__ void gather_step(const char* __restrict__ kvb, const int* sel_l, int e0, int e_n,
+                                            char* buf, int wave, int lane) {
+  int srow[kGatherPerWave];
+#pragma unroll
+  for (int j = 0; j < kGatherPerWave; j++) {  // all selection reads first (no wait between them)
+    const int p = (wave + 4 * j) * 64 + lane;
+    const int r = p / kTileChunks;
+    const int e = max(0, min(e0 + min(r, kNB - 1), e_n - 1));  // in bounds; replaced below if unused
+    srow[j] = sel_l[e];
+  }
+#pragma unroll
+  for (int j = 0; j < kGatherPerWave; j++) {
+    const int c = wave + 4 * j;
     const int p = c * 64 + lane;
-    int r = p / kTileChunks;
+    const int r = p / kTileChunks;
     int col = p - r * kTileChunks;
-    int s = 0;
-    if (r < kNB && e0 + r < e_end) {
-      int v = sel[e0 + r];
-      s = valid_entry(v, n_kv) ? v : 0;
-    }
-    if (col >= kRowChunks) col = 0;
+    const int s = (r < kNB && e0 + r < e_n && srow[j] >= 0) ? srow[j] : 0;
+    col = col >= kRowChunks ? 0 : col;
     const char* src = kvb + (size_t)s * (kDQK * 2) + col * 16;
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + c * 1024), 16, 0, 0);
   }
 }
 
 // Bit i set <=> selection entry e0 + i (i < 32) is a valid row.
-__device__ __forceinline__ unsigned int step_valid_mask(const int32_t* __restrict__ sel, int e0, int e_end,
-                                                        int n_kv, int lane) {
-  bool v = false;
-  if (lane < kNB && e0 + lane < e_end) v = valid_entry(sel[e0 + lane], n_kv);
+__device__ __forceinline__ unsigned int step_valid_mask(const int* sel_l, int e0, int e_n, int lane) {
+  bool v = (lane < kNB && e0 + lane < e_n) ? (sel_l[e0 + lane] >= 0) : false;
   return (unsigned int)(__ballot(v) & 0xFFFFFFFFull);
 }
 
@@ -162,7 +187,8 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 int n_q, int n_kv, int k, float sm_scale, int n_split, int per_split, uint16_t* __restrict__ out,
                 float* __restrict__ lse, float* __restrict__ part, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x % n_split;
   const int t = blockIdx.x / n_split;
   const int b = blockIdx.y;
@@ -170,24 +196,29 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   const int32_t* sel = idx + row * k;
   const char* kvb = (const char*)(kv + (size_t)b * n_kv * kDQK);
   const int e_begin = split * per_split;
-  const int e_end = min(k, e_begin + per_split);
+  const int e_n = max(0, min(k, e_begin + per_split) - e_begin);  // <= kMaxSel entries
 
   int* misc = (int*)(smem + kOffMisc);
+  int* sel_l = (int*)(smem + kOffSel);
   float* alpha_l = (float*)(smem + kOffAlpha);
   unsigned int* rflag = (unsigned int*)(smem + kOffRFlag);
 
-  // extent of this part of the selection: up to its last valid entry
+  // this workgroup's part of the selection -> LDS (invalid entries as -1), and its extent
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   {
     int last = -1;
-    for (int e = e_begin + tid; e < e_end; e += 256)
-      if (valid_entry(sel[e], n_kv)) last = e;
+    for (int e = tid; e < e_n; e += 256) {
+      const int v = sel[e_begin + e];
+      const bool ok = valid_entry(v, n_kv);
+      sel_l[e] = ok ? v : -1;
+      if (ok) last = e;
+    }
     for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
     if (lane == 0) atomicMax(&misc[0], last);
   }
   __syncthreads();
-  const int n_span = misc[0] < 0 ? 0 : misc[0] + 1 - e_begin;
+  const int n_span = misc[0] + 1;
   const int n_steps = (n_span + kNB - 1) / kNB;
 
   // Q^T fragments of this wave's 32 heads: lane holds head 32w + l%32, dims 16ks + 8(l/32) .. +8
@@ -208,41 +239,48 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   float m_run = -INFINITY, l_run = 0.f;
   const float c_scale = sm_scale * kLog2e;
 
-  unsigned int vmask_cur = 0, vmask_next = 0;
-  if (n_steps > 0) {
-    gather_step(kvb, sel, e_begin, e_end, n_kv, smem + kOffBuf0, wave, lane);
-    vmask_cur = step_valid_mask(sel, e_begin, e_end, n_kv, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  char* buf = smem + kOffBuf0;
-  char* nbuf = smem + kOffBuf1;
-  for (int it = 0; it < n_steps; it++) {
-    const int e0 = e_begin + it * kNB;
-    if (it + 1 < n_steps) {
-      gather_step(kvb, sel, e0 + kNB, e_end, n_kv, nbuf, wave, lane);
-      vmask_next = step_valid_mask(sel, e0 + kNB, e_end, n_kv, lane);
-    }
-
-    // ---- S^T = K . Q^T for this wave's heads
-    v16f sacc;
+  // prologue: steps 0 and 1 in flight (unconditionally: entries past the selection copy row 0),
+  // then wait for the query fragments (loaded before the copies, so the copies stay in flight;
+  // otherwise every step would wait for all copies) and for step 0
+  gather_step(kvb, sel_l, 0, e_n, smem + kOffBuf, wave, lane);
+  gather_step(kvb, sel_l, kNB, e_n, smem + kOffBuf + kBufBytes, wave, lane);
 #pragma unroll
-    for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+  for (int ks = 0; ks < kDQK / 16; ks++) asm volatile("" ::"v"(qf[ks]));
+  wait_vmcnt<kGatherPerWave>();
+  lds_barrier();
+
+  int cur = 0;
+  for (int it = 0; it < n_steps; it++) {
+    char* buf = smem + kOffBuf + cur * kBufBytes;
+    const int e0 = it * kNB;
+    const bool ahead2 = it + 2 < n_steps;
+    if (ahead2) {
+      int nb = cur + 2;
+      nb = nb >= kNBuf ? nb - kNBuf : nb;
+      gather_step(kvb, sel_l, e0 + 2 * kNB, e_n, smem + kOffBuf + nb * kBufBytes, wave, lane);
+    }
+    const unsigned int vmask = step_valid_mask(sel_l, e0, e_n, lane);
+
+    // ---- S^T = K . Q^T for this wave's heads (S kept in VGPRs: the AGPR file holds O)
+    v16f sacc;
     {
       const char* kp = buf + (lane & 31) * kTileRowBytes + (lane >> 5) * 16;
-#pragma unroll
-      for (int ks = 0; ks < kDQK / 16; ks++) {
-        v8bf kf = *(const v8bf*)(kp + ks * 32);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
+      {
+        v8bf kf = *(const v8bf*)(kp);
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(kf), "v"(qf[0]));
       }
+#pragma unroll
+      for (int ks = 1; ks < kDQK / 16; ks++) {
+        v8bf kf = *(const v8bf*)(kp + ks * 32);
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(kf), "v"(qf[ks]));
+      }
+      asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
     }
 
     // ---- online softmax: this lane = head 32w + l%32; its 16 values are keys 8(r/4) + 4(l/32) + r%4
     float x[16];
     float bm = -INFINITY;
-    const unsigned int vm = vmask_cur >> (4 * (lane >> 5));
+    const unsigned int vm = vmask >> (4 * (lane >> 5));
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       x[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] * c_scale : -INFINITY;
@@ -251,7 +289,7 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     bm = xor32_max(bm);
     float alpha = 1.f;
     if (bm > m_run + kRescaleThreshold) {
-      alpha = exp2f(m_run - bm);  // 0 when m_run = -inf
+      alpha = __builtin_amdgcn_exp2f(m_run - bm);  // 0 when m_run = -inf
       m_run = bm;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -259,7 +297,7 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     unsigned int pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float p0 = exp2f(x[r] - m_use), p1 = exp2f(x[r + 1] - m_use);
+      float p0 = __builtin_amdgcn_exp2f(x[r] - m_use), p1 = __builtin_amdgcn_exp2f(x[r + 1] - m_use);
       psum += p0 + p1;
       pk[r >> 1] = pack_bf16x2(p0, p1);
     }
@@ -272,9 +310,9 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
       unsigned long long any = __ballot(alpha != 1.f);
       if (lane == 0) rflag[wave] = any ? 1u : 0u;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- rescale O^T where some head's running max moved
+    // ---- rescale O^T where some head's running max moved (rare after the first step)
     if (rflag[0] | rflag[1] | rflag[2] | rflag[3]) {
 #pragma unroll
       for (int hb = 0; hb < 4; hb++) {
@@ -282,14 +320,49 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
         for (int db = 0; db < 4; db++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) o[db][hb][r] *= a;
+          for (int r = 0; r < 16; r++) {
+            // scale the accumulator in place in the AGPR file
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(o[db][hb][r]), "=&v"(tmp) : "v"(a));
+          }
       }
+      asm volatile("s_nop 4" ::: "memory");
     }
 
     // ---- O^T[d][h] += V^T[d][keys] . P^T[keys][h]
     {
       const int G = lane >> 4, j = lane & 15;
       const u32x4* pl = (const u32x4*)(smem + kOffP);
+      // V^T fragments of both 16-key halves: 16 transposing LDS reads issued together and waited for
+      // inside the same asm block (the values are complete when the block ends)
+      const unsigned int vbase =
+          (unsigned int)(uintptr_t)(lds_void*)(buf + (4 * (G >> 1) + (j >> 2)) * kTileRowBytes +
+                                               (128 * wave + 16 * (G & 1) + 4 * (j & 3)) * 2);
+      u32x2 vr[2][4][2];
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+          "ds_read_b64_tr_b16 %1, %16 offset:9344\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
+          "ds_read_b64_tr_b16 %3, %16 offset:9408\n\t"
+          "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+          "ds_read_b64_tr_b16 %5, %16 offset:9472\n\t"
+          "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
+          "ds_read_b64_tr_b16 %7, %16 offset:9536\n\t"
+          "ds_read_b64_tr_b16 %8, %16 offset:18688\n\t"
+          "ds_read_b64_tr_b16 %9, %16 offset:28032\n\t"
+          "ds_read_b64_tr_b16 %10, %16 offset:18752\n\t"
+          "ds_read_b64_tr_b16 %11, %16 offset:28096\n\t"
+          "ds_read_b64_tr_b16 %12, %16 offset:18816\n\t"
+          "ds_read_b64_tr_b16 %13, %16 offset:28160\n\t"
+          "ds_read_b64_tr_b16 %14, %16 offset:18880\n\t"
+          "ds_read_b64_tr_b16 %15, %16 offset:28224\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vr[0][0][0]), "=&v"(vr[0][0][1]), "=&v"(vr[0][1][0]), "=&v"(vr[0][1][1]), "=&v"(vr[0][2][0]),
+            "=&v"(vr[0][2][1]), "=&v"(vr[0][3][0]), "=&v"(vr[0][3][1]), "=&v"(vr[1][0][0]), "=&v"(vr[1][0][1]),
+            "=&v"(vr[1][1][0]), "=&v"(vr[1][1][1]), "=&v"(vr[1][2][0]), "=&v"(vr[1][2][1]), "=&v"(vr[1][3][0]),
+            "=&v"(vr[1][3][1])
+          : "v"(vbase));
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ks2++) {
         v8bf pf[4];
@@ -297,26 +370,21 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         for (int hb = 0; hb < 4; hb++) pf[hb] = __builtin_bit_cast(v8bf, pl[(hb * 2 + ks2) * 64 + lane]);
 #pragma unroll
         for (int db = 0; db < 4; db++) {
-          const int dcol = 128 * wave + 32 * db + 16 * (G & 1) + 4 * (j & 3);
-          const int srow = 16 * ks2 + 4 * (G >> 1) + (j >> 2);
-          const char* a0 = buf + srow * kTileRowBytes + dcol * 2;
-          const char* a1 = a0 + 8 * kTileRowBytes;
-          v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0));
-          v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a1));
-          v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const u32x4 v4 = {vr[ks2][db][0][0], vr[ks2][db][0][1], vr[ks2][db][1][0], vr[ks2][db][1][1]};
+          const v8bf vf = __builtin_bit_cast(v8bf, v4);
 #pragma unroll
           for (int hb = 0; hb < 4; hb++)
             o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hb], o[db][hb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    vmask_cur = vmask_next;
-    char* tb = buf;
-    buf = nbuf;
-    nbuf = tb;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // step it+1's rows must have landed (step it+2's copies may stay in flight)
+    if (ahead2)
+      wait_vmcnt<kGatherPerWave>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    cur = cur + 1 == kNBuf ? 0 : cur + 1;
   }
 
   // ---- epilogue: publish per-head (m, l), normalise, store
@@ -411,12 +479,15 @@ size_t mla_bf16_workspace_bytes(int B, int n_q, int n_split) {
 
 int mla_bf16_pick_split(int B, int n_q, int k) {
   const long long rows = (long long)B * n_q;
-  if (rows >= 512) return 1;
-  // aim for >= 256 workgroups, each with at least 4 steps of 32 rows
-  int split = (int)((256 + rows - 1) / rows);
-  int max_split = (k + 4 * kNB - 1) / (4 * kNB);
-  if (split > max_split) split = max_split;
-  return split < 1 ? 1 : split;
+  const int min_split = (k + kMaxSel - 1) / kMaxSel;  // one workgroup holds at most kMaxSel entries
+  int split = 1;
+  if (rows < 512) {
+    // aim for >= 256 workgroups, each with at least 4 steps of 32 rows
+    split = (int)((256 + rows - 1) / rows);
+    const int max_split = (k + 4 * kNB - 1) / (4 * kNB);
+    if (split > max_split) split = max_split;
+  }
+  return split < min_split ? min_split : (split < 1 ? 1 : split);
 }
 
 hipError_t launch_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int n_q, int n_kv,
