@@ -20,18 +20,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even (inputs here are finite).
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing is the hardware round-to-nearest-even conversion.
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
   return __uint_as_float(((unsigned int)b) << 16);
 }
-__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
-  unsigned int u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
-// Two fp32 -> packed bf16x2 (low half = a).
+// Two fp32 -> packed bf16x2 (low half = a): one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
-  return (unsigned int)f32_to_bf16_bits(a) | ((unsigned int)f32_to_bf16_bits(b) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  return (unsigned short)(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 
 // OCP e4m3fn byte -> fp32 through the hardware converter.

@@ -107,19 +107,23 @@ constexpr int kH = 128;
 constexpr int kDQK = 576;
 constexpr int kDV = 512;
 constexpr int kNB = 32;                        // selected rows per step
-constexpr int kRowChunks = kDQK * 2 / 16;      // 72 chunks of 16 B per latent row
-constexpr int kTileChunks = kRowChunks + 1;    // padded row: 73 chunks = 1168 B
-constexpr int kTileRowBytes = kTileChunks * 16;
-constexpr int kGatherPerWave = 10;             // wave-wide 1 KiB copies per wave and step
-constexpr int kGatherInstr = 4 * kGatherPerWave;   // 40 >= 32 rows * 73 chunks / 64
-constexpr int kBufBytes = kGatherInstr * 1024;     // 40960 B (the tail absorbs the last copies)
-constexpr int kNBuf = 3;                           // steps in flight: the current one and two ahead
+// Step tile in LDS.  Region A: the 512 latent columns (1 KiB) of each row at a 1072-byte stride (the
+// padding makes both the 16-byte K-fragment reads and the transposing V reads bank-conflict free).
+// Region B: the 64 rope columns (128 B) of each row, 16-byte chunks XOR-swizzled by (row>>1)&7.
+// One wave-wide 1 KiB copy brings a row's region A (lane l copies chunk l), four copies bring region B
+// for 8 rows each: 36 copies per step, 9 per wave.
+constexpr int kRowA = 1072;
+constexpr int kTileA = kNB * kRowA;                  // 34304 B
+constexpr int kTileBytes = kTileA + kNB * 128;       // 38400 B
+constexpr int kGatherPerWave = 9;
+constexpr int kNBuf = 3;                           // tiles: step i-1 (PV), step i (QK), step i+1 (landing)
 constexpr int kMaxSel = 2048;                      // selection entries handled by one workgroup
+constexpr int kPBytes = 4 * 2 * 64 * 16;           // P^T fragments of one step: [4 head blocks][2][64][16 B]
 constexpr int kOffBuf = 0;
-constexpr int kOffP = kNBuf * kBufBytes;            // [4 head blocks][2 k-steps][64 lanes][16 B]
-constexpr int kOffSel = kOffP + 4 * 2 * 64 * 16;    // [kMaxSel] i32, the workgroup's selection
-constexpr int kOffAlpha = kOffSel + kMaxSel * 4;    // [128] f32
-constexpr int kOffRFlag = kOffAlpha + kH * 4;       // [4] u32 per-wave "rescaled" bits
+constexpr int kOffP = kNBuf * kTileBytes;           // two P buffers (step parity)
+constexpr int kOffSel = kOffP + 2 * kPBytes;        // [kMaxSel] i32, the workgroup's selection
+constexpr int kOffAlpha = kOffSel + kMaxSel * 4;    // [2][128] f32 rescale factors (step parity)
+constexpr int kOffRFlag = kOffAlpha + 2 * kH * 4;   // [2][4] u32 per-wave "rescaled" bits
 constexpr int kOffL = kOffRFlag + 64;               // [128] f32
 constexpr int kOffM = kOffL + kH * 4;               // [128] f32
 constexpr int kOffMisc = kOffM + kH * 4;            // [16] i32
@@ -127,52 +131,54 @@ constexpr int kLdsBytes = kOffMisc + 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
-static_assert(kGatherInstr * 64 >= kNB * kTileChunks, "gather covers the tile");
 static_assert(kLdsBytes <= 163840, "LDS budget");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bool valid_entry(int s, int n_kv) { return s >= 0 && s < n_kv; }
 
-// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
-// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Wait for this wave's LDS operations, then meet the other waves.  No vector-memory wait: copies
-// into other LDS buffers stay in flight across the barrier.
+// Wait until no vector-memory operation of this wave is outstanding (expcnt and lgkmcnt untouched).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// Wait for this wave's LDS operations, then meet the other waves.  No vector-memory wait is implied.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Copy the 32 rows of one step into an LDS buffer: wave-wide copy c (c = wave + 4j) covers tile
-// chunks 64c .. 64c+63 (row = chunk / 73, column = chunk % 73; column 72 is padding, chunks past the
-// tile land in the buffer's tail).  Row indices come from the LDS copy of the selection (-1 =
-// invalid, which copies row 0: its scores are masked).  Exactly kGatherPerWave copies per wave.
-__device__ __forceinline__ void gather_step(const char* __restrict__ kvb, const int* sel_l, int e0, int e_n,
-                                            char* buf, int wave, int lane) {
-  int srow[kGatherPerWave];
-#pragma unroll
-  for (int j = 0; j < kGatherPerWave; j++) {  // all selection reads first (no wait between them)
-    const int p = (wave + 4 * j) * 64 + lane;
-    const int r = p / kTileChunks;
-    const int e = max(0, min(e0 + min(r, kNB - 1), e_n - 1));  // in bounds; replaced below if unused
-    srow[j] = sel_l[e];
+// Rows of one step copied by this wave: region A of rows w, w+4, ..., w+28 and region B of rows
+// 8w .. 8w+7 (lane l: row 8w + l/8).  Entries past the selection or invalid (-1) copy row 0, whose
+// scores are masked.  Row indices come from the LDS copy of the selection; lane i < 8 holds the
+// region-A row of copy i (read back with readlane), every lane holds its region-B row.
+struct GatherRows {
+  int a;  // lanes 0..7: latent row of copy i
+  int b;  // rope row of this lane
+};
+__device__ __forceinline__ GatherRows gather_rows(const int* sel_l, int e0, int e_n, int wave, int lane) {
+  GatherRows g;
+  {
+    const int e = e0 + wave + 4 * (lane & 7);
+    const int v = sel_l[max(0, min(e, e_n - 1))];
+    g.a = (e < e_n && v >= 0) ? v : 0;
   }
-#pragma unroll
-  for (int j = 0; j < kGatherPerWave; j++) {
-    const int c = wave + 4 * j;
-    const int p = c * 64 + lane;
-    const int r = p / kTileChunks;
-    int col = p - r * kTileChunks;
-    const int s = (r < kNB && e0 + r < e_n && srow[j] >= 0) ? srow[j] : 0;
-    col = col >= kRowChunks ? 0 : col;
-    const char* src = kvb + (size_t)s * (kDQK * 2) + col * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + c * 1024), 16, 0, 0);
+  const int e = e0 + 8 * wave + (lane >> 3);
+  const int v = sel_l[max(0, min(e, e_n - 1))];
+  g.b = (e < e_n && v >= 0) ? v : 0;
+  return g;
+}
+// Copy number j (0..8) of this wave into `tile`: j < 8 -> region A of row w + 4j (lane l: chunk l);
+// j == 8 -> region B of rows 8w .. 8w+7 (stored chunk l%8 holds rope chunk (l%8) ^ ((row>>1)&7)).
+__device__ __forceinline__ void gather_copy(const char* __restrict__ kvb, const GatherRows& g, int j, char* tile,
+                                            int wave, int lane) {
+  if (j < 8) {
+    const int s = __builtin_amdgcn_readlane(g.a, j);
+    const char* src = kvb + (size_t)s * (kDQK * 2) + lane * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tile + (wave + 4 * j) * kRowA), 16, 0, 0);
+  } else {
+    const int rb = 8 * wave + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rb >> 1) & 7);
+    const char* src = kvb + (size_t)g.b * (kDQK * 2) + 1024 + chunk * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tile + kTileA + wave * 1024), 16, 0, 0);
   }
 }
 
@@ -180,6 +186,179 @@ __device__ __forceinline__ void gather_step(const char* __restrict__ kvb, const 
 __device__ __forceinline__ unsigned int step_valid_mask(const int* sel_l, int e0, int e_n, int lane) {
   bool v = (lane < kNB && e0 + lane < e_n) ? (sel_l[e0 + lane] >= 0) : false;
   return (unsigned int)(__ballot(v) & 0xFFFFFFFFull);
+}
+
+// V^T fragments of one 16-key half (ks2) of a step for this wave's 128 output columns: 8 transposing
+// LDS reads issued together and completed inside the same asm block.  vr[db][0/1]: keys
+// 16ks2 + (0..7 | 8..15 in the permuted key order), columns 128w + 32db + l%32.
+// Offsets: +64 B per 32-column block, +8 rows (8576 B) for the second read of a fragment.
+template <int KS2>
+__device__ __forceinline__ void load_vfrags(const char* tile, int wave, int lane, u32x2 (&vr)[4][2]) {
+  const int G = lane >> 4, j = lane & 15;
+  const unsigned int vbase =
+      (unsigned int)(uintptr_t)(lds_void*)(tile + (16 * KS2 + 4 * (G >> 1) + (j >> 2)) * kRowA +
+                                           (128 * wave + 16 * (G & 1) + 4 * (j & 3)) * 2);
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:8576\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:8640\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:8704\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:8768\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vr[0][0]), "=&v"(vr[0][1]), "=&v"(vr[1][0]), "=&v"(vr[1][1]), "=&v"(vr[2][0]), "=&v"(vr[2][1]),
+        "=&v"(vr[3][0]), "=&v"(vr[3][1])
+      : "v"(vbase));
+}
+
+__device__ __forceinline__ v8bf vfrag(const u32x2 (&vr)[4][2], int db) {
+  const u32x4 v4 = {vr[db][0][0], vr[db][0][1], vr[db][1][0], vr[db][1][1]};
+  return __builtin_bit_cast(v8bf, v4);
+}
+
+// O^T *= alpha (per head column) in place in the AGPR file, when some head of the step rescaled.
+__device__ __forceinline__ void rescale_o(v16f (&o)[4][4], const float* alpha_l, int lane) {
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++) {
+    const float a = alpha_l[32 * hb + (lane & 31)];
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float tmp;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(o[db][hb][r]), "=&v"(tmp)
+                     : "v"(a));
+      }
+  }
+  asm volatile("s_nop 4" ::: "memory");
+}
+
+struct PipeState {
+  float m;  // running max (log2 units, scaled), per head of this lane
+  float l;  // running sum of exp2(. - m)
+};
+
+// One pipeline iteration (see the kernel): QK of step `it` (if DO_QK) with the copies of step it+1,
+// then PV of step it-1 (if DO_PV) interleaved with the softmax of step it, then one barrier.
+template <bool DO_QK, bool DO_PV>
+__device__ __forceinline__ bool pipeline_step(int it, int n_steps, int e_n, const char* __restrict__ kvb, char* smem,
+                                              const int* sel_l, const v8bf (&qf)[kDQK / 16], v16f (&o)[4][4],
+                                              PipeState& st, float c_scale, int wave, int lane) {
+  const int cur = it % kNBuf;
+  const int prv = (it + kNBuf - 1) % kNBuf;
+  const int nxt = (it + 1) % kNBuf;
+  char* tile = smem + kOffBuf + cur * kTileBytes;
+  char* ptile = smem + kOffBuf + prv * kTileBytes;
+  char* ntile = smem + kOffBuf + nxt * kTileBytes;
+  const int e0 = it * kNB;
+  // The copies for step it+1 are issued unconditionally: after the last step they fill a free tile
+  // with row 0 (never read), which keeps the instruction stream free of branches.
+  constexpr bool has_next = DO_QK;
+
+  v16f sacc;
+  unsigned int vmask = 0;
+  GatherRows g;
+  if (DO_QK) {
+    g = gather_rows(sel_l, e0 + kNB, e_n, wave, lane);
+    vmask = step_valid_mask(sel_l, e0, e_n, lane);
+    // K fragments: 36 16-byte reads (32 from region A, 4 from the swizzled region B), kept 8 ahead
+    // of the dependent chain of matrix-core instructions
+    const char* kp = tile + (lane & 31) * kRowA + (lane >> 5) * 16;
+    const int rr = lane & 31;
+    const char* kb = tile + kTileA + rr * 128;
+    const int sw = (rr >> 1) & 7;
+    constexpr int kDepth = 8;
+    v8bf kf[kDepth];
+#pragma unroll
+    for (int ks = 0; ks < kDepth; ks++) kf[ks] = *(const v8bf*)(kp + ks * 32);
+#pragma unroll
+    for (int ks = 0; ks < kDQK / 16; ks++) {
+      if (ks == 0)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(kf[0]), "v"(qf[0]));
+      else
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(kf[ks % kDepth]), "v"(qf[ks]));
+      const int nk = ks + kDepth;
+      if (nk < 32)
+        kf[ks % kDepth] = *(const v8bf*)(kp + nk * 32);
+      else if (nk < kDQK / 16)
+        kf[ks % kDepth] = *(const v8bf*)(kb + (((2 * (nk - 32) + (lane >> 5)) ^ sw) << 4));
+    }
+    asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
+  }
+
+  // PV of step it-1 (the caller has already rescaled O if that step moved some head's max)
+  const int pp = (it + 1) & 1;  // parity of step it-1
+  u32x2 vr[4][2];
+  if (DO_PV) load_vfrags<0>(ptile, wave, lane, vr);
+  const u32x4* pl = (const u32x4*)(smem + kOffP + pp * kPBytes);
+
+  // online softmax of step it: this lane = head 32w + l%32, its 16 values are keys 8(r/4) + 4(l/32) + r%4
+  float x[16];
+  float alpha = 1.f, neg_m = 0.f;
+  if (DO_QK) {
+    if (vmask == 0xFFFFFFFFu) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[r] = sacc[r];
+    } else {
+      const unsigned int vm = vmask >> (4 * (lane >> 5));
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, x[r]), x[r + 1]);
+    bm = fmaxf(bm, x[15]);
+    bm = xor32_max(bm) * c_scale;
+    if (bm > st.m + kRescaleThreshold) {
+      alpha = __builtin_amdgcn_exp2f(st.m - bm);  // 0 when m = -inf
+      st.m = bm;
+    }
+    neg_m = (st.m == -INFINITY) ? 0.f : -st.m;
+  }
+  float psum = 0.f;
+  unsigned int pk[8];
+#pragma unroll
+  for (int g8 = 0; g8 < 8; g8++) {
+    if (has_next) gather_copy(kvb, g, g8, ntile, wave, lane);
+    if (DO_PV) {
+      const int ks2 = g8 >> 2, db = g8 & 3;
+      if (g8 == 4) load_vfrags<1>(ptile, wave, lane, vr);
+      const v8bf vf = vfrag(vr, db);
+#pragma unroll
+      for (int hb = 0; hb < 4; hb++) {
+        const v8bf pf = __builtin_bit_cast(v8bf, pl[(hb * 2 + ks2) * 64 + lane]);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db][hb], 0, 0, 0);
+      }
+    }
+    if (DO_QK) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * g8], c_scale, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[2 * g8 + 1], c_scale, neg_m));
+      psum += p0 + p1;
+      pk[g8] = pack_bf16x2(p0, p1);
+    }
+  }
+  if (has_next) gather_copy(kvb, g, 8, ntile, wave, lane);
+  if (DO_QK) {
+    st.l = st.l * alpha + xor32_sum(psum);
+    const int pc = it & 1;
+    u32x4* plw = (u32x4*)(smem + kOffP + pc * kPBytes);
+    plw[(wave * 2 + 0) * 64 + lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    plw[(wave * 2 + 1) * 64 + lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    if (lane < 32) ((float*)(smem + kOffAlpha))[kH * pc + 32 * wave + lane] = alpha;
+    const unsigned long long any = __ballot(alpha != 1.f);
+    if (lane == 0) ((unsigned int*)(smem + kOffRFlag))[4 * pc + wave] = any ? 1u : 0u;
+  }
+  // step it+1's rows have landed (this wave's copies), then meet: every wave's copies landed, step
+  // it's P^T is published and step it-1's tile is free
+  wait_vmcnt0();
+  lds_barrier();
+  // did step it move the running max of some head (anywhere in the workgroup)?
+  if (!DO_QK) return false;
+  const unsigned int* rf = (const unsigned int*)(smem + kOffRFlag) + 4 * (it & 1);
+  return (rf[0] | rf[1] | rf[2] | rf[3]) != 0u;
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
@@ -200,8 +379,6 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 
   int* misc = (int*)(smem + kOffMisc);
   int* sel_l = (int*)(smem + kOffSel);
-  float* alpha_l = (float*)(smem + kOffAlpha);
-  unsigned int* rflag = (unsigned int*)(smem + kOffRFlag);
 
   // this workgroup's part of the selection -> LDS (invalid entries as -1), and its extent
   if (tid == 0) misc[0] = -1;
@@ -239,153 +416,34 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   float m_run = -INFINITY, l_run = 0.f;
   const float c_scale = sm_scale * kLog2e;
 
-  // prologue: steps 0 and 1 in flight (unconditionally: entries past the selection copy row 0),
-  // then wait for the query fragments (loaded before the copies, so the copies stay in flight;
-  // otherwise every step would wait for all copies) and for step 0
-  gather_step(kvb, sel_l, 0, e_n, smem + kOffBuf, wave, lane);
-  gather_step(kvb, sel_l, kNB, e_n, smem + kOffBuf + kBufBytes, wave, lane);
+  // prologue: step 0's rows, then wait for them and for the query fragments
+  {
+    const GatherRows g0 = gather_rows(sel_l, 0, e_n, wave, lane);
 #pragma unroll
-  for (int ks = 0; ks < kDQK / 16; ks++) asm volatile("" ::"v"(qf[ks]));
-  wait_vmcnt<kGatherPerWave>();
+    for (int j = 0; j < kGatherPerWave; j++) gather_copy(kvb, g0, j, smem + kOffBuf, wave, lane);
+  }
+  wait_vmcnt0();
   lds_barrier();
 
-  int cur = 0;
-  for (int it = 0; it < n_steps; it++) {
-    char* buf = smem + kOffBuf + cur * kBufBytes;
-    const int e0 = it * kNB;
-    const bool ahead2 = it + 2 < n_steps;
-    if (ahead2) {
-      int nb = cur + 2;
-      nb = nb >= kNBuf ? nb - kNBuf : nb;
-      gather_step(kvb, sel_l, e0 + 2 * kNB, e_n, smem + kOffBuf + nb * kBufBytes, wave, lane);
+  // Software pipeline.  Iteration `it`: the copies of step it+1 are issued between the QK^T
+  // instructions of step it; then PV of step it-1 (matrix cores) runs interleaved with the softmax of
+  // step it (VALU); then step it's P^T is published and the waves meet once.
+  // The rescale of O (rare once the running max has settled) happens outside the inner loop, so the
+  // loop itself only ever touches O through the matrix cores.  Step 0 needs none: O is still zero.
+  PipeState st{m_run, l_run};
+  if (n_steps > 0) {
+    pipeline_step<true, false>(0, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
+    int it = 1;
+    while (it < n_steps) {
+      bool moved = false;
+      for (; it < n_steps && !moved; it++)
+        moved = pipeline_step<true, true>(it, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
+      if (moved) rescale_o(o, (const float*)(smem + kOffAlpha) + kH * ((it - 1) & 1), lane);
     }
-    const unsigned int vmask = step_valid_mask(sel_l, e0, e_n, lane);
-
-    // ---- S^T = K . Q^T for this wave's heads (S kept in VGPRs: the AGPR file holds O)
-    v16f sacc;
-    {
-      const char* kp = buf + (lane & 31) * kTileRowBytes + (lane >> 5) * 16;
-      {
-        v8bf kf = *(const v8bf*)(kp);
-        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(kf), "v"(qf[0]));
-      }
-#pragma unroll
-      for (int ks = 1; ks < kDQK / 16; ks++) {
-        v8bf kf = *(const v8bf*)(kp + ks * 32);
-        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(kf), "v"(qf[ks]));
-      }
-      asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
-    }
-
-    // ---- online softmax: this lane = head 32w + l%32; its 16 values are keys 8(r/4) + 4(l/32) + r%4
-    float x[16];
-    float bm = -INFINITY;
-    const unsigned int vm = vmask >> (4 * (lane >> 5));
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      x[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] * c_scale : -INFINITY;
-      bm = fmaxf(bm, x[r]);
-    }
-    bm = xor32_max(bm);
-    float alpha = 1.f;
-    if (bm > m_run + kRescaleThreshold) {
-      alpha = __builtin_amdgcn_exp2f(m_run - bm);  // 0 when m_run = -inf
-      m_run = bm;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum = 0.f;
-    unsigned int pk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p0 = __builtin_amdgcn_exp2f(x[r] - m_use), p1 = __builtin_amdgcn_exp2f(x[r + 1] - m_use);
-      psum += p0 + p1;
-      pk[r >> 1] = pack_bf16x2(p0, p1);
-    }
-    l_run = l_run * alpha + xor32_sum(psum);
-    {
-      u32x4* pl = (u32x4*)(smem + kOffP);
-      pl[(wave * 2 + 0) * 64 + lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      pl[(wave * 2 + 1) * 64 + lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-      if (lane < 32) alpha_l[32 * wave + lane] = alpha;
-      unsigned long long any = __ballot(alpha != 1.f);
-      if (lane == 0) rflag[wave] = any ? 1u : 0u;
-    }
-    lds_barrier();
-
-    // ---- rescale O^T where some head's running max moved (rare after the first step)
-    if (rflag[0] | rflag[1] | rflag[2] | rflag[3]) {
-#pragma unroll
-      for (int hb = 0; hb < 4; hb++) {
-        const float a = alpha_l[32 * hb + (lane & 31)];
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            // scale the accumulator in place in the AGPR file
-            float tmp;
-            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                         : "+a"(o[db][hb][r]), "=&v"(tmp) : "v"(a));
-          }
-      }
-      asm volatile("s_nop 4" ::: "memory");
-    }
-
-    // ---- O^T[d][h] += V^T[d][keys] . P^T[keys][h]
-    {
-      const int G = lane >> 4, j = lane & 15;
-      const u32x4* pl = (const u32x4*)(smem + kOffP);
-      // V^T fragments of both 16-key halves: 16 transposing LDS reads issued together and waited for
-      // inside the same asm block (the values are complete when the block ends)
-      const unsigned int vbase =
-          (unsigned int)(uintptr_t)(lds_void*)(buf + (4 * (G >> 1) + (j >> 2)) * kTileRowBytes +
-                                               (128 * wave + 16 * (G & 1) + 4 * (j & 3)) * 2);
-      u32x2 vr[2][4][2];
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
-          "ds_read_b64_tr_b16 %1, %16 offset:9344\n\t"
-          "ds_read_b64_tr_b16 %2, %16 offset:64\n\t"
-          "ds_read_b64_tr_b16 %3, %16 offset:9408\n\t"
-          "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
-          "ds_read_b64_tr_b16 %5, %16 offset:9472\n\t"
-          "ds_read_b64_tr_b16 %6, %16 offset:192\n\t"
-          "ds_read_b64_tr_b16 %7, %16 offset:9536\n\t"
-          "ds_read_b64_tr_b16 %8, %16 offset:18688\n\t"
-          "ds_read_b64_tr_b16 %9, %16 offset:28032\n\t"
-          "ds_read_b64_tr_b16 %10, %16 offset:18752\n\t"
-          "ds_read_b64_tr_b16 %11, %16 offset:28096\n\t"
-          "ds_read_b64_tr_b16 %12, %16 offset:18816\n\t"
-          "ds_read_b64_tr_b16 %13, %16 offset:28160\n\t"
-          "ds_read_b64_tr_b16 %14, %16 offset:18880\n\t"
-          "ds_read_b64_tr_b16 %15, %16 offset:28224\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(vr[0][0][0]), "=&v"(vr[0][0][1]), "=&v"(vr[0][1][0]), "=&v"(vr[0][1][1]), "=&v"(vr[0][2][0]),
-            "=&v"(vr[0][2][1]), "=&v"(vr[0][3][0]), "=&v"(vr[0][3][1]), "=&v"(vr[1][0][0]), "=&v"(vr[1][0][1]),
-            "=&v"(vr[1][1][0]), "=&v"(vr[1][1][1]), "=&v"(vr[1][2][0]), "=&v"(vr[1][2][1]), "=&v"(vr[1][3][0]),
-            "=&v"(vr[1][3][1])
-          : "v"(vbase));
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ks2++) {
-        v8bf pf[4];
-#pragma unroll
-        for (int hb = 0; hb < 4; hb++) pf[hb] = __builtin_bit_cast(v8bf, pl[(hb * 2 + ks2) * 64 + lane]);
-#pragma unroll
-        for (int db = 0; db < 4; db++) {
-          const u32x4 v4 = {vr[ks2][db][0][0], vr[ks2][db][0][1], vr[ks2][db][1][0], vr[ks2][db][1][1]};
-          const v8bf vf = __builtin_bit_cast(v8bf, v4);
-#pragma unroll
-          for (int hb = 0; hb < 4; hb++)
-            o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hb], o[db][hb], 0, 0, 0);
-        }
-      }
-    }
-    // step it+1's rows must have landed (step it+2's copies may stay in flight)
-    if (ahead2)
-      wait_vmcnt<kGatherPerWave>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    cur = cur + 1 == kNBuf ? 0 : cur + 1;
+    pipeline_step<false, true>(n_steps, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
   }
+  m_run = st.m;
+  l_run = st.l;
 
   // ---- epilogue: publish per-head (m, l), normalise, store
   float* l_l = (float*)(smem + kOffL);
