@@ -10,11 +10,11 @@
 //   * an ordered compaction: every wave owns a contiguous segment of the row, counts its "> tau"
 //     and "== tau" keys, a scan over waves gives each its output offset, and the wave writes its
 //     selected positions in ascending order (ballot + mbcnt), so the result is sorted by position.
-// The histogram has 16 copies (a lane uses copy lane%16) padded to 257 words, which spreads the
-// heavy same-bin traffic of the first pass (scores of similar magnitude share their top byte)
-// over distinct addresses and banks.
-// Rows that fit in LDS (n <= 36736) are read from HBM once and kept as keys in LDS; longer rows
-// are re-read from memory in every pass.
+// Memory access: every pass reads in chunks of kUnroll independent loads per thread (16-byte loads
+// when rows are 16-byte aligned) before using any of them (the scores come from HBM once; a row that fits in LDS is kept there as keys).  The
+// histogram has 16 copies (a lane uses copy lane%16) padded to 257 words, which spreads the heavy
+// same-bin traffic of the first pass (scores of similar magnitude share their top byte); the copies
+// are summed by 256 threads in parallel.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -24,9 +24,10 @@ constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kHistCopies = 16;
 constexpr int kHistStride = 257;
 constexpr int kHistWords = kHistCopies * kHistStride;
-constexpr int kMiscWords = 64;
+constexpr int kMiscWords = 64 + 256;  // digit/count scratch + summed histogram
 constexpr int kLdsBytesMax = 163840;
-constexpr int kRowCapMax = ((kLdsBytesMax - (kHistWords + kMiscWords) * 4) / 4) / 64 * 64;  // 36736
+constexpr int kRowCapMax = ((kLdsBytesMax - (kHistWords + kMiscWords) * 4) / 4) / 64 * 64;
+constexpr int kUnroll = 8;
 
 __device__ __forceinline__ unsigned int score_key(float f) {
   unsigned int u = __float_as_uint(f);
@@ -34,19 +35,50 @@ __device__ __forceinline__ unsigned int score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <bool CACHED>
-__device__ __forceinline__ unsigned int row_key(const float* __restrict__ row, const unsigned int* rowk, int i) {
-  if (CACHED) return rowk[i];
-  return score_key(row[i]);
+// Sum the histogram copies (256 threads, one bin each), then wave 0 fixes the digit: the highest bin
+// whose suffix count reaches k_rem.  Writes misc[0] = digit, misc[1] = keys above it.
+__device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned int* misc, unsigned int* tot,
+                                             int k_rem, int tid, int wave, int lane) {
+  if (tid < 256) {
+    unsigned int s = 0;
+#pragma unroll
+    for (int cp = 0; cp < kHistCopies; cp++) s += hist[cp * kHistStride + tid];
+    tot[tid] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    unsigned int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) c[j] = tot[4 * lane + j];
+    const unsigned int mine = c[0] + c[1] + c[2] + c[3];
+    unsigned int suf = mine;  // inclusive suffix sum over lanes: keys in bins >= 4*lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    unsigned int above = suf - mine;  // keys in bins >= 4*lane + 4
+#pragma unroll
+    for (int j = 3; j >= 0; j--) {
+      const unsigned int ge = above + c[j];
+      if (above < (unsigned int)k_rem && ge >= (unsigned int)k_rem) {
+        misc[0] = 4u * lane + j;
+        misc[1] = above;
+      }
+      above = ge;
+    }
+  }
+  __syncthreads();
 }
 
 template <bool CACHED>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld, int n_q,
-                                                          int n_kv, int k, int32_t* __restrict__ idx) {
+                                                          int n_kv, int k, int32_t* __restrict__ idx, bool vec4) {
   extern __shared__ unsigned int lds[];
-  unsigned int* hist = lds;                           // [16][257]
-  unsigned int* misc = lds + kHistWords;              // [64]
-  unsigned int* rowk = lds + kHistWords + kMiscWords;  // [n] (CACHED only)
+  unsigned int* hist = lds;                         // [16][257]
+  unsigned int* misc = lds + kHistWords;            // [64] scratch
+  unsigned int* tot = misc + 64;                    // [256] summed histogram
+  unsigned int* rowk = lds + kHistWords + kMiscWords;  // [n] keys (CACHED only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,69 +104,88 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
     __syncthreads();
-    if (pass == 0) {
-      for (int i = tid; i < n; i += kTkThreads) {
-        unsigned int key = score_key(row[i]);
-        if (CACHED) rowk[i] = key;
-        atomicAdd(&h[key >> 24], 1u);
+    if (pass == 0 || !CACHED) {
+      if (vec4) {
+        // 16-byte loads: kUnroll float4 per thread in flight, the tail (n % 4 keys) one by one
+        const float4* row4 = reinterpret_cast<const float4*>(row);
+        const int n4 = n >> 2;
+        for (int base = 0; base < n4; base += kTkThreads * kUnroll) {
+          float4 v[kUnroll];
+#pragma unroll
+          for (int u = 0; u < kUnroll; u++) {
+            const int j = base + u * kTkThreads + tid;
+            v[u] = j < n4 ? row4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; u++) {
+            const int j = base + u * kTkThreads + tid;
+            if (j < n4) {
+              const unsigned int key[4] = {score_key(v[u].x), score_key(v[u].y), score_key(v[u].z),
+                                           score_key(v[u].w)};
+              if (CACHED) reinterpret_cast<u32x4*>(rowk)[j] = (u32x4){key[0], key[1], key[2], key[3]};
+#pragma unroll
+              for (int e = 0; e < 4; e++)
+                if (pass == 0 || (key[e] >> (shift + 8)) == prefix) atomicAdd(&h[(key[e] >> shift) & 255u], 1u);
+            }
+          }
+        }
+        const int i = 4 * n4 + tid;
+        if (i < n) {
+          const unsigned int key = score_key(row[i]);
+          if (CACHED) rowk[i] = key;
+          if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        }
+      } else {
+        for (int base = 0; base < n; base += kTkThreads * kUnroll) {
+          float v[kUnroll];
+#pragma unroll
+          for (int u = 0; u < kUnroll; u++) {
+            const int i = base + u * kTkThreads + tid;
+            v[u] = i < n ? row[i] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; u++) {
+            const int i = base + u * kTkThreads + tid;
+            if (i < n) {
+              const unsigned int key = score_key(v[u]);
+              if (CACHED) rowk[i] = key;
+              if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+            }
+          }
+        }
       }
     } else {
       for (int i = tid; i < n; i += kTkThreads) {
-        unsigned int key = row_key<CACHED>(row, rowk, i);
+        const unsigned int key = rowk[i];
         if ((key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
       }
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins 4l .. 4l+3 (summed over the copies)
-      unsigned int c[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        unsigned int s = 0;
-        for (int cp = 0; cp < kHistCopies; cp++) s += hist[cp * kHistStride + 4 * lane + j];
-        c[j] = s;
-      }
-      unsigned int mine = c[0] + c[1] + c[2] + c[3];
-      // inclusive suffix sum over lanes: ge_lane = sum of bins >= 4*lane
-      unsigned int suf = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        unsigned int o = __shfl_down(suf, off, 64);
-        if (lane + off < 64) suf += o;
-      }
-      unsigned int above = suf - mine;  // keys in bins >= 4*lane + 4
-      // ge(bin) for bins 4l+3 .. 4l; the digit is the highest bin with ge >= k_rem
-#pragma unroll
-      for (int j = 3; j >= 0; j--) {
-        unsigned int ge = above + c[j];
-        if (above < (unsigned int)k_rem && ge >= (unsigned int)k_rem) {
-          misc[0] = 4u * lane + j;
-          misc[1] = above;  // keys strictly above this digit (within the prefix)
-        }
-        above = ge;
-      }
-    }
-    __syncthreads();
-    const unsigned int d = misc[0];
-    const unsigned int gt = misc[1];
-    prefix = (prefix << 8) | d;
-    k_rem -= (int)gt;
+    select_digit(hist, misc, tot, k_rem, tid, wave, lane);
+    prefix = (prefix << 8) | misc[0];
+    k_rem -= (int)misc[1];
     __syncthreads();  // misc is rewritten by the next pass
   }
   const unsigned int tau = prefix;  // the k-th largest key; k_rem keys equal to tau are taken
 
-  // ordered compaction over per-wave contiguous segments
+  // ordered compaction over per-wave contiguous segments (kUnroll 64-wide groups per load batch)
   const int seg = ((n + kTkWaves * 64 - 1) / (kTkWaves * 64)) * 64;
   const int s0 = wave * seg;
   const int s1 = min(n, s0 + seg);
   unsigned int n_gt = 0, n_eq = 0;
-  for (int i0 = s0; i0 < s1; i0 += 64) {
-    const int i = i0 + lane;
-    unsigned int key = (i < s1) ? row_key<CACHED>(row, rowk, i) : 0u;
-    bool g = (i < s1) && key > tau;
-    bool e = (i < s1) && key == tau;
-    n_gt += __popcll(__ballot(g));
-    n_eq += __popcll(__ballot(e));
+  for (int i0 = s0; i0 < s1; i0 += 64 * kUnroll) {
+    unsigned int key[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int i = i0 + 64 * u + lane;
+      key[u] = (i < s1) ? (CACHED ? rowk[i] : score_key(row[i])) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int i = i0 + 64 * u + lane;
+      n_gt += __popcll(__ballot(i < s1 && key[u] > tau));
+      n_eq += __popcll(__ballot(i < s1 && key[u] == tau));
+    }
   }
   if (lane == 0) {
     misc[2 + wave] = n_gt;
@@ -148,41 +199,47 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   }
   unsigned int e_run = eq_before;
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
-  for (int i0 = s0; i0 < s1; i0 += 64) {
-    const int i = i0 + lane;
-    unsigned int key = (i < s1) ? row_key<CACHED>(row, rowk, i) : 0u;
-    bool g = (i < s1) && key > tau;
-    bool e = (i < s1) && key == tau;
-    unsigned long long be = __ballot(e);
-    unsigned int erank = e_run + (unsigned int)__builtin_amdgcn_mbcnt_hi((unsigned int)(be >> 32),
-                                                                          __builtin_amdgcn_mbcnt_lo((unsigned int)be, 0u));
-    bool sel = g || (e && erank < (unsigned int)k_rem);
-    unsigned long long bs = __ballot(sel);
-    unsigned int opos = p_run + (unsigned int)__builtin_amdgcn_mbcnt_hi((unsigned int)(bs >> 32),
-                                                                        __builtin_amdgcn_mbcnt_lo((unsigned int)bs, 0u));
-    if (sel && opos < (unsigned int)k) out[opos] = i;
-    e_run += __popcll(be);
-    p_run += __popcll(bs);
+  for (int i0 = s0; i0 < s1; i0 += 64 * kUnroll) {
+    unsigned int key[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int i = i0 + 64 * u + lane;
+      key[u] = (i < s1) ? (CACHED ? rowk[i] : score_key(row[i])) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int i = i0 + 64 * u + lane;
+      const bool g = (i < s1) && key[u] > tau;
+      const bool e = (i < s1) && key[u] == tau;
+      const unsigned long long be = __ballot(e);
+      const unsigned int erank = e_run + (unsigned int)__builtin_amdgcn_mbcnt_hi(
+                                             (unsigned int)(be >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)be, 0u));
+      const bool sel = g || (e && erank < (unsigned int)k_rem);
+      const unsigned long long bs = __ballot(sel);
+      const unsigned int opos = p_run + (unsigned int)__builtin_amdgcn_mbcnt_hi(
+                                            (unsigned int)(bs >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)bs, 0u));
+      if (sel && opos < (unsigned int)k) out[opos] = i;
+      e_run += __popcll(be);
+      p_run += __popcll(bs);
+    }
   }
 }
-
-static bool g_topk_attr_set = false;
 
 hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,
                        hipStream_t stream) {
   dim3 grid(n_q, B);
+  // rows start on 16-byte boundaries when the base is aligned and ld is a multiple of 4
+  const bool vec4 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (ld & 3) == 0;
   if (n_kv <= kRowCapMax) {
-    if (!g_topk_attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytesMax);
-      if (e != hipSuccess) return e;
-      g_topk_attr_set = true;
-    }
+    // more than 64 KiB of dynamic LDS needs an explicit opt-in (done once; thread-safe static init)
+    static const hipError_t attr = hipFuncSetAttribute((const void*)topk_kernel<true>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytesMax);
+    if (attr != hipSuccess) return attr;
     size_t lds = (size_t)(kHistWords + kMiscWords + ((n_kv + 3) / 4) * 4) * 4;
-    hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx);
+    hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx, vec4);
   } else {
     size_t lds = (size_t)(kHistWords + kMiscWords) * 4;
-    hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx);
+    hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx, vec4);
   }
   return hipGetLastError();
 }
