@@ -44,7 +44,63 @@ def parse():
     ap.add_argument("--k", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference kernel for the HBM byte "
+                         "counters), then exit")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel, from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over
+# `bench.py --only prefill --steps 1 --warmup 0 --no-cpu-baseline`, each scaled by the reading of the same
+# counter for a plain copy of known size (`bench.py --calib-copy`).  Valid only for the kernel source it
+# was measured on: the sha256 of that source is stored with it and checked at run time.
+MEASURED_TRAFFIC = {
+    "prefill.sparse_mla": {"bytes_per_launch": 14938758963,  # 10.583 GB read + 4.356 GB written
+                           "src_sha256": "d7e8d536485b1fda8de6fa2f8ddf26d5106929a2fa1ac6aac98500aff842ede6",
+                           "profile": "profiles/dsa_kernels_prefill32k_hbm_traffic.md"},
+}
+KERNEL_SOURCES = {
+    "prefill.sparse_mla": "sparse_attention_13_amd/csrc/sparse_mla.hip",
+    "prefill.indexer": "sparse_attention_13_amd/csrc/indexer.hip",
+    "prefill.topk": "sparse_attention_13_amd/csrc/topk.hip",
+    "decode.indexer": "sparse_attention_13_amd/csrc/indexer.hip",
+}
+
+
+def source_sha(stage):
+    import hashlib
+    path = os.path.join(ROOT, KERNEL_SOURCES[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage`'s kernel from the stored counter passes, or None when there is no
+    measurement or the kernel's source has changed since it was taken."""
+    m = MEASURED_TRAFFIC.get(stage)
+    if not m or m["src_sha256"] != source_sha(stage):
+        return None
+    return m["bytes_per_launch"]
+
+
+def calib_copy():
+    """A plain device copy of 2^30 bytes (read 1 GiB, write 1 GiB), five times: the reference reading for
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 5
+    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "ms": round(ms, 4),
+                      "GB/s": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def causal_work(L: int, n_q: int, k: int):
@@ -62,6 +118,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode.",
               file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
     import numpy as np
     import torch
 
@@ -204,7 +263,9 @@ def main():
     # dominant kernel = the stage with the largest time in the step
     dom = max(rooflines.items(), key=lambda kv: kv[1][0]) if rooflines else None
     if dom:
-        out["roofline"] = dict(dom[1][1], kernel=dom[0])
+        roof = dict(dom[1][1], kernel=dom[0])
+        roof["traffic"] = measured_traffic(dom[0]) if dom[0] in KERNEL_SOURCES else None
+        out["roofline"] = roof
 
     # ------------------------------------------------------------------ CPU oracle baseline (bounded sample)
     if not args.no_cpu_baseline and pre:
@@ -222,8 +283,10 @@ def cpu_baseline_prefill(pre, k, sm):
     from sparse_attention_13_amd import synth
     L, x = pre["L"], pre["x"]
     gen = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(k - 4, k + 4), np.arange(L - 8, L),
-                                     gen.choice(L, 40, replace=False)])).astype(np.int64)
+    fixed = np.concatenate([np.arange(0, 64), np.arange(k - 32, k + 32), np.arange(L - 64, L)])
+    rest = np.setdiff1d(np.arange(L), fixed)
+    rows = np.unique(np.concatenate([fixed, gen.choice(rest, 512 - len(np.unique(fixed)), replace=False)]))
+    rows = rows.astype(np.int64)
     rsel = torch.from_numpy(rows).to(x["q8"].device)
     q_i = oracle.dequant_e4m3(synth.u8(x["q8"][rsel]), x["q_scale"][rsel].cpu().numpy())
     w = x["w"][rsel].cpu().numpy()
@@ -238,7 +301,8 @@ def cpu_baseline_prefill(pre, k, sm):
     w_total = sum(work(p) for p in range(L))
     full_s = t * w_total / w_sample
     return {"value": round(L / full_s, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": (f"{len(rows)} of {L} query rows (first, around position k-1, last, uniform), "
+            "sample": (f"{len(rows)} of {L} query rows (first 64, 64 around position k-1, last 64, the rest "
+                       f"uniform), "
                        f"{t:.1f} s, extrapolated to all rows by the per-row work model"),
             "sample_seconds": round(t, 2)}
 
@@ -249,7 +313,7 @@ def cpu_baseline_decode(dec, k, sm):
     import oracle
     from sparse_attention_13_amd import synth
     y, S = dec["y"], dec["S"]
-    nb = 2
+    nb = min(12, dec["B"])
     t_total = 0.0
     for b in range(nb):
         q_i = oracle.dequant_e4m3(synth.u8(y["q8"][b:b + 1]), y["q_scale"][b:b + 1].cpu().numpy())
