@@ -158,13 +158,14 @@ def main():
         idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
         out = torch.empty((1, L, 128, 512), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        tk_ws = torch.empty(max(dsa.topk_workspace_size(1, L, L, k), 256), dtype=torch.uint8, device=dev)
         ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16)
         ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
         q8, qs, k8, ks, w = (x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None])
         q, kv = x["q"][None], x["kv"][None]
         pre_stages = [
             ("indexer", lambda: dsa.indexer_scores(q8, qs, k8, ks, w, scores)),
-            ("topk", lambda: dsa.topk(scores, L, k, idx=idx)),
+            ("topk", lambda: dsa.topk(scores, L, k, idx=idx, workspace=tk_ws)),
             ("sparse_mla", lambda: dsa.sparse_mla_attn(q, kv, idx, 512, sm, out=out, lse=lse, workspace=ws)),
         ]
         pre = dict(L=L, stages=pre_stages, x=x, idx=idx, out=out, lse=lse)
@@ -180,13 +181,14 @@ def main():
         d_idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
         d_out = torch.empty((B, 1, 128, 512), dtype=torch.bfloat16, device=dev)
         d_lse = torch.empty((B, 1, 128), dtype=torch.float32, device=dev)
+        d_tk_ws = torch.empty(max(dsa.topk_workspace_size(B, 1, S, k), 256), dtype=torch.uint8, device=dev)
         ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(B, 1, S, 128, 576, 512, k, dsa.DSA_BF16)
         d_ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
         yq8, yqs, yk8, yks, yw = (y["q8"][:, None], y["q_scale"][:, None], y["k8"], y["k_scale"], y["w"][:, None])
         yq, ykv = y["q"][:, None], y["kv"]
         dec_stages = [
             ("indexer", lambda: dsa.indexer_scores(yq8, yqs, yk8, yks, yw, d_scores)),
-            ("topk", lambda: dsa.topk(d_scores, S, k, idx=d_idx)),
+            ("topk", lambda: dsa.topk(d_scores, S, k, idx=d_idx, workspace=d_tk_ws)),
             ("sparse_mla", lambda: dsa.sparse_mla_attn(yq, ykv, d_idx, 512, sm, out=d_out, lse=d_lse, workspace=d_ws)),
         ]
         dec = dict(B=B, S=S, stages=dec_stages, y=y, idx=d_idx, out=d_out, lse=d_lse)

@@ -93,9 +93,16 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* q_scale, const void*
  * idx[b][t][0..k) in ascending s, padded with -1.  scores is read only at s <= pos_t.
  * scores [B][n_q][ld_scores] fp32 (ld_scores >= n_kv), idx [B][n_q][k] int32.  1 <= k <= 65536.
  * Non-finite scores: NaN is not allowed (result unspecified); +-inf are ordered as usual.
+ * workspace: device memory of at least dsa_topk_workspace_size(B, n_q, n_kv, k) bytes, 256-byte
+ *   aligned (may be NULL when that size is 0).  Long rows, or too few rows to fill the GPU, are
+ *   selected in two stages whose intermediate candidates live there; its contents are scratch.
+ *   Too small, misaligned or missing when needed: DSA_ERR_WORKSPACE, nothing enqueued.
  * ------------------------------------------------------------------------------------------------ */
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int B, int n_q, int n_kv, int k,
-                      int32_t* idx, void* stream);
+                      int32_t* idx, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_topk needs for this shape (0 for invalid sizes or when none is needed). */
+size_t dsa_topk_workspace_size(int B, int n_q, int n_kv, int k);
 
 /* ------------------------------------------------------------------------------------------------
  * dsa_sparse_mla_attn -- attention over the selected latent rows (sections 1.2 and 1.3 of the
@@ -132,7 +139,8 @@ size_t dsa_sparse_mla_attn_workspace_size(int B, int n_q, int n_kv, int H, int d
  * attention inputs as in dsa_sparse_mla_attn (attn_dtype, q, kv, H, d_qk, d_v, sm_scale, out, lse).
  * idx_out: NULL, or [B][n_q][k] int32 that receives the selection (else it stays in the workspace).
  * workspace: at least dsa_forward_workspace_size(...) bytes, 256-byte aligned.  It holds the score
- *   rows ([B][n_q][ld] fp32, ld = n_kv rounded up to 64), the selection and the attention scratch.
+ *   rows ([B][n_q][ld] fp32, ld = n_kv rounded up to 64), the selection, the top-k candidates and
+ *   the attention scratch.
  * ------------------------------------------------------------------------------------------------ */
 dsa_status_t dsa_forward_prefill(const void* q_i, const float* q_i_scale, const void* k_i,
                                  const float* k_i_scale, const float* w, const void* q, const void* kv,

@@ -86,6 +86,14 @@ dsa_status_t check_topk(const float* scores, int64_t ld, int B, int n_q, int n_k
   return DSA_OK;
 }
 
+dsa_status_t check_topk_ws(const dsa::TopkPlan& p, const void* workspace, size_t ws_bytes) {
+  if (p.ws == 0) return DSA_OK;
+  if (!workspace) return fail(DSA_ERR_WORKSPACE, "topk: workspace of %zu bytes required", p.ws);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_WORKSPACE, "topk: workspace must be 256-byte aligned");
+  if (ws_bytes < p.ws) return fail(DSA_ERR_WORKSPACE, "topk: workspace %zu < %zu bytes", ws_bytes, p.ws);
+  return DSA_OK;
+}
+
 // ------------------------------------------------------------------------------------------- attention
 struct AttnPlan {
   bool fast = false;
@@ -147,8 +155,9 @@ dsa_status_t run_attn(const void* q, const void* kv, const int32_t* idx, int B, 
 // ------------------------------------------------------------------------------------------- forward
 struct FwdLayout {
   int64_t ld = 0;
-  size_t off_scores = 0, off_idx = 0, off_attn = 0, total = 0;
+  size_t off_scores = 0, off_idx = 0, off_topk = 0, off_attn = 0, total = 0;
   AttnPlan attn;
+  dsa::TopkPlan topk;
 };
 
 dsa_status_t plan_forward(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k, dsa_dtype_t attn_dtype,
@@ -159,7 +168,9 @@ dsa_status_t plan_forward(int B, int n_q, int n_kv, int H, int d_qk, int d_v, in
   L->ld = (int64_t)align_up((size_t)n_kv, 64);
   L->off_scores = 0;
   L->off_idx = align_up((size_t)B * n_q * L->ld * sizeof(float), 256);
-  L->off_attn = align_up(L->off_idx + (size_t)B * n_q * k * sizeof(int32_t), 256);
+  L->topk = dsa::plan_topk(B, n_q, n_kv, k);
+  L->off_topk = align_up(L->off_idx + (size_t)B * n_q * k * sizeof(int32_t), 256);
+  L->off_attn = L->off_topk + align_up(L->topk.ws, 256);
   L->total = L->off_attn + align_up(L->attn.ws, 256);
   return DSA_OK;
 }
@@ -188,7 +199,7 @@ dsa_status_t forward(const void* q_i, const float* q_i_scale, const void* k_i, c
   st = run_indexer(q_i, q_i_scale, k_i, k_i_scale, w, B, n_q, n_kv, H_I, d_I, idx_dtype, scores, L.ld, fast_idx,
                    stream);
   if (st != DSA_OK) return st;
-  st = hip_status(dsa::launch_topk(scores, L.ld, B, n_q, n_kv, k, idx, stream), "dsa_topk");
+  st = hip_status(dsa::launch_topk(scores, L.ld, B, n_q, n_kv, k, idx, L.topk, ws + L.off_topk, stream), "dsa_topk");
   if (st != DSA_OK) return st;
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, L.attn,
                   L.attn.ws ? ws + L.off_attn : nullptr, stream);
@@ -224,10 +235,19 @@ dsa_status_t dsa_indexer_scores(const void* q, const float* q_scale, const void*
 }
 
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int B, int n_q, int n_kv, int k, int32_t* idx,
-                      void* stream) {
+                      void* workspace, size_t ws_bytes, void* stream) {
   dsa_status_t st = check_topk(scores, ld_scores, B, n_q, n_kv, k, idx);
   if (st != DSA_OK) return st;
-  return hip_status(dsa::launch_topk(scores, ld_scores, B, n_q, n_kv, k, idx, (hipStream_t)stream), "dsa_topk");
+  const dsa::TopkPlan p = dsa::plan_topk(B, n_q, n_kv, k);
+  st = check_topk_ws(p, workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_topk(scores, ld_scores, B, n_q, n_kv, k, idx, p, workspace, (hipStream_t)stream),
+                    "dsa_topk");
+}
+
+size_t dsa_topk_workspace_size(int B, int n_q, int n_kv, int k) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || k < 1 || k > kMaxTopK || n_q > n_kv) return 0;
+  return dsa::plan_topk(B, n_q, n_kv, k).ws;
 }
 
 size_t dsa_sparse_mla_attn_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,

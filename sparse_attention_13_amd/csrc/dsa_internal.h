@@ -72,8 +72,18 @@ hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint
                               const float* w, int B, int n_q, int n_kv, float* scores, int64_t ld,
                               int keys_per_wave, hipStream_t stream);
 
+// Top-k launch plan: one LDS-resident pass per row, two stages (chunk candidates in a workspace, then
+// a merge) for rows too long or too few, or a kernel that re-reads long rows from memory.
+struct TopkPlan {
+  enum Mode { kSingle = 0, kTwoStage = 1, kUncached = 2 };
+  int mode;
+  int chunk;     // keys per chunk (two stages)
+  int n_chunks;
+  size_t ws;     // workspace bytes (two stages), else 0
+};
+TopkPlan plan_topk(int B, int n_q, int n_kv, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,
-                       hipStream_t stream);
+                       const TopkPlan& plan, void* workspace, hipStream_t stream);
 
 hipError_t launch_attn_generic(const float* q, const float* kv, const int32_t* idx, int B, int n_q, int n_kv,
                                int H, int d_qk, int d_v, int k, float sm_scale, float* out, float* lse,

@@ -2,20 +2,29 @@
 // causal candidates s <= pos_t (velog summary "DeepSeek-V3.2: Pushing the Frontier of Open Large
 // Language Models", section 1.2; k = 2048 in the sparse-training stage).
 //
-// Exact radix select on order-preserving 32-bit keys (-0 folded onto +0), one workgroup per row:
+// Exact radix select on order-preserving 32-bit keys (-0 folded onto +0):
 //   * four 8-bit digit passes, most significant first, each building a 256-bin histogram of the
 //     keys that share the digits fixed so far, then fixing the digit that holds the k-th largest
-//     key; after the fourth pass tau (the k-th largest key) is known, together with how many keys
-//     equal to tau must be taken (the lowest positions win ties);
-//   * an ordered compaction: every wave owns a contiguous segment of the row, counts its "> tau"
-//     and "== tau" keys, a scan over waves gives each its output offset, and the wave writes its
-//     selected positions in ascending order (ballot + mbcnt), so the result is sorted by position.
-// Memory access: every pass reads in chunks of kUnroll independent loads per thread (16-byte loads
-// when rows are 16-byte aligned) before using any of them (the scores come from HBM once; a row that fits in LDS is kept there as keys).  The
-// histogram has 16 copies (a lane uses copy lane%16) padded to 257 words, which spreads the heavy
-// same-bin traffic of the first pass (scores of similar magnitude share their top byte); the copies
-// are summed by 256 threads in parallel.
+//     key; afterwards tau (the k-th largest key) is known, and so is the number of keys equal to
+//     tau that are taken (the lowest positions win ties);
+//   * an ordered compaction: every wave owns a contiguous segment of the row, counts its keys above
+//     and equal to tau, a scan over waves gives each its output offset, and the wave writes its
+//     selected positions in ascending order (ballots over per-lane counts), so the result is sorted.
+// One workgroup (8 waves) selects from up to kKeyCap keys held in LDS: the first pass reads them from
+// memory (kLoadUnroll independent 16-byte loads per thread in flight), every later pass and the
+// compaction read LDS in 16-byte pieces, kLdsUnroll per lane in flight.
+//
+// Rows that are longer than kKeyCap, or too few to fill the GPU, run in two stages.  Stage one cuts
+// each row into chunks and selects the top k of every chunk as (key, position) candidates; stage two
+// selects the top k among a row's candidates.  Every member of the row's top k is in its own chunk's
+// top k (fewer than k keys of the row, hence of the chunk, beat it), so the result is exact.  The
+// candidates of a row are stored chunk after chunk, each chunk's in ascending position, so array
+// order is position order and the stage-two compaction keeps both the tie rule and the sorted output.
+// Rows the two stages cannot take (k too large for the LDS budget) use a kernel that re-reads the row
+// from memory in every pass.
 #include "dsa_internal.h"
+
+#include <algorithm>
 
 namespace dsa {
 
@@ -26,13 +35,50 @@ constexpr int kHistStride = 257;
 constexpr int kHistWords = kHistCopies * kHistStride;
 constexpr int kMiscWords = 64 + 256;  // digit/count scratch + summed histogram
 constexpr int kLdsBytesMax = 163840;
-constexpr int kRowCapMax = ((kLdsBytesMax - (kHistWords + kMiscWords) * 4) / 4) / 64 * 64;
-constexpr int kUnroll = 8;
+constexpr int kKeyCap = ((kLdsBytesMax / 4 - kHistWords - kMiscWords) / 256) * 256;  // 36352 keys
+constexpr int kLoadUnroll = 16;
+constexpr int kLdsUnroll = 4;
+constexpr int kSeg = 256;  // keys per wave-wide 16-byte LDS read
+
+enum { kSrcScores = 0, kSrcCand = 1 };
+enum { kDstIdx = 0, kDstCand = 1 };
+
+struct TopkArgs {
+  const float* scores;    // kSrcScores: [B][n_q][ld]
+  int64_t ld;
+  const uint32_t* ckey;   // kSrcCand: [B][n_q][n_cand] keys and positions
+  const int32_t* cpos;
+  int n_cand;
+  int n_q, n_kv, k;
+  int chunk;              // kSrcScores: keys per chunk (a multiple of 256); blockIdx.z = chunk number
+  int n_chunks;
+  int32_t* idx;           // kDstIdx: [B][n_q][k]
+  uint32_t* okey;         // kDstCand: [B][n_q][n_chunks * k]
+  int32_t* opos;
+  bool vec4;              // the first pass may use 16-byte loads
+};
 
 __device__ __forceinline__ unsigned int score_key(float f) {
   unsigned int u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;  // -0 == +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned int lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned int)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)m, 0u));
+}
+
+// Exclusive prefix over lanes of c (0 <= c <= 7) and its wave total, from the ballots of c's bits.
+__device__ __forceinline__ void lane_scan3(unsigned int c, unsigned int* before, unsigned int* total) {
+  const unsigned long long b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+  *before = lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
+  *total = (unsigned int)__popcll(b0) + 2u * (unsigned int)__popcll(b1) + 4u * (unsigned int)__popcll(b2);
+}
+
+__device__ __forceinline__ unsigned int wave_sum(unsigned int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
 }
 
 // Sum the histogram copies (256 threads, one bin each), then wave 0 fixes the digit: the highest bin
@@ -47,9 +93,7 @@ __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned 
   }
   __syncthreads();
   if (wave == 0) {
-    unsigned int c[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) c[j] = tot[4 * lane + j];
+    const u32x4 c = *reinterpret_cast<const u32x4*>(tot + 4 * lane);
     const unsigned int mine = c[0] + c[1] + c[2] + c[3];
     unsigned int suf = mine;  // inclusive suffix sum over lanes: keys in bins >= 4*lane
 #pragma unroll
@@ -71,122 +115,303 @@ __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned 
   __syncthreads();
 }
 
-template <bool CACHED>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld, int n_q,
-                                                          int n_kv, int k, int32_t* __restrict__ idx, bool vec4) {
+template <int SRC, int DST>
+__global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   extern __shared__ unsigned int lds[];
-  unsigned int* hist = lds;                         // [16][257]
-  unsigned int* misc = lds + kHistWords;            // [64] scratch
-  unsigned int* tot = misc + 64;                    // [256] summed histogram
-  unsigned int* rowk = lds + kHistWords + kMiscWords;  // [n] keys (CACHED only)
+  unsigned int* hist = lds;                            // [16][257]
+  unsigned int* misc = lds + kHistWords;               // [64] scratch
+  unsigned int* tot = misc + 64;                       // [256] summed histogram
+  unsigned int* rowk = lds + kHistWords + kMiscWords;  // [m] keys
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t = n_q - 1 - (int)blockIdx.x;  // longest rows first
+  const int t = a.n_q - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y;
-  const int n = n_kv - n_q + t + 1;
-  const size_t rowid = (size_t)b * n_q + t;
-  const float* row = scores + rowid * ld;
-  int32_t* out = idx + rowid * (size_t)k;
+  const int k = a.k;
+  const int n = a.n_kv - a.n_q + t + 1;  // causal row length
+  const size_t rowid = (size_t)b * a.n_q + t;
 
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = (i < n) ? i : -1;
+  int lo = 0, m;
+  if (SRC == kSrcScores) {
+    lo = (int)blockIdx.z * a.chunk;
+    m = min(n, lo + a.chunk) - lo;  // <= 0 when the chunk lies past pos_t
+  } else {
+    m = a.n_cand;
+  }
+  const float* srow = SRC == kSrcScores ? a.scores + rowid * a.ld + lo : nullptr;
+  const uint32_t* crow = SRC == kSrcCand ? a.ckey + rowid * (size_t)a.n_cand : nullptr;
+  const int32_t* cprow = SRC == kSrcCand ? a.cpos + rowid * (size_t)a.n_cand : nullptr;
+  int32_t* out_idx = DST == kDstIdx ? a.idx + rowid * (size_t)k : nullptr;
+  const size_t ostride = (size_t)a.n_chunks * k;
+  uint32_t* out_key = DST == kDstCand ? a.okey + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
+  int32_t* out_pos = DST == kDstCand ? a.opos + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
+
+  if (n <= k) {  // the row keeps all of its keys; stage one leaves such rows to stage two
+    if (DST == kDstIdx)
+      for (int i = tid; i < k; i += kTkThreads) out_idx[i] = (i < n) ? i : -1;
+    return;
+  }
+  if (DST == kDstCand && m <= k) {  // the whole chunk is candidates (none when m <= 0); pad with key 0
+    for (int i = tid; i < k; i += kTkThreads) {
+      const bool v = i < m;
+      out_key[i] = v ? score_key(srow[i]) : 0u;
+      out_pos[i] = v ? lo + i : -1;
+    }
     return;
   }
 
-  unsigned int prefix = 0u;
-  int k_rem = k;
+  // ---- pass 0: keys from memory into LDS, histogram of the top byte
   unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
+  for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
+  __syncthreads();
+  if (a.vec4) {
+    const int n4 = m >> 2;
+    for (int base = 0; base < n4; base += kTkThreads * kLoadUnroll) {
+      u32x4 v[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int j = base + u * kTkThreads + tid;
+        if (j < n4) {
+          if (SRC == kSrcScores) {
+            const float4 f = reinterpret_cast<const float4*>(srow)[j];
+            v[u] = (u32x4){score_key(f.x), score_key(f.y), score_key(f.z), score_key(f.w)};
+          } else {
+            v[u] = reinterpret_cast<const u32x4*>(crow)[j];
+          }
+        } else {
+          v[u] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int j = base + u * kTkThreads + tid;
+        if (j < n4) {
+          reinterpret_cast<u32x4*>(rowk)[j] = v[u];
+#pragma unroll
+          for (int e = 0; e < 4; e++) atomicAdd(&h[v[u][e] >> 24], 1u);
+        }
+      }
+    }
+    const int i = 4 * n4 + tid;  // tail of fewer than 4 keys
+    if (i < m) {
+      const unsigned int key = SRC == kSrcScores ? score_key(srow[i]) : crow[i];
+      rowk[i] = key;
+      atomicAdd(&h[key >> 24], 1u);
+    }
+  } else {
+    for (int base = 0; base < m; base += kTkThreads * kLoadUnroll) {
+      unsigned int v[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = base + u * kTkThreads + tid;
+        v[u] = i < m ? (SRC == kSrcScores ? score_key(srow[i]) : crow[i]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = base + u * kTkThreads + tid;
+        if (i < m) {
+          rowk[i] = v[u];
+          atomicAdd(&h[v[u] >> 24], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  select_digit(hist, misc, tot, k, tid, wave, lane);
+  unsigned int prefix = misc[0];
+  int k_rem = k - (int)misc[1];
+  __syncthreads();
 
+  // wave segments of the LDS keys: [s0, s1), s0 a multiple of 256
+  const int segw = ((m + kTkWaves * kSeg - 1) / (kTkWaves * kSeg)) * kSeg;
+  const int s0 = wave * segw;
+  const int s1 = min(m, s0 + segw);
+
+  // ---- passes 1..3 over LDS
 #pragma unroll 1
-  for (int pass = 0; pass < 4; pass++) {
+  for (int pass = 1; pass < 4; pass++) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
     __syncthreads();
-    if (pass == 0 || !CACHED) {
-      if (vec4) {
-        // 16-byte loads: kUnroll float4 per thread in flight, the tail (n % 4 keys) one by one
-        const float4* row4 = reinterpret_cast<const float4*>(row);
-        const int n4 = n >> 2;
-        for (int base = 0; base < n4; base += kTkThreads * kUnroll) {
-          float4 v[kUnroll];
+    for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
+      u32x4 kk[kLdsUnroll];
 #pragma unroll
-          for (int u = 0; u < kUnroll; u++) {
-            const int j = base + u * kTkThreads + tid;
-            v[u] = j < n4 ? row4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-#pragma unroll
-          for (int u = 0; u < kUnroll; u++) {
-            const int j = base + u * kTkThreads + tid;
-            if (j < n4) {
-              const unsigned int key[4] = {score_key(v[u].x), score_key(v[u].y), score_key(v[u].z),
-                                           score_key(v[u].w)};
-              if (CACHED) reinterpret_cast<u32x4*>(rowk)[j] = (u32x4){key[0], key[1], key[2], key[3]};
-#pragma unroll
-              for (int e = 0; e < 4; e++)
-                if (pass == 0 || (key[e] >> (shift + 8)) == prefix) atomicAdd(&h[(key[e] >> shift) & 255u], 1u);
-            }
-          }
-        }
-        const int i = 4 * n4 + tid;
-        if (i < n) {
-          const unsigned int key = score_key(row[i]);
-          if (CACHED) rowk[i] = key;
-          if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-        }
-      } else {
-        for (int base = 0; base < n; base += kTkThreads * kUnroll) {
-          float v[kUnroll];
-#pragma unroll
-          for (int u = 0; u < kUnroll; u++) {
-            const int i = base + u * kTkThreads + tid;
-            v[u] = i < n ? row[i] : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < kUnroll; u++) {
-            const int i = base + u * kTkThreads + tid;
-            if (i < n) {
-              const unsigned int key = score_key(v[u]);
-              if (CACHED) rowk[i] = key;
-              if (pass == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-            }
-          }
-        }
+      for (int u = 0; u < kLdsUnroll; u++) {
+        const int i = base + kSeg * u + 4 * lane;
+        kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
       }
-    } else {
-      for (int i = tid; i < n; i += kTkThreads) {
-        const unsigned int key = rowk[i];
-        if ((key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+#pragma unroll
+      for (int u = 0; u < kLdsUnroll; u++) {
+        const int i = base + kSeg * u + 4 * lane;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const unsigned int key = kk[u][e];
+          if (i + e < s1 && (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        }
       }
     }
     __syncthreads();
     select_digit(hist, misc, tot, k_rem, tid, wave, lane);
     prefix = (prefix << 8) | misc[0];
     k_rem -= (int)misc[1];
-    __syncthreads();  // misc is rewritten by the next pass
+    __syncthreads();  // misc is rewritten below
   }
   const unsigned int tau = prefix;  // the k-th largest key; k_rem keys equal to tau are taken
 
-  // ordered compaction over per-wave contiguous segments (kUnroll 64-wide groups per load batch)
+  // ---- ordered compaction: counts per wave segment, then the writes
+  unsigned int n_gt = 0, n_eq = 0;
+  for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
+    u32x4 kk[kLdsUnroll];
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) {
+      const int i = base + kSeg * u + 4 * lane;
+      kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) {
+      const int i = base + kSeg * u + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool v = i + e < s1;
+        n_gt += (v && kk[u][e] > tau) ? 1u : 0u;
+        n_eq += (v && kk[u][e] == tau) ? 1u : 0u;
+      }
+    }
+  }
+  n_gt = wave_sum(n_gt);
+  n_eq = wave_sum(n_eq);
+  if (lane == 0) {
+    misc[2 + wave] = n_gt;
+    misc[2 + kTkWaves + wave] = n_eq;
+  }
+  __syncthreads();
+  unsigned int gt_before = 0, eq_before = 0;
+  for (int w2 = 0; w2 < wave; w2++) {
+    gt_before += misc[2 + w2];
+    eq_before += misc[2 + kTkWaves + w2];
+  }
+  unsigned int e_run = eq_before;  // keys equal to tau before this point, in row order
+  unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);  // selected before this point
+  for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
+    u32x4 kk[kLdsUnroll];
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) {
+      const int i = base + kSeg * u + 4 * lane;
+      kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) {
+      const int i = base + kSeg * u + 4 * lane;
+      unsigned int eq_mask = 0, gt_mask = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool v = i + e < s1;
+        gt_mask |= (v && kk[u][e] > tau) ? (1u << e) : 0u;
+        eq_mask |= (v && kk[u][e] == tau) ? (1u << e) : 0u;
+      }
+      unsigned int e_before, e_total;
+      lane_scan3((unsigned int)__popc(eq_mask), &e_before, &e_total);
+      unsigned int er = e_run + e_before;  // tie rank of this lane's first key equal to tau
+      unsigned int sel_mask = gt_mask;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if (eq_mask & (1u << e)) {
+          if (er < (unsigned int)k_rem) sel_mask |= 1u << e;
+          er++;
+        }
+      }
+      unsigned int s_before, s_total;
+      lane_scan3((unsigned int)__popc(sel_mask), &s_before, &s_total);
+      unsigned int op = p_run + s_before;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if ((sel_mask & (1u << e)) && op < (unsigned int)k) {
+          if (DST == kDstIdx) {
+            out_idx[op] = SRC == kSrcScores ? lo + i + e : cprow[i + e];
+          } else {
+            out_key[op] = kk[u][e];
+            out_pos[op] = SRC == kSrcScores ? lo + i + e : cprow[i + e];
+          }
+        }
+        op += (sel_mask >> e) & 1u;
+      }
+      e_run += e_total;
+      p_run += s_total;
+    }
+  }
+}
+
+// Fallback for rows the LDS-resident kernels cannot take: every pass re-reads the row from memory.
+__global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                   int n_q, int n_kv, int k,
+                                                                   int32_t* __restrict__ idx) {
+  extern __shared__ unsigned int lds[];
+  unsigned int* hist = lds;
+  unsigned int* misc = lds + kHistWords;
+  unsigned int* tot = misc + 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t = n_q - 1 - (int)blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = n_kv - n_q + t + 1;
+  const size_t rowid = (size_t)b * n_q + t;
+  const float* row = scores + rowid * ld;
+  int32_t* out = idx + rowid * (size_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  unsigned int prefix = 0u;
+  int k_rem = k;
+  unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; pass++) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < n; base += kTkThreads * kLoadUnroll) {
+      float v[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = base + u * kTkThreads + tid;
+        v[u] = i < n ? row[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; u++) {
+        const int i = base + u * kTkThreads + tid;
+        const unsigned int key = score_key(v[u]);
+        if (i < n && (pass == 0 || (key >> (shift + 8)) == prefix)) atomicAdd(&h[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    select_digit(hist, misc, tot, k_rem, tid, wave, lane);
+    prefix = (prefix << 8) | misc[0];
+    k_rem -= (int)misc[1];
+    __syncthreads();
+  }
+  const unsigned int tau = prefix;
   const int seg = ((n + kTkWaves * 64 - 1) / (kTkWaves * 64)) * 64;
   const int s0 = wave * seg;
   const int s1 = min(n, s0 + seg);
   unsigned int n_gt = 0, n_eq = 0;
-  for (int i0 = s0; i0 < s1; i0 += 64 * kUnroll) {
-    unsigned int key[kUnroll];
+  for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
+    unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
-      key[u] = (i < s1) ? (CACHED ? rowk[i] : score_key(row[i])) : 0u;
+      key[u] = i < s1 ? score_key(row[i]) : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
-      n_gt += __popcll(__ballot(i < s1 && key[u] > tau));
-      n_eq += __popcll(__ballot(i < s1 && key[u] == tau));
+      n_gt += (i < s1 && key[u] > tau) ? 1u : 0u;
+      n_eq += (i < s1 && key[u] == tau) ? 1u : 0u;
     }
   }
+  n_gt = wave_sum(n_gt);
+  n_eq = wave_sum(n_eq);
   if (lane == 0) {
     misc[2 + wave] = n_gt;
     misc[2 + kTkWaves + wave] = n_eq;
@@ -199,25 +424,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   }
   unsigned int e_run = eq_before;
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
-  for (int i0 = s0; i0 < s1; i0 += 64 * kUnroll) {
-    unsigned int key[kUnroll];
+  for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
+    unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
-      key[u] = (i < s1) ? (CACHED ? rowk[i] : score_key(row[i])) : 0u;
+      key[u] = i < s1 ? score_key(row[i]) : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
       const bool g = (i < s1) && key[u] > tau;
       const bool e = (i < s1) && key[u] == tau;
       const unsigned long long be = __ballot(e);
-      const unsigned int erank = e_run + (unsigned int)__builtin_amdgcn_mbcnt_hi(
-                                             (unsigned int)(be >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)be, 0u));
+      const unsigned int erank = e_run + lanes_below(be);
       const bool sel = g || (e && erank < (unsigned int)k_rem);
       const unsigned long long bs = __ballot(sel);
-      const unsigned int opos = p_run + (unsigned int)__builtin_amdgcn_mbcnt_hi(
-                                            (unsigned int)(bs >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)bs, 0u));
+      const unsigned int opos = p_run + lanes_below(bs);
       if (sel && opos < (unsigned int)k) out[opos] = i;
       e_run += __popcll(be);
       p_run += __popcll(bs);
@@ -225,22 +448,107 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   }
 }
 
-hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,
-                       hipStream_t stream) {
-  dim3 grid(n_q, B);
-  // rows start on 16-byte boundaries when the base is aligned and ld is a multiple of 4
-  const bool vec4 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (ld & 3) == 0;
-  if (n_kv <= kRowCapMax) {
-    // more than 64 KiB of dynamic LDS needs an explicit opt-in (done once; thread-safe static init)
-    static const hipError_t attr = hipFuncSetAttribute((const void*)topk_kernel<true>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytesMax);
-    if (attr != hipSuccess) return attr;
-    size_t lds = (size_t)(kHistWords + kMiscWords + ((n_kv + 3) / 4) * 4) * 4;
-    hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx, vec4);
-  } else {
-    size_t lds = (size_t)(kHistWords + kMiscWords) * 4;
-    hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTkThreads), lds, stream, scores, ld, n_q, n_kv, k, idx, vec4);
+// ------------------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// More than 64 KiB of dynamic LDS needs an explicit opt-in, once per kernel.
+template <int SRC, int DST>
+hipError_t allow_full_lds() {
+  static const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<SRC, DST>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytesMax);
+  return e;
+}
+
+size_t lds_bytes(int keys) { return (size_t)(kHistWords + kMiscWords + ((keys + 3) / 4) * 4) * 4; }
+
+}  // namespace
+
+TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
+  TopkPlan p;
+  const long long rows = (long long)B * n_q;
+  p.mode = TopkPlan::kSingle;
+  p.chunk = n_kv;
+  p.n_chunks = 1;
+  p.ws = 0;
+  if (k < 1 || n_kv <= k) return p;  // every row keeps all of its keys (k < 1 is rejected by the caller)
+  int want = 1;
+  if (n_kv > kKeyCap) want = (n_kv + kKeyCap - 1) / kKeyCap;
+  if (rows < 256) {
+    // too few rows to fill the GPU: split each into chunks of at least 4k keys
+    const long long more = std::min<long long>((512 + rows - 1) / rows, n_kv / (4LL * k));
+    if (more > want) want = (int)more;
   }
+  if (want <= 1) return p;
+  const int chunk = (int)((((long long)n_kv + want - 1) / want + kSeg - 1) / kSeg * kSeg);
+  const int n_chunks = (n_kv + chunk - 1) / chunk;
+  if (n_chunks < 2 || chunk <= k || chunk > kKeyCap || (long long)n_chunks * k > kKeyCap) {
+    if (n_kv > kKeyCap) p.mode = TopkPlan::kUncached;
+    return p;
+  }
+  p.mode = TopkPlan::kTwoStage;
+  p.chunk = chunk;
+  p.n_chunks = n_chunks;
+  const size_t n_cand = (size_t)rows * n_chunks * k;
+  p.ws = align256(n_cand * sizeof(uint32_t)) + align256(n_cand * sizeof(int32_t));
+  return p;
+}
+
+hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,
+                       const TopkPlan& p, void* workspace, hipStream_t stream) {
+  TopkArgs a = {};
+  a.scores = scores;
+  a.ld = ld;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.k = k;
+  a.idx = idx;
+  // rows start on 16-byte boundaries when the base is aligned and ld is a multiple of 4
+  const bool rows16 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (ld & 3) == 0;
+  if (p.mode == TopkPlan::kUncached) {
+    hipLaunchKernelGGL(topk_uncached_kernel, dim3(n_q, B), dim3(kTkThreads), lds_bytes(0), stream, scores, ld, n_q,
+                       n_kv, k, idx);
+    return hipGetLastError();
+  }
+  if (p.mode == TopkPlan::kSingle) {
+    hipError_t e = allow_full_lds<kSrcScores, kDstIdx>();
+    if (e != hipSuccess) return e;
+    a.chunk = n_kv;
+    a.n_chunks = 1;
+    a.vec4 = rows16;
+    hipLaunchKernelGGL((topk_select_kernel<kSrcScores, kDstIdx>), dim3(n_q, B, 1), dim3(kTkThreads),
+                       lds_bytes(n_kv > k ? n_kv : 0), stream, a);
+    return hipGetLastError();
+  }
+  // two stages: chunk candidates into the workspace, then the merge
+  hipError_t e = allow_full_lds<kSrcScores, kDstCand>();
+  if (e != hipSuccess) return e;
+  e = allow_full_lds<kSrcCand, kDstIdx>();
+  if (e != hipSuccess) return e;
+  const size_t n_cand_all = (size_t)B * n_q * p.n_chunks * k;
+  uint32_t* ckey = (uint32_t*)workspace;
+  int32_t* cpos = (int32_t*)((char*)workspace + align256(n_cand_all * sizeof(uint32_t)));
+  a.chunk = p.chunk;
+  a.n_chunks = p.n_chunks;
+  a.okey = ckey;
+  a.opos = cpos;
+  a.vec4 = rows16;  // chunk starts are multiples of 256 keys
+  hipLaunchKernelGGL((topk_select_kernel<kSrcScores, kDstCand>), dim3(n_q, B, p.n_chunks), dim3(kTkThreads),
+                     lds_bytes(p.chunk), stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TopkArgs c = a;
+  c.ckey = ckey;
+  c.cpos = cpos;
+  c.n_cand = p.n_chunks * k;
+  c.vec4 = (c.n_cand & 3) == 0;  // the workspace is 256-byte aligned
+  c.okey = nullptr;
+  c.opos = nullptr;
+  hipLaunchKernelGGL((topk_select_kernel<kSrcCand, kDstIdx>), dim3(n_q, B, 1), dim3(kTkThreads),
+                     lds_bytes(c.n_cand), stream, c);
   return hipGetLastError();
 }
 

@@ -28,7 +28,8 @@ SIGNATURES = {
     "dsa_status_string": ([_I], ctypes.c_char_p),
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_indexer_scores": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
-    "dsa_topk": ([_P, _I64, _I, _I, _I, _I, _P, _P], _I),
+    "dsa_topk": ([_P, _I64, _I, _I, _I, _I, _P, _P, _SZ, _P], _I),
+    "dsa_topk_workspace_size": ([_I, _I, _I, _I], _SZ),
     "dsa_sparse_mla_attn": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
     "dsa_sparse_mla_attn_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "dsa_forward_prefill": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P,
@@ -119,13 +120,22 @@ def indexer_scores(q, q_scale, k, k_scale, w, scores, n_q=None, stream=None):
     return scores
 
 
-def topk(scores, n_kv: int, k: int, idx=None, stream=None):
-    """Per row the k best s <= pos_t (ascending, -1 padded).  scores [B, n_q, ld] f32 -> idx [B, n_q, k] int32."""
-    _dev(scores, idx)
+def topk_workspace_size(B: int, n_q: int, n_kv: int, k: int) -> int:
+    return int(lib().dsa_topk_workspace_size(B, n_q, n_kv, k))
+
+
+def topk(scores, n_kv: int, k: int, idx=None, workspace=None, stream=None):
+    """Per row the k best s <= pos_t (ascending, -1 padded).  scores [B, n_q, ld] f32 -> idx [B, n_q, k] int32.
+    workspace: uint8 device tensor of at least topk_workspace_size(...) bytes (allocated when missing)."""
+    _dev(scores, idx, workspace)
     B, nq, ld = scores.shape
     if idx is None:
         idx = torch.empty((B, nq, k), dtype=torch.int32, device=scores.device)
-    _check(lib().dsa_topk(_ptr(scores), ld, B, nq, n_kv, k, _ptr(idx), _stream(stream)))
+    ws = topk_workspace_size(B, nq, n_kv, k)
+    if ws and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=scores.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_topk(_ptr(scores), ld, B, nq, n_kv, k, _ptr(idx), _ptr(workspace), wsz, _stream(stream)))
     return idx
 
 

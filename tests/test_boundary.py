@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ["dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward_prefill", "dsa_forward_decode",
+    for n in ["dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_attn", "dsa_forward_prefill",
+              "dsa_forward_decode",
               "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
               "dsa_last_error", "dsa_version"]:
         assert n in names
@@ -61,14 +62,30 @@ FAKE2 = ctypes.c_void_p(0x20000)
 
 def test_topk_validation(L):
     from sparse_attention_13_amd.dsa import DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED
-    assert L.dsa_topk(None, 10, 1, 1, 10, 4, FAKE, None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(None, 10, 1, 1, 10, 4, FAKE, None, 0, None) == DSA_ERR_INVALID_ARG
     assert b"null" in L.dsa_last_error()
-    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 0, FAKE2, None) == DSA_ERR_INVALID_ARG  # k = 0
-    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 70000, FAKE2, None) == DSA_ERR_INVALID_ARG  # k too large
-    assert L.dsa_topk(FAKE, 9, 1, 1, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # ld < n_kv
-    assert L.dsa_topk(FAKE, 10, 1, 11, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # n_q > n_kv
-    assert L.dsa_topk(FAKE, 10, 0, 1, 10, 4, FAKE2, None) == DSA_ERR_INVALID_ARG  # B = 0
-    assert L.dsa_topk(FAKE, 10, 70000, 1, 10, 4, FAKE2, None) == DSA_ERR_UNSUPPORTED  # grid limit
+    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 0, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG  # k = 0
+    assert L.dsa_topk(FAKE, 10, 1, 1, 10, 70000, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG  # k too large
+    assert L.dsa_topk(FAKE, 9, 1, 1, 10, 4, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG  # ld < n_kv
+    assert L.dsa_topk(FAKE, 10, 1, 11, 10, 4, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG  # n_q > n_kv
+    assert L.dsa_topk(FAKE, 10, 0, 1, 10, 4, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG  # B = 0
+    assert L.dsa_topk(FAKE, 10, 70000, 1, 10, 4, FAKE2, None, 0, None) == DSA_ERR_UNSUPPORTED  # grid limit
+
+
+def test_topk_workspace(L):
+    from sparse_attention_13_amd.dsa import DSA_ERR_WORKSPACE
+    # many rows that fit the LDS-resident kernel: no workspace
+    assert L.dsa_topk_workspace_size(1, 32768, 32768, 2048) == 0
+    assert L.dsa_topk_workspace_size(1, 10, 10, 2048) == 0  # every row keeps all keys
+    assert L.dsa_topk_workspace_size(1, 10, 5, 4) == 0      # invalid: n_q > n_kv
+    # few long rows: two stages, candidates (key + position) of every chunk
+    ws = L.dsa_topk_workspace_size(64, 1, 131072, 2048)
+    assert ws >= 64 * 131072 // 16384 * 2048 * 8
+    big = ctypes.c_void_p(0x40000)
+    assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, None, 0, None) == DSA_ERR_WORKSPACE
+    assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, big, ws - 1, None) == DSA_ERR_WORKSPACE
+    assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, ctypes.c_void_p(0x40010), ws, None) \
+        == DSA_ERR_WORKSPACE  # misaligned
 
 
 def test_indexer_validation(L):

@@ -119,9 +119,14 @@ def test_indexer_fp8_exact_integers(orc, dsa):
 
 # ------------------------------------------------------------------------------------------ top-k
 
+# Covers the three launch plans: one LDS-resident pass per row (many rows, or rows up to the LDS key
+# capacity of 36352 with k too large to split), two stages (few or long rows; chunks past a row's end,
+# chunks shorter than k, unaligned rows), and the fallback that re-reads rows (k too large to split).
 @pytest.mark.parametrize("n_kv,n_q,k,extra_ld", [(300, 300, 32, 0), (5000, 64, 2048, 7), (2048, 16, 2048, 1),
                                                   (40000, 3, 2048, 0), (131072, 2, 2048, 64), (100, 100, 1, 0),
-                                                  (36480, 2, 4096, 0), (36481, 2, 4096, 0)])
+                                                  (36352, 2, 16384, 0), (36353, 2, 16384, 0),
+                                                  (1600, 200, 64, 0), (100000, 3, 2048, 5),
+                                                  (50000, 2, 30000, 0), (70000, 300, 2048, 0)])
 def test_topk_identical_scores_bit_exact(orc, dsa, n_kv, n_q, k, extra_ld):
     gen = np.random.default_rng(n_kv + k)
     ld = n_kv + extra_ld
