@@ -500,34 +500,39 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 }
 
 // Merge the n_split partial results of each (query, head): lse = log sum exp(lse_j),
-// out = sum_j exp(lse_j - lse) * O_j.  One workgroup per query, 256 threads.
+// out = sum_j exp(lse_j - lse) * O_j.  One wave per (query, head), 4 heads per workgroup; lane l
+// holds output columns 4l..4l+3 and 256+4l..256+4l+3 (two 16-byte loads per part).
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part,
                                                           const float* __restrict__ part_lse, int n_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const size_t row = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  for (int h = threadIdx.x >> 6; h < kH; h += 4) {
-    float mx = -INFINITY;
-    for (int j = 0; j < n_split; j++) mx = fmaxf(mx, part_lse[(row * n_split + j) * kH + h]);
-    float wsum = 0.f;
-    float acc[kDV / 64];
-#pragma unroll
-    for (int i = 0; i < kDV / 64; i++) acc[i] = 0.f;
+  const size_t row = (size_t)blockIdx.y * (gridDim.x / (kH / 4)) + blockIdx.x / (kH / 4);
+  const int h = (blockIdx.x % (kH / 4)) * 4 + wave;
+  const float* pl = part_lse + row * n_split * kH + h;
+  float mx = -INFINITY;
+  for (int j = 0; j < n_split; j++) mx = fmaxf(mx, pl[(size_t)j * kH]);
+  float wsum = 0.f;
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
     for (int j = 0; j < n_split; j++) {
-      const float lj = part_lse[(row * n_split + j) * kH + h];
-      if (lj == -INFINITY) continue;
+      const float lj = pl[(size_t)j * kH];
+      if (lj == -INFINITY) continue;  // a part without valid entries contributes nothing (wave-uniform)
       const float wj = __expf(lj - mx);
+      const v4f* pj = reinterpret_cast<const v4f*>(part + ((row * n_split + j) * kH + h) * kDV);
+      const v4f x0 = pj[lane], x1 = pj[64 + lane];
       wsum += wj;
-      const float* pj = part + ((row * n_split + j) * kH + h) * kDV;
-#pragma unroll
-      for (int i = 0; i < kDV / 64; i++) acc[i] = fmaf(wj, pj[i * 64 + lane], acc[i]);
+      a0 += wj * x0;
+      a1 += wj * x1;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* op = out + (row * kH + h) * kDV;
-#pragma unroll
-    for (int i = 0; i < kDV / 64; i++) op[i * 64 + lane] = f32_to_bf16_bits(acc[i] * inv);
-    if (lse && lane == 0) lse[row * kH + h] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* op = out + (row * kH + h) * kDV;
+  const u32x2 o0 = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv)};
+  const u32x2 o1 = {pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+  reinterpret_cast<u32x2*>(op)[lane] = o0;
+  reinterpret_cast<u32x2*>(op)[64 + lane] = o1;
+  if (lse && lane == 0) lse[row * kH + h] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
 size_t mla_bf16_workspace_bytes(int B, int n_q, int n_split) {
@@ -561,7 +566,7 @@ hipError_t launch_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t*
                      per_split, out, lse, part, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(n_q, B), dim3(256), 0, stream, (const float*)part,
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(n_q * (kH / 4), B), dim3(256), 0, stream, (const float*)part,
                      (const float*)part_lse, n_split, out, lse);
   return hipGetLastError();
 }

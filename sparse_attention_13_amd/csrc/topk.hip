@@ -81,6 +81,33 @@ __device__ __forceinline__ unsigned int wave_sum(unsigned int v) {
   return v;
 }
 
+// kLdsUnroll 16-byte LDS reads of keys [base + 256u + 4*lane, +4), all issued before any is used: the
+// address is clamped into [0, s1) so no read needs a branch; callers discard keys at or past s1.
+__device__ __forceinline__ void load_keys(const unsigned int* rowk, int base, int s1, int lane,
+                                          u32x4 (&kk)[kLdsUnroll]) {
+  const int last = (s1 - 1) & ~3;
+#pragma unroll
+  for (int u = 0; u < kLdsUnroll; u++) {
+    const int i = min(base + kSeg * u + 4 * lane, last);
+    kk[u] = *reinterpret_cast<const u32x4*>(rowk + i);
+  }
+}
+
+// Inclusive suffix sum over the 64 lanes (lane l: sum of v over lanes >= l).  Within each row of 16
+// lanes, four DPP row shifts toward lower lanes (sources past the row's end read 0); then every row
+// adds the totals of the rows above it, read from their first lanes.
+__device__ __forceinline__ unsigned int suffix_sum(unsigned int v, int lane) {
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xF, 0xF, true);  // row_shl:1
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xF, 0xF, true);  // row_shl:2
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, true);  // row_shl:4
+  v += (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xF, 0xF, true);  // row_shl:8
+  const unsigned int r1 = (unsigned int)__builtin_amdgcn_readlane((int)v, 16);
+  const unsigned int r2 = (unsigned int)__builtin_amdgcn_readlane((int)v, 32);
+  const unsigned int r3 = (unsigned int)__builtin_amdgcn_readlane((int)v, 48);
+  const int row = lane >> 4;
+  return v + (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
+}
+
 // Sum the histogram copies (256 threads, one bin each), then wave 0 fixes the digit: the highest bin
 // whose suffix count reaches k_rem.  Writes misc[0] = digit, misc[1] = keys above it.
 __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned int* misc, unsigned int* tot,
@@ -95,12 +122,7 @@ __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned 
   if (wave == 0) {
     const u32x4 c = *reinterpret_cast<const u32x4*>(tot + 4 * lane);
     const unsigned int mine = c[0] + c[1] + c[2] + c[3];
-    unsigned int suf = mine;  // inclusive suffix sum over lanes: keys in bins >= 4*lane
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned int o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
+    const unsigned int suf = suffix_sum(mine, lane);  // keys in bins >= 4*lane
     unsigned int above = suf - mine;  // keys in bins >= 4*lane + 4
 #pragma unroll
     for (int j = 3; j >= 0; j--) {
@@ -168,24 +190,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   if (a.vec4) {
     const int n4 = m >> 2;
     for (int base = 0; base < n4; base += kTkThreads * kLoadUnroll) {
+      // every load is issued unconditionally (index clamped into the row) so that all of them are in
+      // flight before the first is used; out-of-range values are discarded below
       u32x4 v[kLoadUnroll];
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
-        const int j = base + u * kTkThreads + tid;
-        if (j < n4) {
-          if (SRC == kSrcScores) {
-            const float4 f = reinterpret_cast<const float4*>(srow)[j];
-            v[u] = (u32x4){score_key(f.x), score_key(f.y), score_key(f.z), score_key(f.w)};
-          } else {
-            v[u] = reinterpret_cast<const u32x4*>(crow)[j];
-          }
-        } else {
-          v[u] = (u32x4){0u, 0u, 0u, 0u};
-        }
+        const int j = min(base + u * kTkThreads + tid, n4 - 1);
+        if (SRC == kSrcScores)
+          v[u] = __builtin_bit_cast(u32x4, reinterpret_cast<const float4*>(srow)[j]);
+        else
+          v[u] = reinterpret_cast<const u32x4*>(crow)[j];
       }
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int j = base + u * kTkThreads + tid;
+        if (SRC == kSrcScores)
+          v[u] = (u32x4){score_key(__uint_as_float(v[u][0])), score_key(__uint_as_float(v[u][1])),
+                         score_key(__uint_as_float(v[u][2])), score_key(__uint_as_float(v[u][3]))};
         if (j < n4) {
           reinterpret_cast<u32x4*>(rowk)[j] = v[u];
 #pragma unroll
@@ -204,12 +225,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
       unsigned int v[kLoadUnroll];
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = base + u * kTkThreads + tid;
-        v[u] = i < m ? (SRC == kSrcScores ? score_key(srow[i]) : crow[i]) : 0u;
+        const int i = min(base + u * kTkThreads + tid, m - 1);
+        v[u] = SRC == kSrcScores ? __float_as_uint(srow[i]) : crow[i];
       }
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int i = base + u * kTkThreads + tid;
+        if (SRC == kSrcScores) v[u] = score_key(__uint_as_float(v[u]));
         if (i < m) {
           rowk[i] = v[u];
           atomicAdd(&h[v[u] >> 24], 1u);
@@ -236,20 +258,21 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
     __syncthreads();
     for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
       u32x4 kk[kLdsUnroll];
+      load_keys(rowk, base, s1, lane, kk);
+      unsigned int hit = 0;  // bit 4u+e: key (u, e) is in range and carries the digits fixed so far
 #pragma unroll
       for (int u = 0; u < kLdsUnroll; u++) {
         const int i = base + kSeg * u + 4 * lane;
-        kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
-      }
 #pragma unroll
-      for (int u = 0; u < kLdsUnroll; u++) {
-        const int i = base + kSeg * u + 4 * lane;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const unsigned int key = kk[u][e];
-          if (i + e < s1 && (key >> (shift + 8)) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-        }
+        for (int e = 0; e < 4; e++)
+          hit |= (i + e < s1 && (kk[u][e] >> (shift + 8)) == prefix) ? 1u << (4 * u + e) : 0u;
       }
+      if (__ballot(hit != 0) == 0) continue;  // the common case once the prefix is long
+#pragma unroll
+      for (int u = 0; u < kLdsUnroll; u++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (hit & (1u << (4 * u + e))) atomicAdd(&h[(kk[u][e] >> shift) & 255u], 1u);
     }
     __syncthreads();
     select_digit(hist, misc, tot, k_rem, tid, wave, lane);
@@ -263,11 +286,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   unsigned int n_gt = 0, n_eq = 0;
   for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
     u32x4 kk[kLdsUnroll];
-#pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) {
-      const int i = base + kSeg * u + 4 * lane;
-      kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
-    }
+    load_keys(rowk, base, s1, lane, kk);
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = base + kSeg * u + 4 * lane;
@@ -295,11 +314,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);  // selected before this point
   for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
     u32x4 kk[kLdsUnroll];
-#pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) {
-      const int i = base + kSeg * u + 4 * lane;
-      kk[u] = i < s1 ? *reinterpret_cast<const u32x4*>(rowk + i) : (u32x4){0u, 0u, 0u, 0u};
-    }
+    load_keys(rowk, base, s1, lane, kk);
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = base + kSeg * u + 4 * lane;
@@ -310,16 +325,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
         gt_mask |= (v && kk[u][e] > tau) ? (1u << e) : 0u;
         eq_mask |= (v && kk[u][e] == tau) ? (1u << e) : 0u;
       }
-      unsigned int e_before, e_total;
-      lane_scan3((unsigned int)__popc(eq_mask), &e_before, &e_total);
-      unsigned int er = e_run + e_before;  // tie rank of this lane's first key equal to tau
       unsigned int sel_mask = gt_mask;
+      if (__ballot(eq_mask != 0) != 0) {  // keys equal to tau: the first k_rem of them in row order
+        unsigned int e_before, e_total;
+        lane_scan3((unsigned int)__popc(eq_mask), &e_before, &e_total);
+        unsigned int er = e_run + e_before;  // tie rank of this lane's first key equal to tau
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        if (eq_mask & (1u << e)) {
-          if (er < (unsigned int)k_rem) sel_mask |= 1u << e;
-          er++;
+        for (int e = 0; e < 4; e++) {
+          if (eq_mask & (1u << e)) {
+            if (er < (unsigned int)k_rem) sel_mask |= 1u << e;
+            er++;
+          }
         }
+        e_run += e_total;
       }
       unsigned int s_before, s_total;
       lane_scan3((unsigned int)__popc(sel_mask), &s_before, &s_total);
@@ -336,7 +354,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
         }
         op += (sel_mask >> e) & 1u;
       }
-      e_run += e_total;
       p_run += s_total;
     }
   }
@@ -374,10 +391,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
     for (int base = 0; base < n; base += kTkThreads * kLoadUnroll) {
       float v[kLoadUnroll];
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) {
-        const int i = base + u * kTkThreads + tid;
-        v[u] = i < n ? row[i] : 0.f;
-      }
+      for (int u = 0; u < kLoadUnroll; u++) v[u] = row[min(base + u * kTkThreads + tid, n - 1)];
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int i = base + u * kTkThreads + tid;
@@ -399,10 +413,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
   for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
     unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) {
-      const int i = i0 + 64 * u + lane;
-      key[u] = i < s1 ? score_key(row[i]) : 0u;
-    }
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = __float_as_uint(row[min(i0 + 64 * u + lane, s1 - 1)]);
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = score_key(__uint_as_float(key[u]));
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
@@ -427,10 +440,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
   for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
     unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) {
-      const int i = i0 + 64 * u + lane;
-      key[u] = i < s1 ? score_key(row[i]) : 0u;
-    }
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = __float_as_uint(row[min(i0 + 64 * u + lane, s1 - 1)]);
+#pragma unroll
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = score_key(__uint_as_float(key[u]));
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
