@@ -95,17 +95,65 @@ __device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b) {
 }
 
 // One group = 64 keys = 4 column blocks of 16.  Lane l loads key (16*j + l%16), bytes 32*(l/16)..+32
-// of column block j: the matrix-core B-operand layout.  Keys past the end are clamped (never stored).
-__device__ __forceinline__ void load_key_group(const uint8_t* __restrict__ kb, int g0, int n_kv, int lane,
-                                               v8i (&kf)[4]) {
+// of column block j: the matrix-core B-operand layout; with it, the scale of key g0 + l.  Keys past the
+// end are clamped (their scores are never stored).
+struct KeyGroup {
+  v8i kf[4];
+  float ksc;
+};
+
+// STREAM: the keys are read once (decode), so the loads are nontemporal; prefill keys are shared by
+// every query row and stay cacheable.
+template <bool STREAM>
+__device__ __forceinline__ void load_key_group(const uint8_t* __restrict__ kb, const float* __restrict__ ksb, int g0,
+                                               int n_kv, int lane, KeyGroup& g) {
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    int s = min(g0 + 16 * j + (lane & 15), n_kv - 1);
-    kf[j] = *(const v8i*)(kb + (size_t)s * kDI + (lane >> 4) * 32);
+    const int s = min(g0 + 16 * j + (lane & 15), n_kv - 1);
+    const v8i* p = (const v8i*)(kb + (size_t)s * kDI + (lane >> 4) * 32);
+    g.kf[j] = STREAM ? __builtin_nontemporal_load(p) : *p;
+  }
+  const float* ps = ksb + min(g0 + lane, n_kv - 1);
+  g.ksc = STREAM ? __builtin_nontemporal_load(ps) : *ps;
+}
+
+// Scores of one key group for the wave's QW queries; lane l stores key g0 + l.
+template <int QW>
+__device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&qa)[QW][4],
+                                                const float (&ww)[QW][4][4], int g0, int s_end, int pos0,
+                                                int nq_here, int lane, float* __restrict__ srow, int64_t ld) {
+  float out[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) out[qi] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    v4f acc[QW][4];
+#pragma unroll
+    for (int qi = 0; qi < QW; qi++)
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) acc[qi][mb] = mfma_f8_16x16x128(qa[qi][mb], g.kf[j]);
+#pragma unroll
+    for (int qi = 0; qi < QW; qi++) {
+      float v = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], fmaxf(acc[qi][mb][r], 0.0f), v);
+      v = xor16_sum(v);
+      v = xor32_sum(v);
+      out[qi] = ((lane >> 4) == j) ? v : out[qi];
+    }
+  }
+  // lane l now holds the score of key g0 + l for every query of the wave
+  const int s = g0 + lane;
+  if (s < s_end) {
+#pragma unroll
+    for (int qi = 0; qi < QW; qi++)
+      if (qi < nq_here && s <= pos0 + qi) srow[(size_t)qi * ld + s] = out[qi] * g.ksc + 0.0f;
   }
 }
 
-template <int QW>
+template <int QW, int NB>
 __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __restrict__ q8,
                                                              const float* __restrict__ q_scale,
                                                              const float* __restrict__ w,
@@ -129,6 +177,10 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   if (s_begin > pos_last) return;
   const int s_end = min(pos_last + 1, s_begin + chunk_keys);
 
+  const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
+  const float* ksb = k_scale + (size_t)b * n_kv;
+  float* srow = scores + ((size_t)b * n_q + t0) * ld;
+
   // A operands: row block mb holds heads 16*mb .. 16*mb+15; lane l supplies head 16*mb + l%16,
   // bytes 32*(l/16) .. +32 of that head's 128-byte query.
   v8i qa[QW][4];
@@ -148,48 +200,35 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
         ww[qi][mb][r] = w[qrow * kHI + h] * q_scale[qrow * kHI + h];
       }
   }
+  // The query side is complete before any key load is issued: the loop below then only ever waits for
+  // key groups, never (through the wait analysis' merge at the loop head) for everything in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
-  const float* ksb = k_scale + (size_t)b * n_kv;
-  float* srow = scores + ((size_t)b * n_q + t0) * ld;
+  // Key loads are unconditional (indexes are clamped into the row, so groups past the range re-read
+  // in-bounds keys that are never scored): with no load skipped on any path, each wait below covers
+  // exactly the group it needs.
+  KeyGroup ring[NB];
+#pragma unroll
+  for (int p = 0; p < NB - 1; p++) load_key_group<QW == 1>(kb, ksb, s_begin + 64 * p, n_kv, lane, ring[p]);
 
-  v8i kcur[4], knext[4];
-  load_key_group(kb, s_begin, n_kv, lane, kcur);
-  for (int g0 = s_begin; g0 < s_end; g0 += 64) {
-    if (g0 + 64 < s_end) load_key_group(kb, g0 + 64, n_kv, lane, knext);
-    const int s = g0 + lane;
-    const float ksc = ksb[min(s, n_kv - 1)];
-    float out[QW];
+  // Ring of NB key groups: group i lives in slot i % NB.  The main loop runs whole rounds of NB groups
+  // with no early exit (every slot index static, every wait exact); loads for group i + NB - 1 are
+  // issued before group i is scored.  The last n_groups % NB groups are already in slots 0.. and are
+  // scored after the loop.
+  const int n_groups = (s_end - s_begin + 63) / 64;
+  int gi = 0;
+  for (; gi + NB <= n_groups; gi += NB) {
 #pragma unroll
-    for (int qi = 0; qi < QW; qi++) out[qi] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      v4f acc[QW][4];
-#pragma unroll
-      for (int qi = 0; qi < QW; qi++)
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++) acc[qi][mb] = mfma_f8_16x16x128(qa[qi][mb], kcur[j]);
-#pragma unroll
-      for (int qi = 0; qi < QW; qi++) {
-        float v = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-          for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], fmaxf(acc[qi][mb][r], 0.0f), v);
-        v = xor16_sum(v);
-        v = xor32_sum(v);
-        out[qi] = ((lane >> 4) == j) ? v : out[qi];
-      }
+    for (int p = 0; p < NB; p++) {
+      const int g0 = s_begin + 64 * (gi + p);
+      load_key_group<QW == 1>(kb, ksb, g0 + 64 * (NB - 1), n_kv, lane, ring[(p + NB - 1) % NB]);
+      score_key_group<QW>(ring[p], qa, ww, g0, s_end, pos0, nq_here, lane, srow, ld);
     }
-    // lane l now holds the score of key g0 + l for every query of the wave
-    if (s < s_end) {
-#pragma unroll
-      for (int qi = 0; qi < QW; qi++)
-        if (qi < nq_here && s <= pos0 + qi) srow[(size_t)qi * ld + s] = out[qi] * ksc + 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) kcur[j] = knext[j];
   }
+#pragma unroll
+  for (int p = 0; p < NB - 1; p++)
+    if (gi + p < n_groups) score_key_group<QW>(ring[p], qa, ww, s_begin + 64 * (gi + p), s_end, pos0, nq_here, lane,
+                                               srow, ld);
 }
 
 hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint8_t* k, const float* k_scale,
@@ -203,8 +242,8 @@ hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint
     const long long items = (long long)B * n_qgroups * n_chunks;
     if (items > (1LL << 30)) return hipErrorInvalidValue;
     const int blocks = (int)((items + 3) / 4);
-    hipLaunchKernelGGL(indexer_fp8_kernel<QW>, dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k, k_scale,
-                       scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
+    hipLaunchKernelGGL((indexer_fp8_kernel<QW, 2>), dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k,
+                       k_scale, scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
   } else {
     constexpr int QW = 1;
     const int n_qgroups = n_q;
@@ -220,8 +259,8 @@ hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint
     const long long items = (long long)B * n_qgroups * n_chunks;
     if (items > (1LL << 30)) return hipErrorInvalidValue;
     const int blocks = (int)((items + 3) / 4);
-    hipLaunchKernelGGL(indexer_fp8_kernel<QW>, dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k, k_scale,
-                       scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
+    hipLaunchKernelGGL((indexer_fp8_kernel<QW, 3>), dim3(blocks), dim3(256), 0, stream, q, q_scale, w, k,
+                       k_scale, scores, ld, B, n_q, n_kv, n_qgroups, n_chunks, chunk, (int)items);
   }
   return hipGetLastError();
 }
