@@ -320,18 +320,22 @@ __device__ __forceinline__ bool pipeline_step(int it, int n_steps, int e_n, cons
   }
   float psum = 0.f;
   unsigned int pk[8];
+  // P^T fragments of one 16-key half, one per head block: read once per half (they serve all four
+  // output blocks), before the copies below, which the compiler must assume may write any LDS byte
+  v8bf pf[4];
 #pragma unroll
   for (int g8 = 0; g8 < 8; g8++) {
+    if (DO_PV && (g8 & 3) == 0) {
+#pragma unroll
+      for (int hb = 0; hb < 4; hb++) pf[hb] = __builtin_bit_cast(v8bf, pl[(hb * 2 + (g8 >> 2)) * 64 + lane]);
+    }
     if (has_next) gather_copy(kvb, g, g8, ntile, wave, lane);
     if (DO_PV) {
-      const int ks2 = g8 >> 2, db = g8 & 3;
+      const int db = g8 & 3;
       if (g8 == 4) load_vfrags<1>(ptile, wave, lane, vr);
       const v8bf vf = vfrag(vr, db);
 #pragma unroll
-      for (int hb = 0; hb < 4; hb++) {
-        const v8bf pf = __builtin_bit_cast(v8bf, pl[(hb * 2 + ks2) * 64 + lane]);
-        o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db][hb], 0, 0, 0);
-      }
+      for (int hb = 0; hb < 4; hb++) o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hb], o[db][hb], 0, 0, 0);
     }
     if (DO_QK) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(x[2 * g8], c_scale, neg_m));
