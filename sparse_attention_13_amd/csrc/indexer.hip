@@ -117,6 +117,11 @@ __device__ __forceinline__ void load_key_group(const uint8_t* __restrict__ kb, c
   g.ksc = STREAM ? __builtin_nontemporal_load(ps) : *ps;
 }
 
+// max(x, 0) as one integer max on the bit pattern: every negative float (and -0) has the sign bit set
+// and compares below 0, the rest are unchanged.  (fmaxf costs two instructions here: the IEEE mode
+// canonicalises its input first.)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores of one key group for the wave's QW queries; lane l stores key g0 + l.
 template <int QW>
 __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&qa)[QW][4],
@@ -138,7 +143,7 @@ __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&q
 #pragma unroll
       for (int mb = 0; mb < 4; mb++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], fmaxf(acc[qi][mb][r], 0.0f), v);
+        for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], relu_bits(acc[qi][mb][r]), v);
       v = xor16_sum(v);
       v = xor32_sum(v);
       out[qi] = ((lane >> 4) == j) ? v : out[qi];
@@ -231,10 +236,119 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
                                                srow, ld);
 }
 
+// ------------------------------------------------------------------------------------------------
+// Prefill: one workgroup = 4 waves x 2 queries = 8 consecutive queries that share their keys.  Each
+// 64-key group is read from memory once per workgroup (every wave loads a quarter of it into
+// registers one group ahead, then writes it to LDS), and every wave takes its matrix-core operands
+// from LDS: the cache traffic for keys drops four-fold against one load per wave.
+// LDS group layout: 64 rows of 128 B, 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so
+// the operand reads (16 rows x one chunk per 16 lanes) hit every bank once; then the 64 scales.
+// Two group slots: while group g is scored from one, group g+1 is written into the other; one barrier
+// per group.
+// ------------------------------------------------------------------------------------------------
+constexpr int kGrpKeyBytes = 64 * kDI;
+constexpr int kGrpBytes = kGrpKeyBytes + 64 * 4;
+
+__device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256, 2) void indexer_fp8_shared_kernel(const uint8_t* __restrict__ q8,
+                                                                    const float* __restrict__ q_scale,
+                                                                    const float* __restrict__ w,
+                                                                    const uint8_t* __restrict__ k8,
+                                                                    const float* __restrict__ k_scale,
+                                                                    float* __restrict__ scores, int64_t ld,
+                                                                    int n_q, int n_kv, int n_oct) {
+  constexpr int QW = 2;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kGrpBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int o = n_oct - 1 - (int)blockIdx.x;  // longest rows first
+  const int b = blockIdx.y;
+  const int t_last = min(8 * o + 7, n_q - 1);
+  const int pos_max = n_kv - n_q + t_last;
+  const int n_groups = (pos_max + 64) / 64;  // keys 0 .. pos_max
+  const int t0 = 8 * o + QW * wave;
+  const int nq_here = max(0, min(QW, n_q - t0));  // 0 for the spare waves of the last octet
+  const int pos0 = n_kv - n_q + t0;
+
+  const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
+  const float* ksb = k_scale + (size_t)b * n_kv;
+  float* srow = scores + ((size_t)b * n_q + min(t0, n_q - 1)) * ld;
+
+  // this wave's quarter of a group: row 16w + l/4, bytes 32 (l%4) .. +32; lane l also loads scale l
+  const int st_row = 16 * wave + (lane >> 2);
+  const int st_c = 2 * (lane & 3);
+  auto stage_load = [&](int g, v8i& kv, float& sc) {
+    const int r = min(64 * g + st_row, n_kv - 1);
+    kv = *(const v8i*)(kb + (size_t)r * kDI + st_c * 16);
+    sc = ksb[min(64 * g + lane, n_kv - 1)];
+  };
+  auto stage_store = [&](int slot, const v8i& kv, float sc) {
+    unsigned char* base = lds[slot] + st_row * kDI;
+    *(u32x4*)(base + (chunk_slot(st_row, st_c) << 4)) = (u32x4){(unsigned)kv[0], (unsigned)kv[1], (unsigned)kv[2],
+                                                                (unsigned)kv[3]};
+    *(u32x4*)(base + (chunk_slot(st_row, st_c + 1) << 4)) =
+        (u32x4){(unsigned)kv[4], (unsigned)kv[5], (unsigned)kv[6], (unsigned)kv[7]};
+    if (wave == 0) ((float*)(lds[slot] + kGrpKeyBytes))[lane] = sc;
+  };
+
+  // A operands and head weights of this wave's two queries (clamped to a valid row; spare waves
+  // compute on it and store nothing)
+  v8i qa[QW][4];
+  float ww[QW][4][4];
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) {
+    const int t = min(t0 + qi, n_q - 1);
+    const size_t qrow = (size_t)b * n_q + t;
+    const uint8_t* qp = q8 + qrow * kHI * kDI;
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) qa[qi][mb] = *(const v8i*)(qp + (16 * mb + (lane & 15)) * kDI + (lane >> 4) * 32);
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int h = 16 * mb + 4 * (lane >> 4) + r;
+        ww[qi][mb][r] = w[qrow * kHI + h] * q_scale[qrow * kHI + h];
+      }
+  }
+
+  v8i stg;
+  float stg_sc;
+  stage_load(0, stg, stg_sc);
+  stage_store(0, stg, stg_sc);
+  stage_load(1, stg, stg_sc);
+  __syncthreads();
+
+  // operand reads: block j, lane l: row 16j + l%16, chunks 2(l/16) and 2(l/16)+1
+  const int fr_c = 2 * (lane >> 4);
+  for (int g = 0; g < n_groups; g++) {
+    const int cur = g & 1;
+    stage_store(cur ^ 1, stg, stg_sc);  // group g+1 (its slot was last read in step g-1)
+    stage_load(g + 2, stg, stg_sc);     // rows clamped: past the end it re-reads in-bounds keys
+    KeyGroup kg;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int r = 16 * j + (lane & 15);
+      const unsigned char* rowp = lds[cur] + r * kDI;
+      const u32x4 lo = *(const u32x4*)(rowp + (chunk_slot(r, fr_c) << 4));
+      const u32x4 hi = *(const u32x4*)(rowp + (chunk_slot(r, fr_c + 1) << 4));
+      kg.kf[j] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    kg.ksc = ((const float*)(lds[cur] + kGrpKeyBytes))[lane];
+    if (nq_here > 0)
+      score_key_group<QW>(kg, qa, ww, 64 * g, pos0 + nq_here, pos0, nq_here, lane, srow, ld);
+    __syncthreads();
+  }
+}
+
 hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint8_t* k, const float* k_scale,
                               const float* w, int B, int n_q, int n_kv, float* scores, int64_t ld,
                               int keys_per_wave, hipStream_t stream) {
-  if (n_q >= 2) {
+  if (n_q >= 8 && keys_per_wave <= 0) {
+    const int n_oct = (n_q + 7) / 8;
+    hipLaunchKernelGGL(indexer_fp8_shared_kernel, dim3(n_oct, B), dim3(256), 0, stream, q, q_scale, w, k, k_scale,
+                       scores, ld, n_q, n_kv, n_oct);
+  } else if (n_q >= 2) {
     constexpr int QW = 2;
     const int n_qgroups = (n_q + QW - 1) / QW;
     const int chunk = keys_per_wave > 0 ? ((keys_per_wave + 63) / 64) * 64 : ((n_kv + 63) / 64) * 64;
