@@ -127,9 +127,8 @@ template <int QW>
 __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&qa)[QW][4],
                                                 const float (&ww)[QW][4][4], int g0, int s_end, int pos0,
                                                 int nq_here, int lane, float* __restrict__ srow, int64_t ld) {
-  float out[QW];
-#pragma unroll
-  for (int qi = 0; qi < QW; qi++) out[qi] = 0.0f;
+  // part[qi][j]: this lane's share (its 16 heads) of the score of key 16j + l%16
+  float part[QW][4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     v4f acc[QW][4];
@@ -144,10 +143,26 @@ __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&q
       for (int mb = 0; mb < 4; mb++)
 #pragma unroll
         for (int r = 0; r < 4; r++) v = fmaf(ww[qi][mb][r], relu_bits(acc[qi][mb][r]), v);
-      v = xor16_sum(v);
-      v = xor32_sum(v);
-      out[qi] = ((lane >> 4) == j) ? v : out[qi];
+      part[qi][j] = v;
     }
+  }
+  // Reduce-scatter over the four 16-lane rows: afterwards lane l holds the full score of key 16(l/16)
+  // + l%16 = l.  Step 1 (lanes l, l^32): the lower half keeps blocks 0 and 1, the upper half 2 and 3;
+  // step 2 (lanes l, l^16): rows keep block row.  Each swap-and-add is one permlane swap and one add.
+  float out[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) {
+    // permlane32_swap(a, b) trades the upper 32 lanes of a with the lower 32 lanes of b, so the lower
+    // half ends with (a, partner's a) and the upper half with (partner's b, b); permlane16_swap does
+    // the same between the odd rows of a and the even rows of b.
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi][0]), __float_as_uint(part[qi][2]),
+                                                      false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi][1]), __float_as_uint(part[qi][3]),
+                                                      false, false);
+    const float ra = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // block 0 (lower) / 2 (upper)
+    const float rb = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // block 1 (lower) / 3 (upper)
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(ra), __float_as_uint(rb), false, false);
+    out[qi] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
   }
   // lane l now holds the score of key g0 + l for every query of the wave
   const int s = g0 + lane;
