@@ -108,6 +108,8 @@ __device__ __forceinline__ unsigned int suffix_sum(unsigned int v, int lane) {
   return v + (row < 1 ? r1 : 0u) + (row < 2 ? r2 : 0u) + (row < 3 ? r3 : 0u);
 }
 
+__device__ __forceinline__ void scan_digit(const unsigned int* tot, unsigned int* misc, int k_rem, int wave, int lane);
+
 // Sum the histogram copies (256 threads, one bin each), then wave 0 fixes the digit: the highest bin
 // whose suffix count reaches k_rem.  Writes misc[0] = digit, misc[1] = keys above it.
 __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned int* misc, unsigned int* tot,
@@ -119,6 +121,12 @@ __device__ __forceinline__ void select_digit(const unsigned int* hist, unsigned 
     tot[tid] = s;
   }
   __syncthreads();
+  scan_digit(tot, misc, k_rem, wave, lane);
+}
+
+// Wave 0 fixes the digit from the summed histogram `tot`: the highest bin whose suffix count reaches
+// k_rem.  Writes misc[0] = digit, misc[1] = keys above it; ends with a barrier.
+__device__ __forceinline__ void scan_digit(const unsigned int* tot, unsigned int* misc, int k_rem, int wave, int lane) {
   if (wave == 0) {
     const u32x4 c = *reinterpret_cast<const u32x4*>(tot + 4 * lane);
     const unsigned int mine = c[0] + c[1] + c[2] + c[3];
@@ -250,40 +258,50 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   const int s0 = wave * segw;
   const int s1 = min(m, s0 + segw);
 
-  // ---- passes 1..3 over LDS
+  // ---- passes over LDS: one histogram pass per digit over the whole row, digits first .. last-1
+  auto lds_hist_passes = [&](int first, int last) {
 #pragma unroll 1
-  for (int pass = 1; pass < 4; pass++) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
-    __syncthreads();
-    for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
-      u32x4 kk[kLdsUnroll];
-      load_keys(rowk, base, s1, lane, kk);
-      unsigned int hit = 0;  // bit 4u+e: key (u, e) is in range and carries the digits fixed so far
+    for (int pass = first; pass < last; pass++) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
+      __syncthreads();
+      for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
+        u32x4 kk[kLdsUnroll];
+        load_keys(rowk, base, s1, lane, kk);
+        unsigned int hit = 0;  // bit 4u+e: key (u, e) is in range and carries the digits fixed so far
 #pragma unroll
-      for (int u = 0; u < kLdsUnroll; u++) {
-        const int i = base + kSeg * u + 4 * lane;
+        for (int u = 0; u < kLdsUnroll; u++) {
+          const int i = base + kSeg * u + 4 * lane;
 #pragma unroll
-        for (int e = 0; e < 4; e++)
-          hit |= (i + e < s1 && (kk[u][e] >> (shift + 8)) == prefix) ? 1u << (4 * u + e) : 0u;
+          for (int e = 0; e < 4; e++)
+            hit |= (i + e < s1 && (kk[u][e] >> (shift + 8)) == prefix) ? 1u << (4 * u + e) : 0u;
+        }
+        if (__ballot(hit != 0) == 0) continue;
+#pragma unroll
+        for (int u = 0; u < kLdsUnroll; u++)
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (hit & (1u << (4 * u + e))) atomicAdd(&h[(kk[u][e] >> shift) & 255u], 1u);
       }
-      if (__ballot(hit != 0) == 0) continue;  // the common case once the prefix is long
-#pragma unroll
-      for (int u = 0; u < kLdsUnroll; u++)
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-          if (hit & (1u << (4 * u + e))) atomicAdd(&h[(kk[u][e] >> shift) & 255u], 1u);
+      __syncthreads();
+      select_digit(hist, misc, tot, k_rem, tid, wave, lane);
+      prefix = (prefix << 8) | misc[0];
+      k_rem -= (int)misc[1];
+      __syncthreads();  // misc is rewritten next
     }
-    __syncthreads();
-    select_digit(hist, misc, tot, k_rem, tid, wave, lane);
-    prefix = (prefix << 8) | misc[0];
-    k_rem -= (int)misc[1];
-    __syncthreads();  // misc is rewritten below
-  }
-  const unsigned int tau = prefix;  // the k-th largest key; k_rem keys equal to tau are taken
+  };
+  lds_hist_passes(1, 2);  // second byte: nearly every key still carries the first
 
-  // ---- ordered compaction: counts per wave segment, then the writes
-  unsigned int n_gt = 0, n_eq = 0;
+  // ---- one sweep over the row: per wave, the keys above the 16-bit prefix are counted and the
+  // positions of the keys on it (the candidates, a small set for real score rows) are listed in the
+  // histogram area.  The last two digits and the per-wave counts above and at tau then come from the
+  // list.  A list that does not fit (rows with very many keys on one 16-bit prefix) falls back to
+  // two more histogram passes over the row and a counting sweep.
+  unsigned int* clist = hist;
+  unsigned int* ccount = misc + 20;
+  if (tid == 0) *ccount = 0u;
+  __syncthreads();
+  unsigned int n_above = 0;
   for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
     u32x4 kk[kLdsUnroll];
     load_keys(rowk, base, s1, lane, kk);
@@ -293,18 +311,76 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const bool v = i + e < s1;
-        n_gt += (v && kk[u][e] > tau) ? 1u : 0u;
-        n_eq += (v && kk[u][e] == tau) ? 1u : 0u;
+        const unsigned int top = kk[u][e] >> 16;
+        n_above += (v && top > prefix) ? 1u : 0u;
+        if (v && top == prefix) {
+          const unsigned int slot = atomicAdd(ccount, 1u);
+          if (slot < (unsigned int)kHistWords) clist[slot] = (unsigned int)(i + e);
+        }
       }
     }
   }
-  n_gt = wave_sum(n_gt);
-  n_eq = wave_sum(n_eq);
-  if (lane == 0) {
-    misc[2 + wave] = n_gt;
-    misc[2 + kTkWaves + wave] = n_eq;
-  }
+  n_above = wave_sum(n_above);
   __syncthreads();
+  const unsigned int n_cand = *ccount;
+  if (n_cand <= (unsigned int)kHistWords) {
+#pragma unroll 1
+    for (int pass = 2; pass < 4; pass++) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) tot[tid] = 0u;
+      __syncthreads();
+      for (unsigned int c = tid; c < n_cand; c += kTkThreads) {
+        const unsigned int key = rowk[clist[c]];
+        if ((key >> (shift + 8)) == prefix) atomicAdd(&tot[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      scan_digit(tot, misc, k_rem, wave, lane);
+      prefix = (prefix << 8) | misc[0];
+      k_rem -= (int)misc[1];
+      __syncthreads();
+    }
+    if (lane == 0) {
+      misc[2 + wave] = n_above;
+      misc[2 + kTkWaves + wave] = 0u;
+    }
+    __syncthreads();
+    for (unsigned int c = tid; c < n_cand; c += kTkThreads) {
+      const unsigned int pos = clist[c];
+      const unsigned int key = rowk[pos];
+      const unsigned int w = pos / (unsigned int)segw;
+      if (key > prefix) atomicAdd(&misc[2 + w], 1u);
+      else if (key == prefix) atomicAdd(&misc[2 + kTkWaves + w], 1u);
+    }
+    __syncthreads();
+  } else {
+    lds_hist_passes(2, 4);
+    const unsigned int t = prefix;
+    unsigned int n_gt = 0, n_eq = 0;
+    for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
+      u32x4 kk[kLdsUnroll];
+      load_keys(rowk, base, s1, lane, kk);
+#pragma unroll
+      for (int u = 0; u < kLdsUnroll; u++) {
+        const int i = base + kSeg * u + 4 * lane;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const bool v = i + e < s1;
+          n_gt += (v && kk[u][e] > t) ? 1u : 0u;
+          n_eq += (v && kk[u][e] == t) ? 1u : 0u;
+        }
+      }
+    }
+    n_gt = wave_sum(n_gt);
+    n_eq = wave_sum(n_eq);
+    if (lane == 0) {
+      misc[2 + wave] = n_gt;
+      misc[2 + kTkWaves + wave] = n_eq;
+    }
+    __syncthreads();
+  }
+  const unsigned int tau = prefix;  // the k-th largest key; k_rem keys equal to tau are taken
+
+  // ---- ordered compaction: every wave writes its selected positions from its output offset
   unsigned int gt_before = 0, eq_before = 0;
   for (int w2 = 0; w2 < wave; w2++) {
     gt_before += misc[2 + w2];
