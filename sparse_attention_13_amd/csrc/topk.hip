@@ -209,13 +209,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
         else
           v[u] = reinterpret_cast<const u32x4*>(crow)[j];
       }
+      const bool full = base + kLoadUnroll * kTkThreads <= n4;  // no bounds test per element
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int j = base + u * kTkThreads + tid;
         if (SRC == kSrcScores)
           v[u] = (u32x4){score_key(__uint_as_float(v[u][0])), score_key(__uint_as_float(v[u][1])),
                          score_key(__uint_as_float(v[u][2])), score_key(__uint_as_float(v[u][3]))};
-        if (j < n4) {
+        if (full || j < n4) {
           reinterpret_cast<u32x4*>(rowk)[j] = v[u];
 #pragma unroll
           for (int e = 0; e < 4; e++) atomicAdd(&h[v[u][e] >> 24], 1u);
@@ -277,11 +278,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
             hit |= (i + e < s1 && (kk[u][e] >> (shift + 8)) == prefix) ? 1u << (4 * u + e) : 0u;
         }
         if (__ballot(hit != 0) == 0) continue;
+        // no branch per key: keys off the prefix count into the pad word of the copy (bin 256)
 #pragma unroll
         for (int u = 0; u < kLdsUnroll; u++)
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            if (hit & (1u << (4 * u + e))) atomicAdd(&h[(kk[u][e] >> shift) & 255u], 1u);
+            atomicAdd(&h[(hit & (1u << (4 * u + e))) ? (kk[u][e] >> shift) & 255u : 256u], 1u);
       }
       __syncthreads();
       select_digit(hist, misc, tot, k_rem, tid, wave, lane);
@@ -305,6 +307,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
     u32x4 kk[kLdsUnroll];
     load_keys(rowk, base, s1, lane, kk);
+    unsigned int cmask = 0;  // bit 4u+e: key (u, e) is a candidate
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = base + kSeg * u + 4 * lane;
@@ -313,10 +316,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
         const bool v = i + e < s1;
         const unsigned int top = kk[u][e] >> 16;
         n_above += (v && top > prefix) ? 1u : 0u;
-        if (v && top == prefix) {
-          const unsigned int slot = atomicAdd(ccount, 1u);
-          if (slot < (unsigned int)kHistWords) clist[slot] = (unsigned int)(i + e);
-        }
+        cmask |= (v && top == prefix) ? 1u << (4 * u + e) : 0u;
+      }
+    }
+    if (__ballot(cmask != 0) != 0) {  // a few candidates per batch: append them, one slot range per lane
+      unsigned int slot = cmask ? atomicAdd(ccount, (unsigned int)__popc(cmask)) : 0u;
+      while (cmask) {
+        const int b = __builtin_ctz(cmask);
+        cmask &= cmask - 1u;
+        if (slot < (unsigned int)kHistWords) clist[slot] = (unsigned int)(base + kSeg * (b >> 2) + 4 * lane + (b & 3));
+        slot++;
       }
     }
   }
@@ -388,6 +397,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   }
   unsigned int e_run = eq_before;  // keys equal to tau before this point, in row order
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);  // selected before this point
+  // The selection is staged in the (now free) histogram area and copied out by the whole workgroup
+  // afterwards: k contiguous, coalesced stores instead of scattered per-lane ones.
+  unsigned int* stage = hist;  // [k] row offsets, then (candidate output) [k] keys
+  const bool staged = (DST == kDstIdx ? k : 2 * k) < kHistWords;  // the last word is the dummy slot
   for (int base = s0; base < s1; base += kSeg * kLdsUnroll) {
     u32x4 kk[kLdsUnroll];
     load_keys(rowk, base, s1, lane, kk);
@@ -420,7 +433,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
       unsigned int op = p_run + s_before;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        if ((sel_mask & (1u << e)) && op < (unsigned int)k) {
+        if (staged) {  // no branch: unselected lanes write the last word of the area
+          const bool sel = (sel_mask & (1u << e)) && op < (unsigned int)k;
+          stage[sel ? op : kHistWords - 1] = (unsigned int)(i + e);
+          if (DST == kDstCand) stage[sel ? k + op : kHistWords - 1] = kk[u][e];
+        } else if ((sel_mask & (1u << e)) && op < (unsigned int)k) {
           if (DST == kDstIdx) {
             out_idx[op] = SRC == kSrcScores ? lo + i + e : cprow[i + e];
           } else {
@@ -431,6 +448,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
         op += (sel_mask >> e) & 1u;
       }
       p_run += s_total;
+    }
+  }
+  if (staged) {  // exactly k entries were staged (m > k)
+    __syncthreads();
+    for (int j = tid; j < k; j += kTkThreads) {
+      const unsigned int r = stage[j];
+      const int pos = SRC == kSrcScores ? lo + (int)r : cprow[r];
+      if (DST == kDstIdx) {
+        out_idx[j] = pos;
+      } else {
+        out_key[j] = stage[k + j];
+        out_pos[j] = pos;
+      }
     }
   }
 }
