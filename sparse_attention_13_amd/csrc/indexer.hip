@@ -122,11 +122,11 @@ __device__ __forceinline__ void load_key_group(const uint8_t* __restrict__ kb, c
 // canonicalises its input first.)
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Scores of one key group for the wave's QW queries; lane l stores key g0 + l.
+// Scores of one key group for the wave's QW queries: afterwards lane l holds in out[qi] the score of
+// key g0 + l for query qi.
 template <int QW>
-__device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&qa)[QW][4],
-                                                const float (&ww)[QW][4][4], int g0, int s_end, int pos0,
-                                                int nq_here, int lane, float* __restrict__ srow, int64_t ld) {
+__device__ __forceinline__ void key_group_scores(const KeyGroup& g, const v8i (&qa)[QW][4],
+                                                 const float (&ww)[QW][4][4], float (&out)[QW]) {
   // part[qi][j]: this lane's share (its 16 heads) of the score of key 16j + l%16
   float part[QW][4];
 #pragma unroll
@@ -149,7 +149,6 @@ __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&q
   // Reduce-scatter over the four 16-lane rows: afterwards lane l holds the full score of key 16(l/16)
   // + l%16 = l.  Step 1 (lanes l, l^32): the lower half keeps blocks 0 and 1, the upper half 2 and 3;
   // step 2 (lanes l, l^16): rows keep block row.  Each swap-and-add is one permlane swap and one add.
-  float out[QW];
 #pragma unroll
   for (int qi = 0; qi < QW; qi++) {
     // permlane32_swap(a, b) trades the upper 32 lanes of a with the lower 32 lanes of b, so the lower
@@ -162,16 +161,30 @@ __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&q
     const float ra = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // block 0 (lower) / 2 (upper)
     const float rb = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // block 1 (lower) / 3 (upper)
     const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(ra), __float_as_uint(rb), false, false);
-    out[qi] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    out[qi] = (__uint_as_float(s[0]) + __uint_as_float(s[1])) * g.ksc + 0.0f;  // + 0 maps -0 to +0
   }
-  // lane l now holds the score of key g0 + l for every query of the wave
+}
+
+// Scores of one key group, stored straight to the score rows: lane l stores key g0 + l.
+template <int QW>
+__device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&qa)[QW][4],
+                                                const float (&ww)[QW][4][4], int g0, int s_end, int pos0,
+                                                int nq_here, int lane, float* __restrict__ srow, int64_t ld) {
+  float out[QW];
+  key_group_scores<QW>(g, qa, ww, out);
   const int s = g0 + lane;
   if (s < s_end) {
 #pragma unroll
     for (int qi = 0; qi < QW; qi++)
-      if (qi < nq_here && s <= pos0 + qi) srow[(size_t)qi * ld + s] = out[qi] * g.ksc + 0.0f;
+      if (qi < nq_here && s <= pos0 + qi) srow[(size_t)qi * ld + s] = out[qi];
   }
 }
+
+// One query per wave (decode) stages its scores in LDS and writes them out after its last key load.
+// Stores count in the same counter as loads and their acknowledgements come back slowly under a full
+// read stream, so a store issued per group holds every later wait for the next group's keys: the
+// stream then loses its lead and the scoring work stops overlapping it.
+constexpr int kStageKeys = 4096;  // keys per wave, at most, when scores are staged (16 KB of LDS)
 
 template <int QW, int NB>
 __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __restrict__ q8,
@@ -196,6 +209,9 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   const int s_begin = kc * chunk_keys;
   if (s_begin > pos_last) return;
   const int s_end = min(pos_last + 1, s_begin + chunk_keys);
+  constexpr bool kStaged = QW == 1;  // chunk_keys <= kStageKeys then (checked by the launch)
+  __shared__ float stage_all[kStaged ? 4 * kStageKeys : 1];
+  float* stage = stage_all + (kStaged ? (threadIdx.x >> 6) * kStageKeys : 0);
 
   const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
   const float* ksb = k_scale + (size_t)b * n_kv;
@@ -229,12 +245,26 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   // exactly the group it needs.
   KeyGroup ring[NB];
 #pragma unroll
-  for (int p = 0; p < NB - 1; p++) load_key_group<QW == 1>(kb, ksb, s_begin + 64 * p, n_kv, lane, ring[p]);
+  for (int p = 0; p < NB - 1; p++) {
+    load_key_group<QW == 1>(kb, ksb, s_begin + 64 * p, n_kv, lane, ring[p]);
+    // in issue order, each group's scale right after its keys: the wait for a group's scale then
+    // never covers the keys of the group after it
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // Ring of NB key groups: group i lives in slot i % NB.  The main loop runs whole rounds of NB groups
   // with no early exit (every slot index static, every wait exact); loads for group i + NB - 1 are
   // issued before group i is scored.  The last n_groups % NB groups are already in slots 0.. and are
   // scored after the loop.
+  auto score = [&](const KeyGroup& g, int g0) {
+    if constexpr (kStaged) {
+      float out[1];
+      key_group_scores<1>(g, qa, ww, out);
+      stage[g0 - s_begin + lane] = out[0];  // < chunk_keys: groups start inside the chunk
+    } else {
+      score_key_group<QW>(g, qa, ww, g0, s_end, pos0, nq_here, lane, srow, ld);
+    }
+  };
   const int n_groups = (s_end - s_begin + 63) / 64;
   int gi = 0;
   for (; gi + NB <= n_groups; gi += NB) {
@@ -242,13 +272,33 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
     for (int p = 0; p < NB; p++) {
       const int g0 = s_begin + 64 * (gi + p);
       load_key_group<QW == 1>(kb, ksb, g0 + 64 * (NB - 1), n_kv, lane, ring[(p + NB - 1) % NB]);
-      score_key_group<QW>(ring[p], qa, ww, g0, s_end, pos0, nq_here, lane, srow, ld);
+      score(ring[p], g0);
+      __builtin_amdgcn_sched_barrier(0);  // one group at a time: no loads hoisted across groups
     }
   }
 #pragma unroll
   for (int p = 0; p < NB - 1; p++)
-    if (gi + p < n_groups) score_key_group<QW>(ring[p], qa, ww, s_begin + 64 * (gi + p), s_end, pos0, nq_here, lane,
-                                               srow, ld);
+    if (gi + p < n_groups) score(ring[p], s_begin + 64 * (gi + p));
+
+  if constexpr (kStaged) {
+    // each wave reads back only what it wrote; the fences keep the LDS reads after the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n = s_end - s_begin;
+    float* dst = srow + s_begin;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      for (int i = 4 * lane; i < n; i += 256) {
+        if (i + 4 <= n) {
+          *(v4f*)(dst + i) = *(const v4f*)(stage + i);
+        } else {
+          for (int e = i; e < n; e++) dst[e] = stage[e];
+        }
+      }
+    } else {
+      for (int i = lane; i < n; i += 64) dst[i] = stage[i];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -378,12 +428,14 @@ hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint
     const int n_qgroups = n_q;
     int chunk = keys_per_wave;
     if (chunk <= 0) {
-      // enough waves to stream the keys from every CU: aim for >= 4096 waves in total
-      long long waves_per_row = (4096 + (long long)B * n_q - 1) / ((long long)B * n_q);
+      // one round of waves that streams from every CU: 2048 waves, 8 per CU (two workgroups at this
+      // kernel's register count)
+      long long waves_per_row = (2048 + (long long)B * n_q - 1) / ((long long)B * n_q);
       chunk = (int)((n_kv + waves_per_row - 1) / waves_per_row);
       chunk = chunk < 512 ? 512 : chunk;
     }
     chunk = ((chunk + 63) / 64) * 64;
+    chunk = chunk < kStageKeys ? chunk : kStageKeys;  // the staged scores of one wave fit its LDS slice
     const int n_chunks = (n_kv + chunk - 1) / chunk;
     const long long items = (long long)B * n_qgroups * n_chunks;
     if (items > (1LL << 30)) return hipErrorInvalidValue;

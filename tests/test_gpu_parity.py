@@ -93,6 +93,30 @@ def test_indexer_fp8_vs_oracle(orc, dsa, B, L, n_q, needles):
             assert np.all(np.isnan(g[b, r, p + 1:]))
 
 
+@pytest.mark.parametrize("pad_ld", [False, True])
+def test_indexer_fp8_decode_many_sequences(orc, dsa, pad_ld):
+    """One query per sequence for 512 sequences of 17000 keys: every wave scores a chunk of 4096 keys
+    (the largest one wave stages), the last chunk of each row is ragged (616 keys), and the scores
+    leave through the scalar path (row pitch 17001 floats) or the 16-byte path (pitch 17024)."""
+    B, S = 512, 17000
+    g = torch.Generator(device=DEV).manual_seed(23)
+    q8, qs = synth.quantize_e4m3_rows(torch.randn((B, 1, 64, 128), generator=g, device=DEV))
+    k8, ks = synth.quantize_e4m3_rows(torch.randn((B, S, 128), generator=g, device=DEV))
+    w = torch.randn((B, 1, 64), generator=g, device=DEV) / 8
+    ld = 17024 if pad_ld else S + 1
+    scores = torch.full((B, 1, ld), float("nan"), device=DEV)
+    dsa.indexer_scores(q8, qs, k8, ks, w, scores)
+    torch.cuda.synchronize()
+    pos = np.array([S - 1], np.int64)
+    for b in (0, 257, 511):
+        xb = {"q8": q8[b], "q_scale": qs[b], "k8": k8[b], "k_scale": ks[b]}
+        o, mag, absmag = orc.indexer(deq_q(xb), np32(w[b]), deq_k(xb), pos, ld=ld, with_mag=True)
+        gb = np32(scores[b])
+        e_mag, e_rel, n = parity.indexer_errors(gb, o, mag, absmag, pos)
+        assert e_mag <= 1.0, (b, e_mag, e_rel)
+        assert np.all(np.isnan(gb[0, S:])), "entries past the row's keys must stay untouched"
+
+
 def test_indexer_fp8_exact_integers(orc, dsa):
     """Integer-valued e4m3 inputs with power-of-two scales: every partial sum is an exact integer
     below 2^24 on both sides, so the scores must agree bit for bit whatever the summation order."""
