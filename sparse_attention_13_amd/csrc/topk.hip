@@ -596,8 +596,10 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
   int want = 1;
   if (n_kv > kKeyCap) want = (n_kv + kKeyCap - 1) / kKeyCap;
   if (rows < 256) {
-    // too few rows to fill the GPU: split each into chunks of at least 4k keys
-    const long long more = std::min<long long>((512 + rows - 1) / rows, n_kv / (4LL * k));
+    // too few rows to fill the GPU: split each into chunks of at least 4k keys, aiming at one
+    // workgroup per CU (a large chunk's row cache leaves room for only one), so that all chunks run
+    // in a single round
+    const long long more = std::min<long long>((256 + rows - 1) / rows, n_kv / (4LL * k));
     if (more > want) want = (int)more;
   }
   if (want <= 1) return p;
