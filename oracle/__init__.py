@@ -57,6 +57,7 @@ def _load():
         lib.oracle_indexer.argtypes = [P, P, P, I64, P, I, I, P, I64, P, P]
         lib.oracle_topk.argtypes = [P, I64, I64, P, I, P, P]
         lib.oracle_sparse_attn.argtypes = [P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
+        lib.oracle_sparse_attn_mha.argtypes = [P, P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
         lib.oracle_threads.restype = I
         _lib = lib
     return _lib
@@ -157,6 +158,28 @@ def sparse_attn(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, d_v: int, sm_sca
     lse = np.empty((R, H), np.float64)
     _load().oracle_sparse_attn(_p(q), _p(kv), _p(idx), R, H, d_qk, d_v, k, float(sm_scale),
                                _p(out), _p(lse))
+    return out, lse
+
+
+def sparse_attn_mha(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, sm_scale: float):
+    """Masked MHA mode: attention over the selected entries with per-head key and value rows (all in
+    double).  Masking every unselected key out of a dense softmax leaves exactly this sum.
+
+    q [R, H, d_qk], k [S, H, d_qk], v [S, H, d_v] float32, idx [R, k_sel] int32 (-1 skipped).
+    Returns (out [R, H, d_v] float64, lse [R, H] float64)."""
+    q = _c(q, np.float32)
+    k = _c(k, np.float32)
+    v = _c(v, np.float32)
+    idx = _c(idx, np.int32)
+    R, H, d_qk = q.shape
+    S, d_v = k.shape[0], v.shape[2]
+    k_sel = idx.shape[1]
+    assert idx.shape[0] == R and k.shape[1:] == (H, d_qk) and v.shape[:2] == (S, H)
+    assert idx.size == 0 or idx.max() < S
+    out = np.empty((R, H, d_v), np.float64)
+    lse = np.empty((R, H), np.float64)
+    _load().oracle_sparse_attn_mha(_p(q), _p(k), _p(v), _p(idx), R, H, d_qk, d_v, k_sel, float(sm_scale),
+                                   _p(out), _p(lse))
     return out, lse
 
 

@@ -224,3 +224,51 @@ void oracle_sparse_attn(const float* q, const float* kv, const int32_t* idx, int
     }
   }
 }
+
+/* Masked MHA mode (velog summary, section 3.3 Inference Cost; notes.yuuk.io, section on inference
+ * cost): short prefills run attention in MHA form, each head with its own key and value rows, and
+ * simulate DSA by masking every key outside the query's top-k selection.  Masking the other keys out
+ * of the softmax leaves exactly the attention over the selected entries, so this is the same
+ * definition as oracle_sparse_attn with per-head rows:
+ *   z_s   = sm_scale * sum_e q[r][h][e] * k[s][h][e]            for s in idx[r] (entries -1 skipped)
+ *   out   = sum_s softmax(z)_s * v[s][h][0:d_v],  lse = log sum_s exp(z_s)
+ *   q [n_rows][H][d_qk], k [n_kv][H][d_qk], v [n_kv][H][d_v], idx [n_rows][k_sel],
+ *   out [n_rows][H][d_v], lse [n_rows][H].  All in double.
+ */
+void oracle_sparse_attn_mha(const float* q, const float* kk, const float* v, const int32_t* idx, int64_t n_rows,
+                            int H, int d_qk, int d_v, int k_sel, double sm_scale, double* out, double* lse) {
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int64_t r = 0; r < n_rows; r++) {
+    for (int h = 0; h < H; h++) {
+      const float* qh = q + (r * H + h) * (int64_t)d_qk;
+      const int32_t* sel = idx + r * (int64_t)k_sel;
+      double* o = out + (r * H + h) * (int64_t)d_v;
+      double* z = (double*)malloc((size_t)k_sel * sizeof(double));
+      double m = -INFINITY;
+      for (int i = 0; i < k_sel; i++) {
+        if (sel[i] < 0) continue;
+        const float* ks = kk + ((int64_t)sel[i] * H + h) * d_qk;
+        double dot = 0.0;
+        for (int e = 0; e < d_qk; e++) dot += (double)qh[e] * (double)ks[e];
+        z[i] = sm_scale * dot;
+        if (z[i] > m) m = z[i];
+      }
+      for (int e = 0; e < d_v; e++) o[e] = 0.0;
+      double l = 0.0;
+      for (int i = 0; i < k_sel; i++) {
+        if (sel[i] < 0) continue;
+        const float* vs = v + ((int64_t)sel[i] * H + h) * d_v;
+        const double p = exp(z[i] - m);
+        l += p;
+        for (int e = 0; e < d_v; e++) o[e] += p * (double)vs[e];
+      }
+      if (l > 0.0) {
+        for (int e = 0; e < d_v; e++) o[e] /= l;
+        lse[r * H + h] = m + log(l);
+      } else {
+        lse[r * H + h] = -INFINITY;
+      }
+      free(z);
+    }
+  }
+}

@@ -295,6 +295,82 @@ def test_attention_permutation_invariant(orc):
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
 
 
+# ------------------------------------------------------------------ masked MHA mode
+
+def _mla_pair(rng, L, H, d_c, d_r, d_h, d_hv):
+    """MLA inputs in both forms, from one latent cache (velog summary, section 1.3): the MHA form
+    decompresses keys and values per head (k_h = [W_UK,h c ; k_rope], v_h = W_UV,h c), the MQA form
+    absorbs W_UK into the query (q' = [W_UK,h^T q_nope ; q_rope]) and attends the latent rows
+    [c ; k_rope] directly."""
+    c = rng.standard_normal((L, d_c))
+    k_rope = rng.standard_normal((L, d_r))
+    w_uk = rng.standard_normal((H, d_h, d_c)) / math.sqrt(d_c)
+    w_uv = rng.standard_normal((H, d_hv, d_c)) / math.sqrt(d_c)
+    q_nope = rng.standard_normal((L, H, d_h))
+    q_rope = rng.standard_normal((L, H, d_r))
+    k_mha = np.concatenate([np.einsum("hdc,sc->shd", w_uk, c), np.broadcast_to(k_rope[:, None], (L, H, d_r))], -1)
+    v_mha = np.einsum("hdc,sc->shd", w_uv, c)
+    q_mha = np.concatenate([q_nope, q_rope], -1)
+    q_mqa = np.concatenate([np.einsum("hdc,thd->thc", w_uk, q_nope), q_rope], -1)
+    kv_mqa = np.concatenate([c, k_rope], -1)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return f32(q_mha), f32(k_mha), f32(v_mha), f32(q_mqa), f32(kv_mqa), w_uv
+
+
+def test_mha_mode_equals_absorbed_mqa_mode(orc):
+    """The MHA form over the selection equals W_UV applied to the (separately pinned) MQA form: the
+    logits agree because q_h . W_UK,h c = (W_UK,h^T q_h) . c, and the outputs because W_UV,h is linear.
+    Equal up to the float32 rounding of the two input sets."""
+    rng = np.random.default_rng(40)
+    L, H, d_c, d_r, d_h, d_hv, k = 50, 4, 32, 8, 12, 10, 17
+    q_mha, k_mha, v_mha, q_mqa, kv_mqa, w_uv = _mla_pair(rng, L, H, d_c, d_r, d_h, d_hv)
+    scores = rng.standard_normal((L, L)).astype(np.float32)
+    idx, _ = orc.topk(scores, np.arange(L, dtype=np.int64), k)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    out, lse = orc.sparse_attn_mha(q_mha, k_mha, v_mha, idx, scale)
+    out_c, lse_c = orc.sparse_attn(q_mqa, kv_mqa, idx, d_c, scale)
+    np.testing.assert_allclose(out, np.einsum("hvc,thc->thv", w_uv, out_c), rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(lse, lse_c, rtol=1e-5, atol=1e-5)
+
+
+def test_mha_mode_dense_equals_sdpa(orc):
+    """Selection of every s <= t: the masked MHA mode is dense causal attention (torch SDPA, CPU)."""
+    rng = np.random.default_rng(41)
+    L, H, dqk, dv = 29, 3, 20, 12
+    q = rng.standard_normal((L, H, dqk)).astype(np.float32)
+    k = rng.standard_normal((L, H, dqk)).astype(np.float32)
+    v = rng.standard_normal((L, H, dv)).astype(np.float32)
+    idx, _ = orc.topk(np.zeros((L, L), np.float32), np.arange(L, dtype=np.int64), L + 5)
+    scale = 1.0 / math.sqrt(dqk)
+    out, lse = orc.sparse_attn_mha(q, k, v, idx, scale)
+    Q, K, V = (torch.from_numpy(a).double().permute(1, 0, 2) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    logits = (Q @ K.transpose(1, 2)) * scale
+    mask = torch.triu(torch.ones(L, L, dtype=torch.bool), 1)
+    ref_lse = torch.logsumexp(logits.masked_fill(mask, -math.inf), dim=-1).T.numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_mha_mode_single_entry_and_padding(orc):
+    """One selected entry gives that entry's value row of the same head exactly; -1 entries and their
+    order do not matter."""
+    rng = np.random.default_rng(42)
+    S, H, dqk, dv = 16, 3, 8, 5
+    q = rng.standard_normal((2, H, dqk)).astype(np.float32)
+    k = rng.standard_normal((S, H, dqk)).astype(np.float32)
+    v = rng.standard_normal((S, H, dv)).astype(np.float32)
+    idx = np.array([[-1, 9, -1, -1], [2, 14, 6, -1]], np.int32)
+    out, lse = orc.sparse_attn_mha(q, k, v, idx, 0.4)
+    for h in range(H):
+        assert np.array_equal(out[0, h], v[9, h].astype(np.float64))
+        assert abs(lse[0, h] - 0.4 * float(np.dot(q[0, h].astype(np.float64), k[9, h].astype(np.float64)))) < 1e-12
+    idx2 = np.array([[9, -1, -1, -1], [-1, 6, 2, 14]], np.int32)
+    out2, lse2 = orc.sparse_attn_mha(q, k, v, idx2, 0.4)
+    np.testing.assert_allclose(out2, out, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
+
+
 # ------------------------------------------------------------------ composition
 
 def test_forward_tiny_config_is_self_consistent(orc):
