@@ -78,9 +78,10 @@ def test_topk_workspace(L):
     assert L.dsa_topk_workspace_size(1, 32768, 32768, 2048) == 0
     assert L.dsa_topk_workspace_size(1, 10, 10, 2048) == 0  # every row keeps all keys
     assert L.dsa_topk_workspace_size(1, 10, 5, 4) == 0      # invalid: n_q > n_kv
-    # few long rows: two stages, candidates (key + position) of every chunk
+    # few long rows: two stages, candidates (key + position) of every chunk; 64 rows of 131072 keys
+    # split into 4 chunks each (256 chunk workgroups, one round on 256 CUs)
     ws = L.dsa_topk_workspace_size(64, 1, 131072, 2048)
-    assert ws >= 64 * 131072 // 16384 * 2048 * 8
+    assert ws == 2 * 64 * 4 * 2048 * 4
     big = ctypes.c_void_p(0x40000)
     assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, None, 0, None) == DSA_ERR_WORKSPACE
     assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, big, ws - 1, None) == DSA_ERR_WORKSPACE
