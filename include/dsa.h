@@ -131,6 +131,35 @@ size_t dsa_sparse_mla_attn_workspace_size(int B, int n_q, int n_kv, int H, int d
                                           dsa_dtype_t dtype);
 
 /* ------------------------------------------------------------------------------------------------
+ * dsa_masked_mha_attn -- masked MHA mode for short prefills (velog summary, section 3.3 Inference
+ * Cost; notes.yuuk.io, section on inference cost): attention in MHA form, each head with its own
+ * key and value rows, computed densely over the causal keys with every key outside the query's
+ * top-k selection masked out of the softmax.  For every query t (pos_t = n_kv - n_q + t) and head h:
+ *
+ *   z_s   = sm_scale * q[b][t][h][:] . k[b][s][h][:]     over S_t = { s = idx[b][t][i] : 0 <= s <= pos_t }
+ *   out   = sum_{s in S_t} softmax(z)_s * v[b][s][h][:]
+ *   lse   = log sum_{s in S_t} exp(z_s)                  (natural log)
+ *
+ * which is the attention over the selected entries (entries -1, duplicates-free as dsa_topk writes
+ * them; entries outside [0, pos_t] are ignored).  A row with no such entry gets out = 0, lse = -inf.
+ * q [B][n_q][H][d_qk], k [B][n_kv][H][d_qk], v [B][n_kv][H][d_v] (token-major, as an up-projection
+ * of the latent rows writes them), idx [B][n_q][k_sel] int32, out [B][n_q][H][d_v],
+ * lse [B][n_q][H] fp32 or NULL.
+ * dtype = DSA_BF16 only, with d_qk = 192 and d_v = 128 (CDNA4 bf16 matrix cores, fp32 accumulation),
+ *   any H; n_kv <= 524288.  q, k, v, out 16-byte aligned.  Other shapes: DSA_ERR_UNSUPPORTED.
+ * workspace: device memory of at least dsa_masked_mha_workspace_size(B, n_q, n_kv) bytes, 256-byte
+ *   aligned; it receives the selection as one bit per (query, key) (scratch).  Too small,
+ *   misaligned or missing: DSA_ERR_WORKSPACE, nothing enqueued.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_masked_mha_attn(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                                 int n_q, int n_kv, int H, int d_qk, int d_v, int k_sel, float sm_scale,
+                                 dsa_dtype_t dtype, void* out, float* lse, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_masked_mha_attn needs (0 for invalid sizes). */
+size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv);
+
+/* ------------------------------------------------------------------------------------------------
  * dsa_forward_prefill -- the whole path for B sequences of n_kv tokens whose last n_q tokens are
  * queries: dsa_indexer_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.  Chunked prefill
  * is one call per chunk with n_kv growing by the chunk length (all state is in the caller's caches).

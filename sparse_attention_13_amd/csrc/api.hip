@@ -12,6 +12,9 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// masked MHA mode: one workgroup's LDS holds a query row's mask words (2 per 64 keys, 64 KiB)
+constexpr int kMhaMaxKeys = 1 << 19;
+
 dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -266,6 +269,37 @@ dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* i
   st = check_attn_ptrs(q, kv, idx, out, sm_scale, p, workspace, ws_bytes);
   if (st != DSA_OK) return st;
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, p, workspace, (hipStream_t)stream);
+}
+
+size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv || n_kv > kMhaMaxKeys) return 0;
+  return align_up((size_t)B * n_q * dsa::mha_mask_words(n_kv) * 4, 256);
+}
+
+dsa_status_t dsa_masked_mha_attn(const void* q, const void* k, const void* v, const int32_t* idx, int B, int n_q,
+                                 int n_kv, int H, int d_qk, int d_v, int k_sel, float sm_scale, dsa_dtype_t dtype,
+                                 void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || H < 1 || k_sel < 1)
+    return fail(DSA_ERR_INVALID_ARG, "masked_mha: sizes must be positive");
+  if (n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "masked_mha: n_q=%d exceeds n_kv=%d", n_q, n_kv);
+  if (dtype != DSA_BF16 || d_qk != 192 || d_v != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "masked_mha: supports bf16 with d_qk=192, d_v=128 (got dtype %d, %d, %d)",
+                (int)dtype, d_qk, d_v);
+  if (n_kv > kMhaMaxKeys) return fail(DSA_ERR_UNSUPPORTED, "masked_mha: n_kv=%d exceeds %d", n_kv, kMhaMaxKeys);
+  if (B > 65535 || (long long)((n_q + 127) / 128) * H > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "masked_mha: grid too large");
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "masked_mha: null q, k, v, idx or out");
+  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "masked_mha: sm_scale must be finite");
+  if (!(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(out, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "masked_mha: q, k, v and out must be 16-byte aligned");
+  const size_t need = dsa_masked_mha_workspace_size(B, n_q, n_kv);
+  if (!workspace) return fail(DSA_ERR_WORKSPACE, "masked_mha: workspace of %zu bytes required", need);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_WORKSPACE, "masked_mha: workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "masked_mha: workspace %zu < %zu bytes", ws_bytes, need);
+  const hipError_t e = dsa::launch_masked_mha((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, B, n_q,
+                                              n_kv, H, k_sel, sm_scale, (uint16_t*)out, lse, (uint32_t*)workspace,
+                                              (hipStream_t)stream);
+  return hip_status(e, "dsa_masked_mha_attn");
 }
 
 size_t dsa_forward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,

@@ -92,6 +92,12 @@ hipError_t launch_attn_generic(const float* q, const float* kv, const int32_t* i
 // bf16 matrix-core sparse MLA, H = 128, d_qk = 576, d_v = 512.  n_split > 1 splits each query's
 // selection into n_split contiguous parts whose partial results go to `partial` (fp32) and are
 // merged by a second kernel.
+// Masked MHA mode (bf16, d_qk = 192, d_v = 128): mask words per query row, and the two launches
+// (mask from the selection, then dense attention under it).  mask: [B][n_q][mha_mask_words(n_kv)] u32.
+int mha_mask_words(int n_kv);
+hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int B,
+                             int n_q, int n_kv, int H, int k_sel, float sm_scale, uint16_t* out, float* lse,
+                             uint32_t* mask, hipStream_t stream);
 size_t mla_bf16_workspace_bytes(int B, int n_q, int n_split);
 int mla_bf16_pick_split(int B, int n_q, int k);
 hipError_t launch_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int n_q, int n_kv,

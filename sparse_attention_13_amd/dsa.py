@@ -37,6 +37,8 @@ SIGNATURES = {
     "dsa_forward_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P, _P,
                             _P, _SZ, _P], _I),
     "dsa_forward_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "dsa_masked_mha_attn": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
+    "dsa_masked_mha_workspace_size": ([_I, _I, _I], _SZ),
 }
 
 _lib = None
@@ -157,6 +159,32 @@ def sparse_mla_attn(q, kv, idx, d_v: int, sm_scale: float, out=None, lse=None, w
     wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().dsa_sparse_mla_attn(_ptr(q), _ptr(kv), _ptr(idx), B, nq, n_kv, H, d_qk, d_v, k, float(sm_scale), dt,
                                      _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
+    return out, lse
+
+
+def masked_mha_workspace_size(B: int, n_q: int, n_kv: int) -> int:
+    return int(lib().dsa_masked_mha_workspace_size(B, n_q, n_kv))
+
+
+def masked_mha_attn(q, k, v, idx, sm_scale: float, out=None, lse=None, workspace=None, stream=None):
+    """Masked MHA mode: dense attention with per-head rows under the top-k mask.  q [B, n_q, H, d_qk],
+    k [B, n_kv, H, d_qk], v [B, n_kv, H, d_v] (bf16), idx [B, n_q, k_sel] int32 -> out [B, n_q, H, d_v]
+    bf16, lse [B, n_q, H] f32.  workspace: uint8 device tensor (allocated when missing)."""
+    _dev(q, k, v, idx, out, lse, workspace)
+    B, nq, H, d_qk = q.shape
+    n_kv, d_v = k.shape[1], v.shape[-1]
+    k_sel = idx.shape[-1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, nq, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, nq, H), dtype=torch.float32, device=q.device)
+    ws = masked_mha_workspace_size(B, nq, n_kv)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    _check(lib().dsa_masked_mha_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, nq, n_kv, H, d_qk, d_v, k_sel,
+                                     float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
     return out, lse
 
 

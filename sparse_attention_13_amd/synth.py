@@ -117,6 +117,20 @@ def prefill(L: int, seed: int = 0, device="cpu", n_needles: int = 0, needle_layo
     return out
 
 
+def mha_heads(L: int, seed: int = 0, device="cpu", n_q: int | None = None, H: int = 128, d_qk: int = 192,
+              d_v: int = 128) -> dict:
+    """MHA-form attention inputs of one sequence (masked MHA mode): per-head queries of the last n_q
+    tokens and per-head key and value rows of all L tokens, bf16 ~ N(0, 1), token-major.
+    Draw order: q, k, v (a generator of its own, seed + 1000003, so the indexer inputs of the same
+    seed stay as prefill() draws them)."""
+    n_q = L if n_q is None else n_q
+    g = _gen(seed + 1000003, device)
+    return dict(kind="mha", L=L, n_q=n_q, H=H, d_qk=d_qk, d_v=d_v, sm_scale=1.0 / math.sqrt(d_qk),
+                q=_randn((n_q, H, d_qk), g, device, torch.bfloat16, chunk_rows=1024),
+                k=_randn((L, H, d_qk), g, device, torch.bfloat16, chunk_rows=1024),
+                v=_randn((L, H, d_v), g, device, torch.bfloat16, chunk_rows=1024))
+
+
 def decode(B: int, S: int, seed: int = 0, device="cpu", H_I: int = 64, d_I: int = 128, H: int = 128,
            d_qk: int = 576, d_v: int = 512, k: int = 2048) -> dict:
     """B sequences, one new query each at position S-1 over S cached tokens (per-sequence seed

@@ -37,7 +37,7 @@ def test_header_declares_the_path():
     for n in ["dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_attn", "dsa_forward_prefill",
               "dsa_forward_decode",
               "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
-              "dsa_last_error", "dsa_version"]:
+              "dsa_last_error", "dsa_version", "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size"]:
         assert n in names
 
 
@@ -140,6 +140,38 @@ def test_attention_validation_and_workspace(L):
     bad = [ctypes.c_void_p(0x10002), FAKE, FAKE, 1, 1, 10, 128, 576, 512, 8, 0.1, DSA_BF16, FAKE2, None, None, 0,
            None]
     assert f(*bad) == DSA_ERR_INVALID_ARG  # misaligned q on the bf16 path
+
+
+def test_masked_mha_validation_and_workspace(L):
+    from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE,
+                                             DSA_F32)
+    f = L.dsa_masked_mha_attn
+    # one bit per (query, key), two 32-bit words per 64 keys, rounded up to 256 bytes
+    assert L.dsa_masked_mha_workspace_size(1, 8192, 8192) == 8192 * 256 * 4
+    assert L.dsa_masked_mha_workspace_size(2, 3, 100) == 256
+    assert L.dsa_masked_mha_workspace_size(1, 11, 10) == 0          # n_q > n_kv
+    assert L.dsa_masked_mha_workspace_size(1, 1, (1 << 19) + 1) == 0  # beyond the mask row capacity
+    ws = L.dsa_masked_mha_workspace_size(1, 100, 1000)
+    ok = [FAKE, FAKE, FAKE, FAKE, 1, 100, 1000, 16, 192, 128, 64, 0.07, DSA_BF16, FAKE2, None, None, 0, None]
+    assert f(*ok) == DSA_ERR_WORKSPACE                               # missing
+    a = list(ok); a[15], a[16] = ctypes.c_void_p(0x30000 + 64), ws
+    assert f(*a) == DSA_ERR_WORKSPACE                                # misaligned
+    a = list(ok); a[15], a[16] = ctypes.c_void_p(0x30000), ws - 1
+    assert f(*a) == DSA_ERR_WORKSPACE                                # too small
+    a = list(ok); a[8] = 128
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # d_qk other than 192
+    a = list(ok); a[12] = DSA_F32
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # bf16 only
+    a = list(ok); a[5] = 1001
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # n_q > n_kv
+    a = list(ok); a[3] = None
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # null idx
+    a = list(ok); a[11] = float("inf")
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # non-finite scale
+    a = list(ok); a[1] = ctypes.c_void_p(0x10008)
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned k
+    a = list(ok); a[10] = 0
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # k_sel = 0
 
 
 def test_forward_validation(L):

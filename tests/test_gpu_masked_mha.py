@@ -1,0 +1,117 @@
+"""Masked MHA mode (dense attention with per-head rows under the top-k mask) vs the CPU oracle, through
+the C ABI, on the GPU.  Small cases compare every element; the 8K prefill runs in the benchmark's launch
+configuration and is compared on sampled rows.  Tolerances: tests/parity.py (attention rules).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from sparse_attention_13_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_13_amd import dsa as d
+    d.lib()
+    return d
+
+
+def f32(orc, t):
+    return orc.bf16_to_f32(synth.bf16_bits(t))
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def check_rows(orc, q, k, v, idx, out, lse, rows, sm_scale, what):
+    """Oracle on the given query rows of one sequence; q/out/lse/idx indexed by query row."""
+    kf, vf = f32(orc, k), f32(orc, v)
+    tr = torch.as_tensor(rows, dtype=torch.long, device=q.device)
+    o_out, o_lse = orc.sparse_attn_mha(f32(orc, q[tr]), kf, vf, idx[rows], sm_scale)
+    ratio, mx, lse_err = parity.attention_errors(np32(out[tr]), o_out, np32(lse[tr]), o_lse)
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (what, ratio, mx, lse_err)
+
+
+def causal_clean(idx, pos):
+    """The selection the kernel attends: entries in [0, pos_t], the rest as -1."""
+    out = idx.copy()
+    for r, p in enumerate(pos):
+        bad = (out[r] < 0) | (out[r] > p)
+        out[r][bad] = -1
+    return out
+
+
+# B, L, n_q, H, k_sel: several tiles with a ragged tail, k_sel >= L (the mask keeps every causal key:
+# dense causal attention), one query per sequence, exactly one key tile, rows both above and below k
+@pytest.mark.parametrize("B,L,n_q,H,k_sel", [(2, 300, 300, 4, 64), (1, 1000, 77, 3, 2048), (1, 517, 200, 2, 100),
+                                             (3, 130, 1, 5, 16), (1, 64, 64, 1, 8), (1, 2100, 300, 2, 2048)])
+def test_masked_mha_vs_oracle(orc, dsa, B, L, n_q, H, k_sel):
+    rng = np.random.default_rng(L * 7 + n_q)
+    xs = [synth.mha_heads(L, seed=b, device=DEV, n_q=n_q, H=H) for b in range(B)]
+    q = torch.stack([x["q"] for x in xs]).contiguous()
+    k = torch.stack([x["k"] for x in xs]).contiguous()
+    v = torch.stack([x["v"] for x in xs]).contiguous()
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    idx = np.stack([orc.topk(rng.standard_normal((n_q, L)).astype(np.float32), pos, k_sel)[0] for _ in range(B)])
+    sm_scale = 1.0 / math.sqrt(192)
+    out, lse = dsa.masked_mha_attn(q, k, v, torch.from_numpy(idx).to(DEV), sm_scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        check_rows(orc, q[b], k[b], v[b], idx[b], out[b], lse[b], np.arange(n_q), sm_scale, (b,))
+
+
+def test_masked_mha_ignored_entries_and_empty_rows(orc, dsa):
+    """Entries -1, past the query's position or past the keys are ignored; a row left with none gets
+    out = 0 and lse = -inf; the order of the entries does not matter."""
+    L, n_q, H, k_sel = 400, 150, 3, 40
+    x = synth.mha_heads(L, seed=5, device=DEV, n_q=n_q, H=H)
+    rng = np.random.default_rng(9)
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    idx = np.stack([rng.choice(L + 30, size=k_sel, replace=False) for _ in range(n_q)]).astype(np.int32)
+    idx[:, ::5] = -1
+    idx[7, :] = -1                       # nothing selected
+    idx[8, :] = L + 3                    # only entries past the keys
+    idx[9, :] = -1
+    idx[9, 0] = pos[9] + 1               # only an entry past the query's position
+    gi = torch.from_numpy(idx).to(DEV)[None]
+    sm_scale = 0.07
+    out, lse = dsa.masked_mha_attn(x["q"][None], x["k"][None], x["v"][None], gi, sm_scale)
+    torch.cuda.synchronize()
+    clean = causal_clean(idx, pos)
+    live = np.array([r for r in range(n_q) if (clean[r] >= 0).any()])
+    check_rows(orc, x["q"], x["k"], x["v"], clean, out[0], lse[0], live, sm_scale, "live rows")
+    for r in (7, 8, 9):
+        assert torch.count_nonzero(out[0, r]).item() == 0
+        assert torch.all(torch.isneginf(lse[0, r]))
+    out2, lse2 = dsa.masked_mha_attn(x["q"][None], x["k"][None], x["v"][None],
+                                     torch.from_numpy(idx[:, ::-1].copy()).to(DEV)[None], sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
+
+
+def test_masked_mha_full_8k(orc, dsa):
+    """Prefill of 8192 tokens, 128 heads, k = 2048 from the indexer and top-k of the same sequence, in the
+    benchmark's launch configuration; rows sampled across query tiles, including rows that keep every
+    causal key (t < 2048) and rows whose mask leaves a quarter of them."""
+    L, k_sel = 8192, 2048
+    x = synth.prefill(L, seed=0, device=DEV, n_needles=64, with_mla=False)
+    m = synth.mha_heads(L, seed=0, device=DEV)
+    scores = torch.empty((1, L, L), device=DEV)
+    dsa.indexer_scores(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None], scores)
+    idx = dsa.topk(scores, L, k_sel)
+    del scores
+    out, lse = dsa.masked_mha_attn(m["q"][None], m["k"][None], m["v"][None], idx, m["sm_scale"])
+    torch.cuda.synchronize()
+    gi = idx[0].cpu().numpy()
+    parity.assert_idx_wellformed(gi, np.arange(L, dtype=np.int64), k_sel)
+    rows = np.array([0, 1, 63, 127, 128, 2047, 2048, 2049, 4095, 5000, 8064, 8191])
+    check_rows(orc, m["q"], m["k"], m["v"], gi, out[0], lse[0], rows, m["sm_scale"], "8k")
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
