@@ -31,7 +31,8 @@ namespace {
 constexpr int kMD = 192;                    // d_qk of the fast path
 constexpr int kMV = 128;                    // d_v of the fast path
 constexpr int kMBK = 64;                    // keys per tile
-constexpr int kMBQ = 128;                   // queries per workgroup
+constexpr int kMhaQB = 1;  // 32-query blocks per wave (128 QB queries per workgroup); two blocks
+                           // would halve the LDS reads per flop but exceed the register file
 constexpr int kKTile = kMBK * kMD * 2;      // 24576 B
 constexpr int kVTile = kMBK * kMV * 2;      // 16384 B
 constexpr int kKCopies = kKTile / 1024 / 4;  // 6 copies of 1 KiB per wave
@@ -118,82 +119,109 @@ __device__ __forceinline__ void vt_frags(const char* vt, const int (&voff)[4], i
       : "v"(b0), "v"(b1), "v"(b2), "v"(b3));
 }
 
-// One key tile for this wave's 32 queries.
-__device__ __forceinline__ void compute_tile(const char* kt, const char* vt, const uint32_t (&mw)[2],
-                                             const v8bf (&qf)[kMD / 16], const int (&koff)[4], const int (&voff)[4],
-                                             v16f (&o)[4], MhaState& st, float c_scale, int lane) {
+// One key tile for this wave's QB x 32 queries (query block qb: queries 32qb + l%32 of the wave's).
+template <int QB>
+__device__ __forceinline__ void compute_tile(const char* kt, const char* vt, const uint32_t (&mw)[QB][2],
+                                             const v8bf (&qf)[QB][kMD / 16], const int (&koff)[4],
+                                             const int (&voff)[4], v16f (&o)[QB][4], MhaState (&st)[QB],
+                                             float c_scale, int lane) {
   // no selected key for any of this wave's queries in the tile: nothing to do
-  if (__ballot((mw[0] | mw[1]) != 0u) == 0ull) return;
+  uint32_t any_w = 0u;
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) any_w |= mw[qb][0] | mw[qb][1];
+  if (__ballot(any_w != 0u) == 0ull) return;
 
-  v16f sacc[2];
+  v16f sacc[QB][2];
 #pragma unroll
   for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
     for (int ks = 0; ks < kMD / 16; ks++) {
       const v8bf kf = *(const v8bf*)(kt + koff[ks & 3] + 128 * (ks >> 2) + kb * 32 * (kMD * 2));
-      if (ks == 0)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], (v16f){}, 0, 0, 0);
-      else
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++) {
+        if (ks == 0)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][0], (v16f){}, 0, 0, 0);
+        else
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sacc[qb][kb], 0, 0, 0);
+      }
+      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // at most 4 K fragments in flight
     }
   }
-  // mask, then the online softmax of this lane's query over the tile's 64 keys (32 here, 32 in lane
-  // l ^ 32).  Value r of block kb is key 32kb + 8(r/4) + 4(l/32) + r%4.
+  // mask, then the online softmax of this lane's queries over the tile's 64 keys (32 here, 32 in lane
+  // l ^ 32).  Value r of block kb is key 32kb + 8(r/4) + 4(l/32) + r%4.  Scores stay unscaled until
+  // the exponent (c_scale > 0 keeps the maximum).
   const int kk0 = 4 * (lane >> 5);
-  float bm = -INFINITY;
+  unsigned int pk[QB][2][8];
+  float alpha[QB];
+  bool rescale = false;
 #pragma unroll
-  for (int kb = 0; kb < 2; kb++)
+  for (int qb = 0; qb < QB; qb++) {
+    float bm = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int kk = 8 * (r >> 2) + kk0 + (r & 3);
-      sacc[kb][r] = ((mw[kb] >> kk) & 1u) ? sacc[kb][r] * c_scale : -INFINITY;
-      bm = fmaxf(bm, sacc[kb][r]);
+    for (int kb = 0; kb < 2; kb++) {
+      if (__ballot(mw[qb][kb] != 0xFFFFFFFFu) != 0ull) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int kk = 8 * (r >> 2) + kk0 + (r & 3);
+          sacc[qb][kb][r] = ((mw[qb][kb] >> kk) & 1u) ? sacc[qb][kb][r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) bm = fmaxf(bm, sacc[qb][kb][r]);
     }
-  bm = xor32_max(bm);
-  float alpha = 1.f;
-  if (bm > st.m + kRescaleM) {
-    alpha = __builtin_amdgcn_exp2f(st.m - bm);  // 0 while m = -inf
-    st.m = bm;
-  }
-  if (__ballot(alpha != 1.f) != 0ull) {
-#pragma unroll
-    for (int db = 0; db < 4; db++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) o[db][r] *= alpha;
-  }
-  const float neg_m = (st.m == -INFINITY) ? 0.f : -st.m;
-  float psum = 0.f;
-  unsigned int pk[2][8];
-#pragma unroll
-  for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-      const float p0 = __builtin_amdgcn_exp2f(sacc[kb][2 * g] + neg_m);
-      const float p1 = __builtin_amdgcn_exp2f(sacc[kb][2 * g + 1] + neg_m);
-      psum += p0 + p1;
-      pk[kb][g] = pack_bf16x2(p0, p1);
+    bm = xor32_max(bm) * c_scale;
+    alpha[qb] = 1.f;
+    if (bm > st[qb].m + kRescaleM) {
+      alpha[qb] = __builtin_amdgcn_exp2f(st[qb].m - bm);  // 0 while m = -inf
+      st[qb].m = bm;
     }
-  st.l = st.l * alpha + xor32_sum(psum);
+    rescale |= alpha[qb] != 1.f;
+    const float neg_m = (st[qb].m == -INFINITY) ? 0.f : -st[qb].m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int g = 0; g < 8; g++) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][2 * g], c_scale, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][2 * g + 1], c_scale, neg_m));
+        psum += p0 + p1;
+        pk[qb][kb][g] = pack_bf16x2(p0, p1);
+      }
+    st[qb].l = st[qb].l * alpha[qb] + xor32_sum(psum);
+  }
+  if (__ballot(rescale) != 0ull) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[qb][db][r] *= alpha[qb];
+  }
 
-  // PV: four 16-key halves, four 32-column blocks each
+  // PV: four 16-key halves, four 32-column blocks each; every V^T fragment serves all query blocks
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
 #pragma unroll
     for (int kh = 0; kh < 2; kh++) {
+      __builtin_amdgcn_sched_barrier(0);
       u32x2 vr[4][2];
       vt_frags(vt, voff, 32 * kb + 16 * kh, vr);
-      const v8bf pf = __builtin_bit_cast(
-          v8bf, (u32x4){pk[kb][4 * kh], pk[kb][4 * kh + 1], pk[kb][4 * kh + 2], pk[kb][4 * kh + 3]});
 #pragma unroll
-      for (int db = 0; db < 4; db++) {
-        const v8bf vf =
-            __builtin_bit_cast(v8bf, (u32x4){vr[db][0][0], vr[db][0][1], vr[db][1][0], vr[db][1][1]});
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[db], 0, 0, 0);
+      for (int qb = 0; qb < QB; qb++) {
+        const v8bf pf = __builtin_bit_cast(v8bf, (u32x4){pk[qb][kb][4 * kh], pk[qb][kb][4 * kh + 1],
+                                                         pk[qb][kb][4 * kh + 2], pk[qb][kb][4 * kh + 3]});
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const v8bf vf =
+              __builtin_bit_cast(v8bf, (u32x4){vr[db][0][0], vr[db][0][1], vr[db][1][0], vr[db][1][1]});
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[qb][db], 0, 0, 0);
+        }
       }
     }
 }
 
-__global__ __launch_bounds__(256, 2) void mha_masked_kernel(const uint16_t* __restrict__ q,
+template <int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void mha_masked_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint32_t* __restrict__ mask, int n_q, int n_kv,
@@ -208,22 +236,26 @@ __global__ __launch_bounds__(256, 2) void mha_masked_kernel(const uint16_t* __re
   const int qt = n_qt - 1 - (int)blockIdx.x / H;  // longest query tiles first
   const int h = (int)blockIdx.x % H;
   const int b = blockIdx.y;
-  const int t0 = qt * kMBQ;
-  const int t_last = min(t0 + kMBQ - 1, n_q - 1);
+  constexpr int kQ = 128 * QB;  // queries per workgroup
+  const int t0 = qt * kQ;
+  const int t_last = min(t0 + kQ - 1, n_q - 1);
   const int pos_last = n_kv - n_q + t_last;
   const int n_tiles = pos_last / kMBK + 1;
-  const int t = t0 + 32 * wave + (lane & 31);
-  const int tq = min(t, n_q - 1);
-  const size_t qrow = (size_t)b * n_q + tq;
 
-  // Q^T fragments: lane holds query t, dims 16ks + 8(l/32) .. +8
-  v8bf qf[kMD / 16];
-  {
+  // Q^T fragments: query block qb of lane l is query t0 + 32(QB w + qb) + l%32, dims 16ks + 8(l/32) .. +8
+  v8bf qf[QB][kMD / 16];
+  const uint32_t* mrow[QB];
+  int tq_[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    const int t = t0 + 32 * (QB * wave + qb) + (lane & 31);
+    tq_[qb] = t;
+    const size_t qrow = (size_t)b * n_q + min(t, n_q - 1);
     const uint16_t* qp = q + (qrow * H + h) * kMD + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kMD / 16; ks++) qf[ks] = *(const v8bf*)(qp + 16 * ks);
+    for (int ks = 0; ks < kMD / 16; ks++) qf[qb][ks] = *(const v8bf*)(qp + 16 * ks);
+    mrow[qb] = mask + qrow * W;
   }
-  const uint32_t* mrow = mask + qrow * W;
 
   // fragment offsets inside a tile (see the header: swizzled 16-byte chunks)
   int koff[4], voff[4];
@@ -241,21 +273,31 @@ __global__ __launch_bounds__(256, 2) void mha_masked_kernel(const uint16_t* __re
   const char* kh = (const char*)k + ((size_t)b * n_kv * H + h) * (kMD * 2);
   const char* vh = (const char*)v + ((size_t)b * n_kv * H + h) * (kMV * 2);
 
-  v16f o[4];
+  v16f o[QB][4];
+  MhaState st[QB];
 #pragma unroll
-  for (int db = 0; db < 4; db++)
+  for (int qb = 0; qb < QB; qb++) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) o[db][r] = 0.f;
-  MhaState st{-INFINITY, 0.f};
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) o[qb][db][r] = 0.f;
+    st[qb] = MhaState{-INFINITY, 0.f};
+  }
   const float c_scale = sm_scale * kLog2eM;
 
   // The query side is complete before the first copy is issued, so the waits below only ever cover
   // tile copies and mask words.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  uint32_t mw0[2], mw1[2];
+  uint32_t mw0[QB][2], mw1[QB][2];
+  auto load_mask = [&](uint32_t (&mw)[QB][2], int j) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) {
+      mw[qb][0] = mrow[qb][2 * j];
+      mw[qb][1] = mrow[qb][2 * j + 1];
+    }
+  };
   issue_tile(kh, vh, row_k, row_v, 0, n_kv, src, kt0, vt0, wave);
-  mw0[0] = mrow[0];
-  mw0[1] = mrow[1];
+  load_mask(mw0, 0);
   wait_vm0();
   barrier_lds();
   // Two tiles per round, buffer 0 then buffer 1.  Copies are unconditional (past the last tile they
@@ -263,34 +305,36 @@ __global__ __launch_bounds__(256, 2) void mha_masked_kernel(const uint16_t* __re
   for (int j = 0; j < n_tiles; j += 2) {
     const int j1 = min(j + 1, n_tiles - 1);
     issue_tile(kh, vh, row_k, row_v, j1, n_kv, src, kt1, vt1, wave);
-    mw1[0] = mrow[2 * j1];
-    mw1[1] = mrow[2 * j1 + 1];
-    compute_tile(kt0, vt0, mw0, qf, koff, voff, o, st, c_scale, lane);
+    load_mask(mw1, j1);
+    compute_tile<QB>(kt0, vt0, mw0, qf, koff, voff, o, st, c_scale, lane);
     wait_vm0();
     barrier_lds();
     const int j2 = min(j + 2, n_tiles - 1);
     issue_tile(kh, vh, row_k, row_v, j2, n_kv, src, kt0, vt0, wave);
-    mw0[0] = mrow[2 * j2];
-    mw0[1] = mrow[2 * j2 + 1];
-    if (j + 1 < n_tiles) compute_tile(kt1, vt1, mw1, qf, koff, voff, o, st, c_scale, lane);
+    load_mask(mw0, j2);
+    if (j + 1 < n_tiles) compute_tile<QB>(kt1, vt1, mw1, qf, koff, voff, o, st, c_scale, lane);
     wait_vm0();
     barrier_lds();
   }
 
-  if (t < n_q) {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    uint16_t* op = out + (((size_t)b * n_q + t) * H + h) * kMV + 4 * (lane >> 5);
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+  for (int qb = 0; qb < QB; qb++) {
+    const int t = tq_[qb];
+    if (t < n_q) {
+      const float inv = st[qb].l > 0.f ? 1.f / st[qb].l : 0.f;
+      uint16_t* op = out + (((size_t)b * n_q + t) * H + h) * kMV + 4 * (lane >> 5);
 #pragma unroll
-      for (int qd = 0; qd < 4; qd++) {
-        u32x2 w2;
-        w2[0] = pack_bf16x2(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
-        w2[1] = pack_bf16x2(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-        *(u32x2*)(op + 32 * db + 8 * qd) = w2;
-      }
-    if (lse != nullptr && lane < 32)
-      lse[((size_t)b * n_q + t) * H + h] = st.l > 0.f ? (st.m + log2f(st.l)) * kLn2M : -INFINITY;
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int qd = 0; qd < 4; qd++) {
+          u32x2 w2;
+          w2[0] = pack_bf16x2(o[qb][db][4 * qd + 0] * inv, o[qb][db][4 * qd + 1] * inv);
+          w2[1] = pack_bf16x2(o[qb][db][4 * qd + 2] * inv, o[qb][db][4 * qd + 3] * inv);
+          *(u32x2*)(op + 32 * db + 8 * qd) = w2;
+        }
+      if (lse != nullptr && lane < 32)
+        lse[((size_t)b * n_q + t) * H + h] = st[qb].l > 0.f ? (st[qb].m + log2f(st[qb].l)) * kLn2M : -INFINITY;
+    }
   }
 }
 
@@ -324,9 +368,10 @@ hipError_t launch_masked_mha(const uint16_t* q, const uint16_t* k, const uint16_
   hipLaunchKernelGGL(mha_mask_kernel, dim3(n_q, B), dim3(256), (size_t)W * 4, stream, idx, n_q, n_kv, k_sel, W, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_qt = (n_q + kMBQ - 1) / kMBQ;
-  hipLaunchKernelGGL(mha_masked_kernel, dim3(n_qt * H, B), dim3(256), 0, stream, q, k, v, (const uint32_t*)mask, n_q,
-                     n_kv, H, W, sm_scale, n_qt, out, lse);
+  constexpr int QB = kMhaQB;
+  const int n_qt = (n_q + 128 * QB - 1) / (128 * QB);
+  hipLaunchKernelGGL(mha_masked_kernel<QB>, dim3(n_qt * H, B), dim3(256), 0, stream, q, k, v, (const uint32_t*)mask,
+                     n_q, n_kv, H, W, sm_scale, n_qt, out, lse);
   return hipGetLastError();
 }
 
