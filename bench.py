@@ -31,6 +31,7 @@ PEAK_HBM_GBS = 8000.0
 
 IDX_FLOP_PER_PAIR = 2 * 64 * 128          # one causal (query, key) pair: 64 heads x 128-dim dot
 ATT_FLOP_PER_ENTRY = 2 * 128 * (576 + 512)  # one selected entry: QK (576) and PV (512) for 128 heads
+MHA_FLOP_PER_PAIR = 2 * 128 * (192 + 128)   # masked MHA mode: QK (192) and PV (128) per (query, key), 128 heads
 
 
 def parse():
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--k", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--mha-lens", default="4096,8192,12288,16384",
+                    help="prefill lengths of the masked-MHA vs sparse-MQA attention sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference kernel for the HBM byte "
                          "counters), then exit")
@@ -274,7 +277,82 @@ def main():
         out["cpu_baseline"] = cpu_baseline_prefill(pre, k, sm)
         if dec:
             out["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, k, sm)
+
+    # ------------------------------------------------------------------ masked MHA mode (short prefill)
+    if args.only in (None, "prefill") and args.mha_lens:
+        out["masked_mha"] = masked_mha_sweep([int(v) for v in args.mha_lens.split(",")], k, dev, stream)
     print(json.dumps(out), flush=True)
+
+
+def masked_mha_sweep(lens, k, dev, stream):
+    """Attention of one prefill of L tokens in both modes, on the same selection (indexer + top-k of the
+    sequence): masked MHA mode (MHA form: 128 heads, d_qk 192, d_v 128; the mask build included) and
+    sparse MQA mode (latent rows, d_qk 576, d_v 512).  Reported: both times per L, the masked-MHA rate at
+    8K against the bf16 peak (dense-equivalent: every causal pair is computed, masked or not), and the
+    length where the two modes cross (linear interpolation between the measured lengths)."""
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def t_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return sorted(ts)[len(ts) // 2]
+
+    sweep = []
+    for L in lens:
+        print(f"[bench] masked MHA vs sparse MQA at L={L}", file=sys.stderr, flush=True)
+        x = synth.prefill(L, seed=0, device=dev, n_needles=max(1, L // 128), needle_layout="random")
+        scores = torch.empty((1, L, L), dtype=torch.float32, device=dev)
+        dsa.indexer_scores(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None], scores)
+        idx = dsa.topk(scores, L, k)
+        del scores
+        m = synth.mha_heads(L, seed=0, device=dev)
+        ws = torch.empty(max(dsa.masked_mha_workspace_size(1, L, L), 256), dtype=torch.uint8, device=dev)
+        o1 = torch.empty((1, L, 128, 128), dtype=torch.bfloat16, device=dev)
+        l1 = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        t_mha = t_ms(lambda: dsa.masked_mha_attn(m["q"][None], m["k"][None], m["v"][None], idx, m["sm_scale"], out=o1,
+                                                 lse=l1, workspace=ws))
+        del m, ws, o1, l1
+        mq_ws = dsa.lib().dsa_sparse_mla_attn_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16)
+        ws2 = torch.empty(max(mq_ws, 256), dtype=torch.uint8, device=dev)
+        o2 = torch.empty((1, L, 128, 512), dtype=torch.bfloat16, device=dev)
+        l2 = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        t_mqa = t_ms(lambda: dsa.sparse_mla_attn(x["q"][None], x["kv"][None], idx, 512, x["sm_scale"], out=o2, lse=l2,
+                                                 workspace=ws2))
+        del x, idx, ws2, o2, l2
+        torch.cuda.empty_cache()
+        pairs, entries = causal_work(L, L, k)
+        sweep.append({"L": L, "masked_mha_ms": round(t_mha, 4), "sparse_mqa_ms": round(t_mqa, 4),
+                      "masked_mha_dense_TFLOP/s": round(pairs * MHA_FLOP_PER_PAIR / (t_mha * 1e-3) / 1e12, 1),
+                      "masked_mha_useful_TFLOP/s": round(entries * MHA_FLOP_PER_PAIR / (t_mha * 1e-3) / 1e12, 1),
+                      "sparse_mqa_TFLOP/s": round(entries * ATT_FLOP_PER_ENTRY / (t_mqa * 1e-3) / 1e12, 1)})
+    res = {"workload": ("prefill 1xL, attention only, both modes on the same top-k (k=%d) selection; masked MHA: "
+                        "128 heads d_qk=192 d_v=128 bf16; sparse MQA: 128 heads d_qk=576 d_v=512 bf16" % k),
+           "sweep": sweep}
+    ref = next((e for e in sweep if e["L"] == 8192), sweep[0] if sweep else None)
+    if ref:
+        tf = ref["masked_mha_dense_TFLOP/s"]
+        res["roofline"] = {"bound": "mfma", "L": ref["L"], "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    cut = None
+    for a, b in zip(sweep, sweep[1:]):
+        da, db = a["masked_mha_ms"] - a["sparse_mqa_ms"], b["masked_mha_ms"] - b["sparse_mqa_ms"]
+        if da <= 0.0 < db:
+            cut = round(a["L"] + (b["L"] - a["L"]) * (-da) / (db - da))
+            break
+    res["cutover_L"] = cut
+    res["cutover_rule"] = "masked MHA mode below cutover_L, sparse MQA mode above (attention time only)"
+    return res
 
 
 def cpu_baseline_prefill(pre, k, sm):
