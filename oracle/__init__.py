@@ -193,3 +193,25 @@ def forward(q_i: np.ndarray, w: np.ndarray, k_i: np.ndarray, q: np.ndarray, kv: 
     idx, kth = topk(scores, pos, k)
     out, lse = sparse_attn(q, kv, idx, d_v, sm_scale)
     return dict(scores=scores, kth=kth, idx=idx, out=out, lse=lse)
+
+
+def absorb_q(q_mha: np.ndarray, w_ukt: np.ndarray) -> np.ndarray:
+    """MQA-mode query of MLA (velog summary, section 1.3: every latent entry serves all heads): the
+    no-rope part of each head's query is carried into latent space by that head's key up-projection,
+    q'_h = [W_UK,h^T q_nope,h ; q_rope,h], so that q'_h . [c ; k_rope] equals the MHA-form logit.
+
+    q_mha [R, H, d_nope + d_rope], w_ukt [H, d_c, d_nope] (row c of head h holds W_UK,h[:, c]).
+    Returns [R, H, d_c + d_rope] float64 (a float64 matmul as the step)."""
+    d_c, d_nope = w_ukt.shape[1:]
+    qn = np.asarray(q_mha[..., :d_nope], np.float64)
+    lat = np.einsum("rhd,hcd->rhc", qn, np.asarray(w_ukt, np.float64))
+    return np.concatenate([lat, np.asarray(q_mha[..., d_nope:], np.float64)], -1)
+
+
+def out_proj(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Per-head value up-projection applied after MQA-mode attention: o_h = W_UV,h o'_h, where o'_h is the
+    attention output in latent space (the first d_c latent columns are the values).
+
+    o_lat [R, H, d_c], w_uv [H, d_v, d_c].  Returns [R, H, d_v] float64 (a float64 matmul as the step)."""
+    return np.einsum("rhc,hvc->rhv", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+

@@ -371,6 +371,70 @@ def test_mha_mode_single_entry_and_padding(orc):
     np.testing.assert_allclose(lse2, lse, rtol=1e-14)
 
 
+# ------------------------------------------------------------------ MQA-mode projections
+
+def test_projections_brute_force(orc):
+    """Loops over every output element on tiny shapes (no library routine)."""
+    rng = np.random.default_rng(50)
+    R, H, dn, dr, dc, dv = 3, 2, 4, 2, 5, 3
+    q = rng.standard_normal((R, H, dn + dr)).astype(np.float32)
+    wk = rng.standard_normal((H, dc, dn)).astype(np.float32)
+    o = rng.standard_normal((R, H, dc)).astype(np.float32)
+    wv = rng.standard_normal((H, dv, dc)).astype(np.float32)
+    a = orc.absorb_q(q, wk)
+    b = orc.out_proj(o, wv)
+    for r in range(R):
+        for h in range(H):
+            for c in range(dc):
+                acc = 0.0
+                for d in range(dn):
+                    acc += float(q[r, h, d]) * float(wk[h, c, d])
+                assert abs(a[r, h, c] - acc) < 1e-12
+            for e in range(dr):
+                assert a[r, h, dc + e] == float(q[r, h, dn + e])
+            for v in range(dv):
+                acc = 0.0
+                for c in range(dc):
+                    acc += float(o[r, h, c]) * float(wv[h, v, c])
+                assert abs(b[r, h, v] - acc) < 1e-12
+
+
+def test_projections_exact_integers(orc):
+    """Small integers: every product and sum is exact, so the result equals an int64 computation."""
+    rng = np.random.default_rng(51)
+    q = rng.integers(-8, 9, (6, 3, 16 + 4)).astype(np.float32)
+    wk = rng.integers(-8, 9, (3, 24, 16)).astype(np.float32)
+    ref = (q[..., :16].astype(np.int64)[:, :, None, :] * wk.astype(np.int64)[None]).sum(-1)
+    a = orc.absorb_q(q, wk)
+    assert np.array_equal(a[..., :24], ref.astype(np.float64))
+    assert np.array_equal(a[..., 24:], q[..., 16:].astype(np.float64))
+    o = rng.integers(-8, 9, (6, 3, 24)).astype(np.float32)
+    wv = rng.integers(-8, 9, (3, 10, 24)).astype(np.float32)
+    ref = (o.astype(np.int64)[:, :, None, :] * wv.astype(np.int64)[None]).sum(-1)
+    assert np.array_equal(orc.out_proj(o, wv), ref.astype(np.float64))
+
+
+def test_projections_compose_mqa_attention_into_mha_attention(orc):
+    """out_proj(MQA attention(absorb_q(q), latent rows)) equals the MHA-form attention with per-head rows
+    k_h = [W_UK,h c ; k_rope], v_h = W_UV,h c: the two oracles and the two projections agree."""
+    rng = np.random.default_rng(52)
+    L, H, d_c, d_r, d_h, d_hv, k = 40, 3, 24, 6, 10, 8, 13
+    q_mha, _, v_mha, _, kv_mqa, w_uv = _mla_pair(rng, L, H, d_c, d_r, d_h, d_hv)
+    # keys rebuilt from an explicit W_UK (the helper does not return its own), values as the helper built
+    c = kv_mqa[:, :d_c].astype(np.float64)
+    w_uk = rng.standard_normal((H, d_h, d_c)) / math.sqrt(d_c)
+    k_mha = np.concatenate([np.einsum("hdc,sc->shd", w_uk, c),
+                            np.broadcast_to(kv_mqa[:, None, d_c:], (L, H, d_r))], -1).astype(np.float32)
+    w_ukt = np.ascontiguousarray(np.transpose(w_uk, (0, 2, 1))).astype(np.float32)
+    q_mqa = orc.absorb_q(q_mha, w_ukt).astype(np.float32)
+    idx, _ = orc.topk(rng.standard_normal((L, L)).astype(np.float32), np.arange(L, dtype=np.int64), k)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    o_lat, lse_c = orc.sparse_attn(q_mqa, kv_mqa, idx, d_c, scale)
+    out, lse = orc.sparse_attn_mha(q_mha, k_mha, v_mha, idx, scale)
+    np.testing.assert_allclose(orc.out_proj(o_lat, w_uv.astype(np.float32)), out, rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(lse_c, lse, rtol=1e-5, atol=1e-5)
+
+
 # ------------------------------------------------------------------ composition
 
 def test_forward_tiny_config_is_self_consistent(orc):
