@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--k", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--no-proj", action="store_true", help="skip the MQA-mode projection measurement")
     ap.add_argument("--mha-lens", default="4096,8192,12288,16384",
                     help="prefill lengths of the masked-MHA vs sparse-MQA attention sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -281,7 +282,48 @@ def main():
     # ------------------------------------------------------------------ masked MHA mode (short prefill)
     if args.only in (None, "prefill") and args.mha_lens:
         out["masked_mha"] = masked_mha_sweep([int(v) for v in args.mha_lens.split(",")], k, dev, stream)
+    if args.only in (None, "prefill") and not args.no_proj:
+        out["mla_projections"] = projections_bench(args.prefill_len, dev, stream)
     print(json.dumps(out), flush=True)
+
+
+def projections_bench(L, dev, stream):
+    """The MQA-mode projections at the prefill size (L tokens x 128 heads): query absorption of W_UK
+    (reads the 192-wide per-head query, writes the 576-wide latent query) and the output up-projection
+    W_UV (reads the 512-wide latent output, writes 128).  HBM-bound: bytes per (token, head) are
+    384 + 1152 and 1024 + 256 (weights, 16 MiB each, stay in cache)."""
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    H = 128
+    print(f"[bench] MQA-mode projections at {L} tokens", file=sys.stderr, flush=True)
+    g = torch.Generator(device=dev).manual_seed(0)
+    q = torch.randn((L, H, 192), generator=g, device=dev).to(torch.bfloat16)
+    o_lat = torch.randn((L, H, 512), generator=g, device=dev).to(torch.bfloat16)
+    w = synth.mla_weights(H, seed=0, device=dev)
+    q_mqa = torch.empty((L, H, 576), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((L, H, 128), dtype=torch.bfloat16, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ta, tb = [], []
+    for rep in range(6):
+        ev[0].record(stream)
+        dsa.mla_absorb_q(q, w["w_ukt"], q_mqa)
+        ev[1].record(stream)
+        dsa.mla_out_proj(o_lat, w["w_uv"], o)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            ta.append(ev[0].elapsed_time(ev[1]))
+            tb.append(ev[1].elapsed_time(ev[2]))
+    res = {"workload": f"{L} tokens x {H} heads, bf16; absorb 128->512 (+64 rope), out 512->128"}
+    for name, ts, per, flop in (("absorb_q", ta, 384 + 1152, 2 * 128 * 512), ("out_proj", tb, 1024 + 256, 2 * 512 * 128)):
+        t = sorted(ts)[len(ts) // 2]
+        gbs = L * H * per / (t * 1e-3) / 1e9
+        res[name] = {"ms": round(t, 4), "GB/s": round(gbs, 1), "TFLOP/s": round(L * H * flop / (t * 1e-3) / 1e12, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return res
 
 
 def masked_mha_sweep(lens, k, dev, stream):

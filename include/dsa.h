@@ -160,6 +160,28 @@ dsa_status_t dsa_masked_mha_attn(const void* q, const void* k, const void* v, co
 size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv);
 
 /* ------------------------------------------------------------------------------------------------
+ * MQA-mode projections either side of dsa_sparse_mla_attn (velog summary, section 1.3: MLA in MQA
+ * mode shares each latent entry across the query heads, so the key up-projection W_UK is absorbed
+ * into the query and the value up-projection W_UV is applied after attention).  Per head h of each
+ * of `rows` tokens (rows = B * n_q, any batch layout that is token-major):
+ *
+ *   dsa_mla_absorb_q:  q_mqa[r][h][0:d_c]        = sum_d q_mha[r][h][d] * W_UK,h[d][:]   (d < d_nope)
+ *                      q_mqa[r][h][d_c:d_c+d_rope] = q_mha[r][h][d_nope:d_nope+d_rope]   (copied)
+ *   dsa_mla_out_proj:  o[r][h][v]                = sum_c W_UV,h[v][c] * o_lat[r][h][c]
+ *
+ * Layouts: q_mha [rows][H][d_nope + d_rope], q_mqa [rows][H][d_c + d_rope] (the dsa_sparse_mla_attn
+ * query), o_lat [rows][H][d_c] (its output), o [rows][H][d_v].  Weights are row-major with the
+ * contraction dimension last: w_ukt [H][d_c][d_nope] (w_ukt[h][c][d] = W_UK,h[d][c]) and
+ * w_uv [H][d_v][d_c].  bf16 in and out, fp32 accumulation; d_nope = 128, d_rope = 64, d_c = 512,
+ * d_v = 128, any H.  All pointers 16-byte aligned.  Other shapes: DSA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa, int rows, int H,
+                              int d_nope, int d_rope, int d_c, dsa_dtype_t dtype, void* stream);
+
+dsa_status_t dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int rows, int H, int d_c,
+                              int d_v, dsa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * dsa_forward_prefill -- the whole path for B sequences of n_kv tokens whose last n_q tokens are
  * queries: dsa_indexer_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.  Chunked prefill
  * is one call per chunk with n_kv growing by the chunk length (all state is in the caller's caches).

@@ -271,6 +271,36 @@ dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* i
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, p, workspace, (hipStream_t)stream);
 }
 
+dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa, int rows, int H, int d_nope,
+                              int d_rope, int d_c, dsa_dtype_t dtype, void* stream) {
+  if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "absorb_q: rows and H must be positive");
+  if (dtype != DSA_BF16 || d_nope != 128 || d_rope != 64 || d_c != 512)
+    return fail(DSA_ERR_UNSUPPORTED, "absorb_q: supports bf16 with d_nope=128, d_rope=64, d_c=512");
+  if (((long long)(rows + 127) / 128 * H + 7) / 8 * 8 * 4 > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "absorb_q: grid too large");
+  if (!q_mha || !w_ukt || !q_mqa) return fail(DSA_ERR_INVALID_ARG, "absorb_q: null pointer");
+  if (!(aligned(q_mha, 16) && aligned(w_ukt, 16) && aligned(q_mqa, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "absorb_q: pointers must be 16-byte aligned");
+  return hip_status(dsa::launch_mla_absorb_q((const uint16_t*)q_mha, (const uint16_t*)w_ukt, (uint16_t*)q_mqa, rows,
+                                             H, (hipStream_t)stream),
+                    "dsa_mla_absorb_q");
+}
+
+dsa_status_t dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int rows, int H, int d_c, int d_v,
+                              dsa_dtype_t dtype, void* stream) {
+  if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "out_proj: rows and H must be positive");
+  if (dtype != DSA_BF16 || d_c != 512 || d_v != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "out_proj: supports bf16 with d_c=512, d_v=128");
+  if (((long long)(rows + 127) / 128 * H + 7) / 8 * 8 > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "out_proj: grid too large");
+  if (!o_lat || !w_uv || !o) return fail(DSA_ERR_INVALID_ARG, "out_proj: null pointer");
+  if (!(aligned(o_lat, 16) && aligned(w_uv, 16) && aligned(o, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "out_proj: pointers must be 16-byte aligned");
+  return hip_status(dsa::launch_mla_out_proj((const uint16_t*)o_lat, (const uint16_t*)w_uv, (uint16_t*)o, rows, H,
+                                             (hipStream_t)stream),
+                    "dsa_mla_out_proj");
+}
+
 size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv) {
   if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv || n_kv > kMhaMaxKeys) return 0;
   return align_up((size_t)B * n_q * dsa::mha_mask_words(n_kv) * 4, 256);

@@ -39,6 +39,8 @@ SIGNATURES = {
     "dsa_forward_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "dsa_masked_mha_attn": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
     "dsa_masked_mha_workspace_size": ([_I, _I, _I], _SZ),
+    "dsa_mla_absorb_q": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
+    "dsa_mla_out_proj": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
 }
 
 _lib = None
@@ -186,6 +188,31 @@ def masked_mha_attn(q, k, v, idx, sm_scale: float, out=None, lse=None, workspace
     _check(lib().dsa_masked_mha_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, nq, n_kv, H, d_qk, d_v, k_sel,
                                      float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
     return out, lse
+
+
+def mla_absorb_q(q_mha, w_ukt, q_mqa=None, stream=None):
+    """MQA-mode query: q_mha [..., H, 192] bf16 (no-rope 128 + rope 64), w_ukt [H, 512, 128] bf16 ->
+    q_mqa [..., H, 576] bf16 (W_UK absorbed into the no-rope part, rope copied)."""
+    _dev(q_mha, w_ukt, q_mqa)
+    H = q_mha.shape[-2]
+    rows = q_mha.numel() // (H * 192)
+    if q_mqa is None:
+        q_mqa = torch.empty(tuple(q_mha.shape[:-1]) + (576,), dtype=q_mha.dtype, device=q_mha.device)
+    _check(lib().dsa_mla_absorb_q(_ptr(q_mha), _ptr(w_ukt), _ptr(q_mqa), rows, H, 128, 64, 512, _dtype_code(q_mha),
+                                  _stream(stream)))
+    return q_mqa
+
+
+def mla_out_proj(o_lat, w_uv, o=None, stream=None):
+    """Per-head value up-projection: o_lat [..., H, 512] bf16, w_uv [H, 128, 512] bf16 -> o [..., H, 128]."""
+    _dev(o_lat, w_uv, o)
+    H = o_lat.shape[-2]
+    rows = o_lat.numel() // (H * 512)
+    if o is None:
+        o = torch.empty(tuple(o_lat.shape[:-1]) + (128,), dtype=o_lat.dtype, device=o_lat.device)
+    _check(lib().dsa_mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(o), rows, H, 512, 128, _dtype_code(o_lat),
+                                  _stream(stream)))
+    return o
 
 
 def forward_workspace_size(B, n_q, n_kv, H, d_qk, d_v, k, attn_dtype) -> int:

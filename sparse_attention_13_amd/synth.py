@@ -131,6 +131,17 @@ def mha_heads(L: int, seed: int = 0, device="cpu", n_q: int | None = None, H: in
                 v=_randn((L, H, d_v), g, device, torch.bfloat16, chunk_rows=1024))
 
 
+def mla_weights(H: int = 128, seed: int = 0, device="cpu", d_nope: int = 128, d_c: int = 512, d_v: int = 128) -> dict:
+    """Random up-projection weights of MLA (no trained weights are used): W_UK,h [d_nope, d_c] and
+    W_UV,h [d_v, d_c], entries N(0, 1) / sqrt(fan-in), bf16, stored with the contraction dimension last:
+    w_ukt [H, d_c, d_nope] (the transpose of W_UK,h) and w_uv [H, d_v, d_c].
+    Draw order: W_UK, W_UV (a generator of its own, seed + 2000003)."""
+    g = _gen(seed + 2000003, device)
+    w_uk = _randn((H, d_nope, d_c), g, device) / math.sqrt(d_nope)
+    w_uv = _randn((H, d_v, d_c), g, device) / math.sqrt(d_c)
+    return dict(w_ukt=w_uk.transpose(1, 2).contiguous().to(torch.bfloat16), w_uv=w_uv.to(torch.bfloat16))
+
+
 def decode(B: int, S: int, seed: int = 0, device="cpu", H_I: int = 64, d_I: int = 128, H: int = 128,
            d_qk: int = 576, d_v: int = 512, k: int = 2048) -> dict:
     """B sequences, one new query each at position S-1 over S cached tokens (per-sequence seed

@@ -11,7 +11,9 @@ Tolerances:
     within 1e-3 relative of the row's k-th score (the band) may be exchanged for one another: outside
     the band the sets must be equal and inside it the counts must match;
   * attention outputs: |gpu - oracle| <= 2e-2 + 1e-2 * |oracle| (bf16 outputs); the log-sum-exp, kept in
-    fp32, must be within 2e-4 absolute (a dropped or duplicated key moves it by about 1/k).
+    fp32, must be within 2e-4 absolute (a dropped or duplicated key moves it by about 1/k);
+  * projections (bf16 products with fp32 accumulation): |gpu - oracle| <= 1e-3 + 8e-3 * |oracle|; bit-exact
+    on exact-integer inputs whose sums bf16 represents.
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ IDX_REL = 1e-3
 IDX_ROUND = 1e-5
 ATT_ABS, ATT_REL = 2e-2, 1e-2
 LSE_ABS = 2e-4
+PROJ_ABS, PROJ_REL = 1e-3, 8e-3  # bf16 output of an fp32-accumulated product: rounding <= 2^-9 relative
 
 
 def indexer_errors(gpu_rows: np.ndarray, ora_rows: np.ndarray, mag_rows: np.ndarray, absmag_rows: np.ndarray,

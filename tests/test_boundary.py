@@ -37,7 +37,8 @@ def test_header_declares_the_path():
     for n in ["dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_attn", "dsa_forward_prefill",
               "dsa_forward_decode",
               "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
-              "dsa_last_error", "dsa_version", "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size"]:
+              "dsa_last_error", "dsa_version", "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size",
+              "dsa_mla_absorb_q", "dsa_mla_out_proj"]:
         assert n in names
 
 
@@ -172,6 +173,23 @@ def test_masked_mha_validation_and_workspace(L):
     assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned k
     a = list(ok); a[10] = 0
     assert f(*a) == DSA_ERR_INVALID_ARG                              # k_sel = 0
+
+
+def test_projection_validation(L):
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_F32
+    a = L.dsa_mla_absorb_q
+    assert a(FAKE, FAKE, FAKE2, 0, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_INVALID_ARG      # no rows
+    assert a(FAKE, FAKE, FAKE2, 10, 128, 64, 64, 512, DSA_BF16, None) == DSA_ERR_UNSUPPORTED     # d_nope
+    assert a(FAKE, FAKE, FAKE2, 10, 128, 128, 64, 512, DSA_F32, None) == DSA_ERR_UNSUPPORTED     # dtype
+    assert a(None, FAKE, FAKE2, 10, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_INVALID_ARG    # null
+    assert a(ctypes.c_void_p(0x10004), FAKE, FAKE2, 10, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_INVALID_ARG
+    o = L.dsa_mla_out_proj
+    assert o(FAKE, FAKE, FAKE2, 10, 0, 512, 128, DSA_BF16, None) == DSA_ERR_INVALID_ARG         # H = 0
+    assert o(FAKE, FAKE, FAKE2, 10, 128, 576, 128, DSA_BF16, None) == DSA_ERR_UNSUPPORTED       # d_c
+    assert o(FAKE, None, FAKE2, 10, 128, 512, 128, DSA_BF16, None) == DSA_ERR_INVALID_ARG       # null
+    assert o(FAKE, FAKE, ctypes.c_void_p(0x20002), 10, 128, 512, 128, DSA_BF16, None) == DSA_ERR_INVALID_ARG
+    assert o(FAKE, FAKE, FAKE2, 2**31 - 1, 128, 512, 128, DSA_BF16, None) == DSA_ERR_UNSUPPORTED  # grid
+    assert a(FAKE, FAKE, FAKE2, 2**30, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_UNSUPPORTED    # grid
 
 
 def test_forward_validation(L):
