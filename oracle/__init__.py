@@ -58,6 +58,9 @@ def _load():
         lib.oracle_topk.argtypes = [P, I64, I64, P, I, P, P]
         lib.oracle_sparse_attn.argtypes = [P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
         lib.oracle_sparse_attn_mha.argtypes = [P, P, P, P, I64, I, I, I, I, ctypes.c_double, P, P]
+        lib.oracle_warmup_target.argtypes = [P, P, I64, P, I, I, ctypes.c_double, P, I64]
+        lib.oracle_warmup_loss.argtypes = [P, P, I64, P, I64, I64, P, P, I64]
+        lib.oracle_warmup_backward.argtypes = [P, P, P, P, I64, P, I, I, I64, I64, P, P, P]
         lib.oracle_threads.restype = I
         _lib = lib
     return _lib
@@ -214,4 +217,52 @@ def out_proj(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
 
     o_lat [R, H, d_c], w_uv [H, d_v, d_c].  Returns [R, H, d_v] float64 (a float64 matmul as the step)."""
     return np.einsum("rhc,hvc->rhv", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+
+
+def warmup_target(q: np.ndarray, kv: np.ndarray, pos: np.ndarray, sm_scale: float, ld: int | None = None):
+    """Dense warm-up target (velog summary, Continued Pre-Training, Stage 1): the main MQA-mode attention
+    summed over heads and L1-normalised, p[r][s] for s <= pos[r] (float64, zero elsewhere).
+    q [R, H, d_qk], kv [S, d_qk] float32."""
+    q = _c(q, np.float32)
+    kv = _c(kv, np.float32)
+    pos = _c(pos, np.int64)
+    R, H, d_qk = q.shape
+    ld = kv.shape[0] if ld is None else ld
+    assert kv.shape[1] == d_qk and (R == 0 or pos.max() < kv.shape[0])
+    p = np.zeros((R, ld), np.float64)
+    _load().oracle_warmup_target(_p(q), _p(kv), R, _p(pos), H, d_qk, float(sm_scale), _p(p), ld)
+    return p
+
+
+def warmup_loss(p: np.ndarray, scores: np.ndarray, pos: np.ndarray):
+    """KL(p[r] || softmax(I[r])) over s <= pos[r] and its gradient with respect to I, g = softmax(I) - p.
+    p [R, ld] float64, scores [R, ld_s] float32.  Returns (loss [R] float64, g [R, ld] float64)."""
+    p = _c(p, np.float64)
+    scores = _c(scores, np.float32)
+    pos = _c(pos, np.int64)
+    R = p.shape[0]
+    loss = np.empty(R, np.float64)
+    g = np.zeros_like(p)
+    _load().oracle_warmup_loss(_p(p), _p(scores), R, _p(pos), p.shape[1], scores.shape[1], _p(loss), _p(g),
+                               g.shape[1])
+    return loss, g
+
+
+def warmup_backward(q: np.ndarray, w: np.ndarray, k: np.ndarray, g: np.ndarray, pos: np.ndarray):
+    """Gradients of the warm-up loss through the indexer, given g = dL/dI [R, ld] (float64):
+    returns (dq [R, H, d], dw [R, H], dk [S, d]) float64 with respect to the dequantised q, the weights w and
+    the dequantised k."""
+    q = _c(q, np.float32)
+    w = _c(w, np.float32)
+    k = _c(k, np.float32)
+    g = _c(g, np.float64)
+    pos = _c(pos, np.int64)
+    R, H, d = q.shape
+    S = k.shape[0]
+    dq = np.empty((R, H, d), np.float64)
+    dw = np.empty((R, H), np.float64)
+    dk = np.empty((S, d), np.float64)
+    _load().oracle_warmup_backward(_p(q), _p(w), _p(k), _p(g), R, _p(pos), H, d, S, g.shape[1], _p(dq), _p(dw),
+                                   _p(dk))
+    return dq, dw, dk
 

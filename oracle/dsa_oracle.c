@@ -272,3 +272,120 @@ void oracle_sparse_attn_mha(const float* q, const float* kk, const float* v, con
     }
   }
 }
+
+/* ---------------------------------------------------------------- indexer warm-up loss
+ * Dense warm-up stage (velog summary, Continued Pre-Training, Stage 1): the main model is frozen and
+ * only the indexer learns.  Its target for query t is the main attention summed over heads and
+ * L1-normalised; its loss is the KL divergence from that target to the softmax of the index scores:
+ *   A_h[t][s] = softmax_s(sm_scale * q[t][h] . kv[s])              over s <= pos_t (dense, causal)
+ *   p[t][s]   = sum_h A_h[t][s] / sum_s' sum_h A_h[t][s']  =  (1/H) sum_h A_h[t][s]
+ *   L_t       = KL(p[t] || softmax(I[t]))  = sum_s p (log p - log softmax(I)_s)   (0 log 0 = 0)
+ * and the gradient of L = sum_t L_t with respect to the index scores is g = softmax(I[t]) - p[t].
+ */
+
+/* p [n_rows][ld] (double) from q [n_rows][H][d_qk], kv [n_kv][d_qk]; entries past pos untouched. */
+void oracle_warmup_target(const float* q, const float* kv, int64_t n_rows, const int64_t* pos, int H, int d_qk,
+                          double sm_scale, double* p, int64_t ld) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; r++) {
+    const int64_t n = pos[r] + 1;
+    double* z = (double*)malloc((size_t)n * sizeof(double));
+    double* pr = p + r * ld;
+    for (int64_t s = 0; s < n; s++) pr[s] = 0.0;
+    for (int h = 0; h < H; h++) {
+      const float* qh = q + (r * H + h) * (int64_t)d_qk;
+      double m = -INFINITY;
+      for (int64_t s = 0; s < n; s++) {
+        const float* c = kv + s * (int64_t)d_qk;
+        double dot = 0.0;
+        for (int e = 0; e < d_qk; e++) dot += (double)qh[e] * (double)c[e];
+        z[s] = sm_scale * dot;
+        if (z[s] > m) m = z[s];
+      }
+      double l = 0.0;
+      for (int64_t s = 0; s < n; s++) l += exp(z[s] - m);
+      for (int64_t s = 0; s < n; s++) pr[s] += exp(z[s] - m) / l;  /* A_h[t][s] */
+    }
+    double tot = 0.0;
+    for (int64_t s = 0; s < n; s++) tot += pr[s];
+    for (int64_t s = 0; s < n; s++) pr[s] /= tot;  /* L1 normalisation */
+    free(z);
+  }
+}
+
+/* loss [n_rows] and g [n_rows][ld] from the target p and the index scores I (both over s <= pos). */
+void oracle_warmup_loss(const double* p, const float* scores, int64_t n_rows, const int64_t* pos, int64_t ld_p,
+                        int64_t ld_s, double* loss, double* g, int64_t ld_g) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; r++) {
+    const int64_t n = pos[r] + 1;
+    const double* pr = p + r * ld_p;
+    const float* ir = scores + r * ld_s;
+    double m = -INFINITY;
+    for (int64_t s = 0; s < n; s++)
+      if ((double)ir[s] > m) m = (double)ir[s];
+    double l = 0.0;
+    for (int64_t s = 0; s < n; s++) l += exp((double)ir[s] - m);
+    const double lse = m + log(l);
+    double kl = 0.0;
+    for (int64_t s = 0; s < n; s++) {
+      const double logq = (double)ir[s] - lse;
+      if (pr[s] > 0.0) kl += pr[s] * (log(pr[s]) - logq);
+      g[r * ld_g + s] = exp(logq) - pr[s];
+    }
+    loss[r] = kl;
+  }
+}
+
+/* Gradients of L through I[t][s] = sum_j w[t][j] * ReLU(q[t][j] . k[s]) (s <= pos_t), given g = dL/dI:
+ *   dw[t][j]    = sum_s g[t][s] * ReLU(q[t][j] . k[s])
+ *   dq[t][j][:] = sum_s g[t][s] * w[t][j] * [q[t][j] . k[s] > 0] * k[s][:]
+ *   dk[s][:]    = sum_t sum_j g[t][s] * w[t][j] * [q[t][j] . k[s] > 0] * q[t][j][:]
+ * q [n_rows][H][d], k [n_kv][d] dequantised fp32 (the gradient is with respect to these values); all sums
+ * in double.  The dot products decide the indicator in double.
+ */
+void oracle_warmup_backward(const float* q, const float* w, const float* k, const double* g, int64_t n_rows,
+                            const int64_t* pos, int H, int d, int64_t n_kv, int64_t ld_g, double* dq, double* dw,
+                            double* dk) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; r++) {
+    for (int j = 0; j < H; j++) {
+      const float* qj = q + (r * H + j) * (int64_t)d;
+      double* dqj = dq + (r * H + j) * (int64_t)d;
+      for (int i = 0; i < d; i++) dqj[i] = 0.0;
+      double dwj = 0.0;
+      for (int64_t s = 0; s <= pos[r]; s++) {
+        const float* ks = k + s * (int64_t)d;
+        double dot = 0.0;
+        for (int i = 0; i < d; i++) dot += (double)qj[i] * (double)ks[i];
+        if (dot > 0.0) {
+          const double gs = g[r * ld_g + s];
+          dwj += gs * dot;
+          for (int i = 0; i < d; i++) dqj[i] += gs * (double)w[r * H + j] * (double)ks[i];
+        }
+      }
+      dw[r * H + j] = dwj;
+    }
+  }
+  /* dk: one key at a time, summing over every (query, head) that sees it */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t s = 0; s < n_kv; s++) {
+    double* dks = dk + s * (int64_t)d;
+    const float* ks = k + s * (int64_t)d;
+    for (int i = 0; i < d; i++) dks[i] = 0.0;
+    for (int64_t r = 0; r < n_rows; r++) {
+      if (s > pos[r]) continue;
+      const double gs = g[r * ld_g + s];
+      for (int j = 0; j < H; j++) {
+        const float* qj = q + (r * H + j) * (int64_t)d;
+        double dot = 0.0;
+        for (int i = 0; i < d; i++) dot += (double)qj[i] * (double)ks[i];
+        if (dot > 0.0) {
+          const double c = gs * (double)w[r * H + j];
+          for (int i = 0; i < d; i++) dks[i] += c * (double)qj[i];
+        }
+      }
+    }
+  }
+}
+

@@ -435,6 +435,110 @@ def test_projections_compose_mqa_attention_into_mha_attention(orc):
     np.testing.assert_allclose(lse_c, lse, rtol=1e-5, atol=1e-5)
 
 
+# ------------------------------------------------------------------ indexer warm-up loss
+
+def test_warmup_target_is_the_head_mean_of_causal_softmax(orc):
+    """p = (1/H) sum_h softmax(masked logits), computed here with torch on the CPU per head."""
+    rng = np.random.default_rng(60)
+    R, S, H, d = 6, 11, 4, 9
+    q = rng.standard_normal((R, H, d)).astype(np.float32)
+    kv = rng.standard_normal((S, d)).astype(np.float32)
+    pos = np.arange(S - R, S, dtype=np.int64)
+    p = orc.warmup_target(q, kv, pos, 0.37)
+    logits = torch.einsum("rhd,sd->rhs", torch.from_numpy(q).double(), torch.from_numpy(kv).double()) * 0.37
+    mask = torch.arange(S)[None, None, :] > torch.from_numpy(pos)[:, None, None]
+    ref = torch.softmax(logits.masked_fill(mask, -math.inf), dim=-1).mean(dim=1).numpy()
+    np.testing.assert_allclose(p, ref, rtol=1e-12, atol=1e-15)
+    # q = 0: every visible key equally likely
+    p0 = orc.warmup_target(np.zeros_like(q), kv, pos, 0.37)
+    for r, ps in enumerate(pos):
+        np.testing.assert_allclose(p0[r, :ps + 1], 1.0 / (ps + 1), rtol=1e-14)
+        assert np.all(p0[r, ps + 1:] == 0.0)
+
+
+def test_warmup_loss_closed_forms(orc):
+    # two keys by hand: p = (0.25, 0.75), I = (0, log 3) -> softmax(I) = (0.25, 0.75): KL = 0, g = 0
+    p = np.array([[0.25, 0.75]])
+    loss, g = orc.warmup_loss(p, np.array([[0.0, math.log(3.0)]], np.float32), np.array([1], np.int64))
+    assert abs(loss[0]) < 1e-7 and np.abs(g).max() < 1e-7
+    # I = (0, 0): q = (1/2, 1/2): KL = 0.25 log(0.5) + 0.75 log(1.5)
+    loss, g = orc.warmup_loss(p, np.zeros((1, 2), np.float32), np.array([1], np.int64))
+    assert abs(loss[0] - (0.25 * math.log(0.5) + 0.75 * math.log(1.5))) < 1e-14
+    np.testing.assert_allclose(g[0], [0.25, -0.25], atol=1e-15)
+    # random rows against torch's kl_div (input = log softmax(I), target = p), zero-probability entries too
+    rng = np.random.default_rng(61)
+    pos = np.array([0, 4, 9, 9], np.int64)
+    I = rng.standard_normal((4, 10)).astype(np.float32)
+    pt = np.zeros((4, 10))
+    for r, ps in enumerate(pos):
+        v = rng.random(ps + 1)
+        v[::3] = 0.0 if ps > 0 else v[::3]
+        pt[r, :ps + 1] = v / v.sum()
+    loss, g = orc.warmup_loss(pt, I, pos)
+    for r, ps in enumerate(pos):
+        li = torch.log_softmax(torch.from_numpy(I[r, :ps + 1]).double(), 0)
+        ref = torch.nn.functional.kl_div(li, torch.from_numpy(pt[r, :ps + 1]), reduction="sum").item()
+        assert abs(loss[r] - ref) < 1e-12, r
+        np.testing.assert_allclose(g[r, :ps + 1], li.exp().numpy() - pt[r, :ps + 1], atol=1e-15)
+
+
+def test_warmup_gradients_match_finite_differences(orc):
+    """dL/dI, dq, dw and dk against central differences of the whole composite loss
+    L(q, w, k) = sum_t KL(p_t || softmax(I(q, w, k)_t)), with I from the (separately pinned) indexer."""
+    rng = np.random.default_rng(62)
+    R, S, H, d = 3, 7, 2, 5
+    q = rng.standard_normal((R, H, d))
+    w = rng.standard_normal((R, H))
+    k = rng.standard_normal((S, d))
+    pos = np.arange(S - R, S, dtype=np.int64)
+    pt = np.zeros((R, S))
+    for r, ps in enumerate(pos):
+        v = rng.random(ps + 1)
+        pt[r, :ps + 1] = v / v.sum()
+
+    def total(qq, ww, kk):
+        # the indexer in double: the oracle's fp32 output rounding would swamp the differences
+        sc = np.zeros((R, S))
+        for r, ps in enumerate(pos):
+            dots = np.einsum("hd,sd->hs", qq[r], kk[:ps + 1])
+            sc[r, :ps + 1] = (ww[r][:, None] * np.maximum(dots, 0.0)).sum(0)
+        tot = 0.0
+        for r, ps in enumerate(pos):
+            li = sc[r, :ps + 1] - np.log(np.exp(sc[r, :ps + 1]).sum())
+            tot += float((pt[r, :ps + 1] * (np.log(pt[r, :ps + 1]) - li)).sum())
+        return tot, sc
+
+    base, sc = total(q, w, k)
+    # the oracle's loss and g on the same (float32-rounded) scores agree with the double evaluation
+    loss, g = orc.warmup_loss(pt, sc.astype(np.float32), pos)
+    assert abs(loss.sum() - base) < 1e-5
+    # the indexer oracle on these inputs reproduces the scores (links the two pinned functions)
+    io = orc.indexer(q.astype(np.float32), w.astype(np.float32), k.astype(np.float32), pos, ld=S)
+    for r, ps in enumerate(pos):
+        np.testing.assert_allclose(io[r, :ps + 1], sc[r, :ps + 1], rtol=1e-5, atol=1e-6)
+    g_exact = np.zeros((R, S))
+    for r, ps in enumerate(pos):
+        e = np.exp(sc[r, :ps + 1] - sc[r, :ps + 1].max())
+        g_exact[r, :ps + 1] = e / e.sum() - pt[r, :ps + 1]
+    dq, dw, dk = orc.warmup_backward(q.astype(np.float32), w.astype(np.float32), k.astype(np.float32), g_exact, pos)
+    eps = 1e-6
+
+    def num(arr, idx):
+        a1, a2 = arr.copy(), arr.copy()
+        a1[idx] += eps
+        a2[idx] -= eps
+        args1 = [a1 if arr is x else x for x in (q, w, k)]
+        args2 = [a2 if arr is x else x for x in (q, w, k)]
+        return (total(*args1)[0] - total(*args2)[0]) / (2 * eps)
+
+    for idx in [(0, 0, 0), (1, 1, 3), (2, 0, 4), (2, 1, 1)]:
+        assert abs(num(q, idx) - dq[idx]) < 1e-6 * max(1.0, abs(dq[idx])), ("dq", idx)
+    for idx in [(0, 0), (1, 1), (2, 0)]:
+        assert abs(num(w, idx) - dw[idx]) < 1e-6 * max(1.0, abs(dw[idx])), ("dw", idx)
+    for idx in [(0, 0), (3, 2), (6, 4), (5, 1)]:
+        assert abs(num(k, idx) - dk[idx]) < 1e-6 * max(1.0, abs(dk[idx])), ("dk", idx)
+
+
 # ------------------------------------------------------------------ composition
 
 def test_forward_tiny_config_is_self_consistent(orc):
