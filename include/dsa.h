@@ -160,6 +160,27 @@ dsa_status_t dsa_masked_mha_attn(const void* q, const void* k, const void* v, co
 size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv);
 
 /* ------------------------------------------------------------------------------------------------
+ * dsa_warmup_loss -- the indexer's dense warm-up loss (velog summary, Continued Pre-Training, Stage 1):
+ * the main model is frozen and the indexer learns to reproduce its attention.  For every query t
+ * (pos_t = n_kv - n_q + t) and s <= pos_t:
+ *
+ *   target[t][s] = (1/H) sum_h exp(sm_scale * q[t][h] . kv[s] - lse[t][h])
+ *                  (the main attention summed over heads and L1-normalised; lse[t][h] is that dense causal
+ *                   attention's natural-log log-sum-exp, as its forward pass produces it)
+ *   loss[t]      = KL(target[t] || softmax(I[t])) = sum_s target (log target - log softmax(I[t])_s)
+ *   scores[t][s] <- softmax(I[t])_s - target[t][s]      (the gradient of sum_t loss[t] with respect to I)
+ *
+ * q [B][n_q][H][d_qk], kv [B][n_kv][d_qk] bf16 (the MQA-mode inputs of dsa_sparse_mla_attn, 16-byte
+ * aligned), lse [B][n_q][H] fp32; scores [B][n_q][ld_scores] fp32 holds the index scores I on entry
+ * (as dsa_indexer_scores writes them) and the gradient on return; target [B][n_q][ld_target] fp32
+ * receives the target; loss [B][n_q] fp32.  Entries past pos_t are neither read nor written.
+ * bf16 with H = 128 and d_qk = 576 only.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, int B, int n_q, int n_kv, int H,
+                             int d_qk, float sm_scale, dsa_dtype_t dtype, float* scores, int64_t ld_scores,
+                             float* target, int64_t ld_target, float* loss, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * MQA-mode projections either side of dsa_sparse_mla_attn (velog summary, section 1.3: MLA in MQA
  * mode shares each latent entry across the query heads, so the key up-projection W_UK is absorbed
  * into the query and the value up-projection W_UV is applied after attention).  Per head h of each

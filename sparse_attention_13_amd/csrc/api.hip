@@ -271,6 +271,22 @@ dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* i
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, p, workspace, (hipStream_t)stream);
 }
 
+dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, int B, int n_q, int n_kv, int H, int d_qk,
+                             float sm_scale, dsa_dtype_t dtype, float* scores, int64_t ld_scores, float* target,
+                             int64_t ld_target, float* loss, void* stream) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: bad sizes");
+  if (dtype != DSA_BF16 || H != 128 || d_qk != 576)
+    return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: supports bf16 with H=128, d_qk=576 (got %d, %d)", H, d_qk);
+  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: grid too large");
+  if (!q || !kv || !lse || !scores || !target || !loss) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: null pointer");
+  if (ld_scores < n_kv || ld_target < n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: ld below n_kv");
+  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: sm_scale must be finite");
+  if (!(aligned(q, 16) && aligned(kv, 16))) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: q, kv must be 16-byte aligned");
+  return hip_status(dsa::launch_warmup_forward((const uint16_t*)q, (const uint16_t*)kv, lse, B, n_q, n_kv, sm_scale,
+                                               scores, ld_scores, target, ld_target, loss, (hipStream_t)stream),
+                    "dsa_warmup_loss");
+}
+
 dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa, int rows, int H, int d_nope,
                               int d_rope, int d_c, dsa_dtype_t dtype, void* stream) {
   if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "absorb_q: rows and H must be positive");

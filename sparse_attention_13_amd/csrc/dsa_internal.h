@@ -98,6 +98,11 @@ hipError_t launch_mla_absorb_q(const uint16_t* q_mha, const uint16_t* w_ukt, uin
                                hipStream_t stream);
 hipError_t launch_mla_out_proj(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int rows, int H,
                                hipStream_t stream);
+// Indexer warm-up loss: target p [B][n_q][ld_p] from the main attention (bf16, H = 128, d_qk = 576) and its
+// log-sum-exp lse [B][n_q][128], then per row the loss and g = softmax(I) - p over the scores [B][n_q][ld_s].
+hipError_t launch_warmup_forward(const uint16_t* q, const uint16_t* kv, const float* lse, int B, int n_q, int n_kv,
+                                 float sm_scale, float* scores, int64_t ld_s, float* p, int64_t ld_p, float* loss,
+                                 hipStream_t stream);
 // Masked MHA mode (bf16, d_qk = 192, d_v = 128): mask words per query row, and the two launches
 // (mask from the selection, then dense attention under it).  mask: [B][n_q][mha_mask_words(n_kv)] u32.
 int mha_mask_words(int n_kv);

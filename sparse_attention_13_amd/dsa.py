@@ -39,6 +39,7 @@ SIGNATURES = {
     "dsa_forward_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "dsa_masked_mha_attn": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
     "dsa_masked_mha_workspace_size": ([_I, _I, _I], _SZ),
+    "dsa_warmup_loss": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64, _P, _I64, _P, _P], _I),
     "dsa_mla_absorb_q": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "dsa_mla_out_proj": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
 }
@@ -188,6 +189,23 @@ def masked_mha_attn(q, k, v, idx, sm_scale: float, out=None, lse=None, workspace
     _check(lib().dsa_masked_mha_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, nq, n_kv, H, d_qk, d_v, k_sel,
                                      float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
     return out, lse
+
+
+def warmup_loss(q, kv, lse, scores, sm_scale: float, target=None, loss=None, stream=None):
+    """Indexer warm-up loss: q [B, n_q, 128, 576], kv [B, n_kv, 576] bf16, lse [B, n_q, 128] f32 (the main
+    attention's), scores [B, n_q, ld] f32 (index scores in, gradient softmax(I) - target out).
+    Returns (loss [B, n_q], target [B, n_q, ld])."""
+    _dev(q, kv, lse, scores, target, loss)
+    B, nq, H, d_qk = q.shape
+    n_kv = kv.shape[1]
+    if target is None:
+        target = torch.zeros_like(scores)
+    if loss is None:
+        loss = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+    _check(lib().dsa_warmup_loss(_ptr(q), _ptr(kv), _ptr(lse), B, nq, n_kv, H, d_qk, float(sm_scale), _dtype_code(q),
+                                 _ptr(scores), scores.shape[-1], _ptr(target), target.shape[-1], _ptr(loss),
+                                 _stream(stream)))
+    return loss, target
 
 
 def mla_absorb_q(q_mha, w_ukt, q_mqa=None, stream=None):
