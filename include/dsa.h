@@ -180,6 +180,24 @@ dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, in
                              int d_qk, float sm_scale, dsa_dtype_t dtype, float* scores, int64_t ld_scores,
                              float* target, int64_t ld_target, float* loss, void* stream);
 
+/* dsa_warmup_indexer_backward -- gradients of sum_t loss[t] (dsa_warmup_loss) through the indexer
+ * I[t][s] = sum_j w[t][j] ReLU(q^[t][j] . k^[s]), with q^ = q_i * q_i_scale and k^ = k_i * k_i_scale the
+ * dequantised inputs, given grad = dL/dI (the scores buffer dsa_warmup_loss returns):
+ *
+ *   dw[t][j]      = sum_{s <= pos_t} grad[t][s] ReLU(q^[t][j] . k^[s])
+ *   dq_i[t][j][:] = sum_{s <= pos_t} grad[t][s] w[t][j] [q^[t][j] . k^[s] > 0] k^[s][:]
+ *   dk_i[s][:]    = sum_t sum_j grad[t][s] w[t][j] [q^[t][j] . k^[s] > 0] q^[t][j][:]
+ *
+ * Inputs as dsa_indexer_scores (fp8 e4m3 codes, fp32 scales, H_I = 64, d_I = 128); grad
+ * [B][n_q][ld_grad] fp32 (entries past pos_t are not read).  Outputs fp32: dq_i [B][n_q][64][128]
+ * (16-byte aligned), dw [B][n_q][64], dk_i [B][n_kv][128] (overwritten).  The ReLU decision is taken on
+ * the codes' dot product in fp32 (the scales are positive).
+ */
+dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale, const void* k_i,
+                                         const float* k_i_scale, const float* w, const float* grad,
+                                         int64_t ld_grad, int B, int n_q, int n_kv, int H_I, int d_I,
+                                         dsa_dtype_t dtype, float* dq_i, float* dw, float* dk_i, void* stream);
+
 /* ------------------------------------------------------------------------------------------------
  * MQA-mode projections either side of dsa_sparse_mla_attn (velog summary, section 1.3: MLA in MQA
  * mode shares each latent entry across the query heads, so the key up-projection W_UK is absorbed

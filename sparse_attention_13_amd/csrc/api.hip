@@ -287,6 +287,24 @@ dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, in
                     "dsa_warmup_loss");
 }
 
+dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale, const void* k_i,
+                                         const float* k_i_scale, const float* w, const float* grad, int64_t ld_grad,
+                                         int B, int n_q, int n_kv, int H_I, int d_I, dsa_dtype_t dtype, float* dq_i,
+                                         float* dw, float* dk_i, void* stream) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_backward: bad sizes");
+  if (dtype != DSA_FP8_E4M3 || H_I != 64 || d_I != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "warmup_backward: supports fp8 e4m3 with H_I=64, d_I=128");
+  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "warmup_backward: grid too large");
+  if (!q_i || !q_i_scale || !k_i || !k_i_scale || !w || !grad || !dq_i || !dw || !dk_i)
+    return fail(DSA_ERR_INVALID_ARG, "warmup_backward: null pointer");
+  if (ld_grad < n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_backward: ld_grad below n_kv");
+  if (!(aligned(q_i, 16) && aligned(k_i, 16) && aligned(dq_i, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "warmup_backward: q_i, k_i and dq_i must be 16-byte aligned");
+  return hip_status(dsa::launch_warmup_backward((const uint8_t*)q_i, q_i_scale, (const uint8_t*)k_i, k_i_scale, w,
+                                                grad, ld_grad, B, n_q, n_kv, dq_i, dw, dk_i, (hipStream_t)stream),
+                    "dsa_warmup_indexer_backward");
+}
+
 dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa, int rows, int H, int d_nope,
                               int d_rope, int d_c, dsa_dtype_t dtype, void* stream) {
   if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "absorb_q: rows and H must be positive");

@@ -103,6 +103,11 @@ hipError_t launch_mla_out_proj(const uint16_t* o_lat, const uint16_t* w_uv, uint
 hipError_t launch_warmup_forward(const uint16_t* q, const uint16_t* kv, const float* lse, int B, int n_q, int n_kv,
                                  float sm_scale, float* scores, int64_t ld_s, float* p, int64_t ld_p, float* loss,
                                  hipStream_t stream);
+// Gradients of the warm-up loss through the fp8 indexer (H_I = 64, d_I = 128), given g [B][n_q][ld_g]:
+// dq [B][n_q][64][128], dw [B][n_q][64], dk [B][n_kv][128] fp32 (dk is zeroed, then accumulated).
+hipError_t launch_warmup_backward(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
+                                  const float* w, const float* g, int64_t ld_g, int B, int n_q, int n_kv, float* dq,
+                                  float* dw, float* dk, hipStream_t stream);
 // Masked MHA mode (bf16, d_qk = 192, d_v = 128): mask words per query row, and the two launches
 // (mask from the selection, then dense attention under it).  mask: [B][n_q][mha_mask_words(n_kv)] u32.
 int mha_mask_words(int n_kv);

@@ -12,6 +12,19 @@
 //                         lane-local plus one swap, then one LDS exchange across the waves.
 //   warmup_loss_kernel    per query row: lse_I of the index scores, loss_t = sum_s p (log p - log softmax(I)),
 //                         g = softmax(I) - p written over the scores.
+//   warmup_dq_kernel      gradients of the loss through I = sum_j w_j ReLU(q^_j . k^_s) for 4 queries per
+//                         workgroup (one per wave): dw[t][j] = sum_s g ReLU(d), dq^[t][j] = w_j sum_s g [d > 0] k^_s.
+//                         The key codes of a 32-key block are converted to bf16 (exact for e4m3) into LDS;
+//                         D^T = K . Q^T on the bf16 matrix core gives each lane one head and 16 keys, the
+//                         ReLU decision and g k_scale make M^T in registers, in the key order the second
+//                         product takes (as P^T in attention), and dq^T += K^T . M^T reads K^T through the
+//                         transposing LDS read.
+//   warmup_dk_kernel      dk^[s] = sum_t sum_j g w_j [d > 0] q^_j: the same two products with the roles of
+//                         queries and keys exchanged (128 keys per workgroup, one part of the queries; parts
+//                         are summed with atomics into dk, which a fill kernel zeroes first).
+// The ReLU decisions use d = q^ . k^ = q_scale k_scale (codes . codes), so the codes' dot product decides.
+#include <algorithm>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -162,6 +175,383 @@ __global__ __launch_bounds__(256) void warmup_loss_kernel(float* __restrict__ sc
   if (threadIdx.x == 0) loss[row] = kl;
 }
 
+
+// ---------------------------------------------------------------------------------------------- backward
+constexpr int kIH = 64;   // indexer heads
+constexpr int kID = 128;  // indexer head dim
+constexpr int kBKT = 32 * kID * 2;  // bf16 key tile of 32 rows: 8 KiB
+
+// 16-byte chunk swizzle of a 256-byte bf16 row: the fragment reads (16 rows, one chunk) and the
+// transposing reads (8 rows, four 8-byte units) both hit every bank once.
+__device__ __forceinline__ int cswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// 16 e4m3 codes -> 16 bf16 values (exact), as 8 packed pairs
+__device__ __forceinline__ void codes_to_bf16(const u32x4 c, unsigned int (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i], true);
+    o[2 * i] = pack_bf16x2(a[0], a[1]);
+    o[2 * i + 1] = pack_bf16x2(b[0], b[1]);
+  }
+}
+
+// Write one 16-code chunk (dims 16c .. 16c+15) of tile row r as bf16 chunks 2c, 2c+1 (swizzled).
+__device__ __forceinline__ void store_row_chunk(char* tile, int r, int c, const u32x4 codes) {
+  unsigned int o[8];
+  codes_to_bf16(codes, o);
+  char* rowp = tile + r * (kID * 2);
+  *(u32x4*)(rowp + 16 * ((2 * c) ^ cswz(r))) = (u32x4){o[0], o[1], o[2], o[3]};
+  *(u32x4*)(rowp + 16 * ((2 * c + 1) ^ cswz(r))) = (u32x4){o[4], o[5], o[6], o[7]};
+}
+
+// Transposing reads of a bf16 tile (256-byte rows): for the 16-row half at row r0, the A operand of
+// four 32-column blocks (as V^T in attention): out[db][0] rows r0 + 0..7, out[db][1] rows r0 + 8..15.
+// toff[db][rd]: the lane's byte offset for column block db and 8-row half rd (the swizzle differs).
+__device__ __forceinline__ void tr_frags(const char* tile, const int (&toff)[4][2], int r0, u32x2 (&vr)[4][2]) {
+  const char* base = tile + r0 * (kID * 2);
+  const unsigned int a0 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[0][0]);
+  const unsigned int a1 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[0][1]);
+  const unsigned int a2 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[1][0]);
+  const unsigned int a3 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[1][1]);
+  const unsigned int a4 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[2][0]);
+  const unsigned int a5 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[2][1]);
+  const unsigned int a6 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[3][0]);
+  const unsigned int a7 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[3][1]);
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vr[0][0]), "=&v"(vr[0][1]), "=&v"(vr[1][0]), "=&v"(vr[1][1]), "=&v"(vr[2][0]), "=&v"(vr[2][1]),
+        "=&v"(vr[3][0]), "=&v"(vr[3][1])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7));
+}
+
+// Lane offsets for tr_frags: rows 8rd + 4(G>>1) + (j>>2), columns 32db + 16(G&1) + 4(j&3) (G = l/16, j = l%16).
+__device__ __forceinline__ void tr_offsets(int lane, int (&toff)[4][2]) {
+  const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int rd = 0; rd < 2; rd++) {
+    const int r = 8 * rd + 4 * (G >> 1) + (j >> 2);  // r0 (a multiple of 16) does not change cswz
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+      const int c = 4 * db + 2 * (G & 1) + ((j & 3) >> 1);
+      toff[db][rd] = r * (kID * 2) + 16 * (c ^ cswz(r)) + 8 * (j & 1);
+    }
+  }
+}
+
+// A-operand fragment offset (row l%32 of a 32-row block, k-step ks of 16 dims) in a bf16 tile.
+__device__ __forceinline__ int frag_offset(int lane, int ks) {
+  const int r = lane & 31;
+  return r * (kID * 2) + 16 * ((2 * ks + (lane >> 5)) ^ cswz(r));
+}
+
+__device__ __forceinline__ float relu_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+__global__ __launch_bounds__(256, 1) void warmup_dq_kernel(const uint8_t* __restrict__ q8, const float* __restrict__ qs,
+                                                           const uint8_t* __restrict__ k8, const float* __restrict__ ks,
+                                                           const float* __restrict__ w, const float* __restrict__ g,
+                                                           int64_t ld_g, int n_q, int n_kv, int n_quad,
+                                                           float* __restrict__ dq, float* __restrict__ dw) {
+  __shared__ __attribute__((aligned(1024))) char kt0[kBKT];
+  __shared__ __attribute__((aligned(1024))) char kt1[kBKT];
+  __shared__ __attribute__((aligned(16))) float gk0[4][32];
+  __shared__ __attribute__((aligned(16))) float gk1[4][32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int quad = n_quad - 1 - (int)blockIdx.x;  // longest rows first
+  const int b = blockIdx.y;
+  const int t0 = 4 * quad;
+  const int t = min(t0 + wave, n_q - 1);
+  const int pos_last = n_kv - n_q + min(t0 + 3, n_q - 1);
+  const int n_blk = pos_last / 32 + 1;
+  const size_t row = (size_t)b * n_q + t;
+  const uint8_t* kb = k8 + (size_t)b * n_kv * kID;
+  const float* ksb = ks + (size_t)b * n_kv;
+
+  // Q^T (B operand of D^T = K . Q^T): lane holds head 32hb + l%32, dims 16ks + 8(l/32) .. +8, as bf16
+  v8bf qf[2][kID / 16];
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    const uint8_t* qp = q8 + (row * kIH + 32 * hb + (lane & 31)) * kID + 8 * (lane >> 5);
+#pragma unroll
+    for (int k2 = 0; k2 < kID / 32; k2++) {
+      // dims 32 k2 + 8(l/32) .. +8 and 32 k2 + 16 + 8(l/32) .. +8: two k-steps from two 8-byte loads
+      const u32x2 c0 = *(const u32x2*)(qp + 32 * k2);
+      const u32x2 c1 = *(const u32x2*)(qp + 32 * k2 + 16);
+      unsigned int o[8];
+      codes_to_bf16((u32x4){c0[0], c0[1], c1[0], c1[1]}, o);
+      qf[hb][2 * k2] = __builtin_bit_cast(v8bf, (u32x4){o[0], o[1], o[2], o[3]});
+      qf[hb][2 * k2 + 1] = __builtin_bit_cast(v8bf, (u32x4){o[4], o[5], o[6], o[7]});
+    }
+  }
+  int koff[kID / 16], toff[4][2];
+#pragma unroll
+  for (int k = 0; k < kID / 16; k++) koff[k] = frag_offset(lane, k);
+  tr_offsets(lane, toff);
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+  float dwa[2] = {0.f, 0.f};
+
+  // staging of block i: thread -> key row tid/8, codes 16 (tid%8) .. +16; threads < 128 also fetch
+  // g k_scale of (query tid/32, key tid%32), zero past the query's position
+  const int st_r = tid >> 3, st_c = tid & 7;
+  u32x4 st_codes;
+  float st_gk = 0.f;
+  auto stage_load = [&](int i) {
+    const int s = min(32 * i + st_r, n_kv - 1);
+    st_codes = *(const u32x4*)(kb + (size_t)s * kID + 16 * st_c);
+    if (tid < 128) {
+      const int qt = min(t0 + (tid >> 5), n_q - 1);
+      const int key = 32 * i + (tid & 31);
+      const int kc = min(key, n_kv - 1);
+      const float gv = g[((size_t)b * n_q + qt) * ld_g + min(kc, n_kv - n_q + qt)];
+      st_gk = (key <= n_kv - n_q + qt) ? gv * ksb[kc] : 0.f;
+    }
+  };
+  auto stage_store = [&](char* tile, float (*gk)[32]) {
+    store_row_chunk(tile, st_r, st_c, st_codes);
+    if (tid < 128) gk[tid >> 5][tid & 31] = st_gk;
+  };
+
+  auto block = [&](const char* tile, float (*gk)[32]) {
+    // D^T[key][head] for the wave's query: lane = head 32hb + l%32, value r = key 8(r/4) + 4(l/32) + r%4
+    v16f d[2];
+#pragma unroll
+    for (int k = 0; k < kID / 16; k++) {
+      const v8bf kf = *(const v8bf*)(tile + koff[k]);
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++)
+        d[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[hb][k], k == 0 ? (v16f){} : d[hb], 0, 0, 0);
+    }
+    float gkv[16];
+#pragma unroll
+    for (int qd = 0; qd < 4; qd++) {
+      const v4f v = *(const v4f*)(&gk[wave][8 * qd + 4 * (lane >> 5)]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) gkv[4 * qd + e] = v[e];
+    }
+    unsigned int pk[2][8];
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++) {
+      float m[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        dwa[hb] = fmaf(gkv[r], relu_f(d[hb][r]), dwa[hb]);
+        m[r] = d[hb][r] > 0.f ? gkv[r] : 0.f;
+      }
+#pragma unroll
+      for (int g8 = 0; g8 < 8; g8++) pk[hb][g8] = pack_bf16x2(m[2 * g8], m[2 * g8 + 1]);
+    }
+    // dq^T[dim][head] += K^T[dim][keys] . M^T[keys][head], two 16-key halves
+#pragma unroll
+    for (int kh = 0; kh < 2; kh++) {
+      u32x2 vr[4][2];
+      tr_frags(tile, toff, 16 * kh, vr);
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        const v8bf mf = __builtin_bit_cast(v8bf, (u32x4){pk[hb][4 * kh], pk[hb][4 * kh + 1], pk[hb][4 * kh + 2],
+                                                         pk[hb][4 * kh + 3]});
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const v8bf kf = __builtin_bit_cast(v8bf, (u32x4){vr[db][0][0], vr[db][0][1], vr[db][1][0], vr[db][1][1]});
+          acc[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, mf, acc[db][hb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  stage_load(0);
+  stage_store(kt0, gk0);
+  stage_load(1);
+  __syncthreads();
+  for (int i = 0; i < n_blk; i += 2) {
+    stage_store(kt1, gk1);  // block i+1 (its buffers were last read in block i-1)
+    stage_load(i + 2);
+    block(kt0, gk0);
+    __syncthreads();
+    stage_store(kt0, gk0);  // block i+2
+    stage_load(i + 3);
+    if (i + 1 < n_blk) block(kt1, gk1);
+    __syncthreads();
+  }
+
+  if (t0 + wave < n_q) {
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++) {
+      const int h = 32 * hb + (lane & 31);
+      const float wh = w[row * kIH + h];
+      float* dqp = dq + (row * kIH + h) * kID + 4 * (lane >> 5);
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int qd = 0; qd < 4; qd++)
+          *(v4f*)(dqp + 32 * db + 8 * qd) = (v4f){acc[db][hb][4 * qd] * wh, acc[db][hb][4 * qd + 1] * wh,
+                                                  acc[db][hb][4 * qd + 2] * wh, acc[db][hb][4 * qd + 3] * wh};
+      const float dsum = xor32_sum(dwa[hb]);
+      if (lane < 32) dw[row * kIH + h] = dsum * qs[row * kIH + h];
+    }
+  }
+}
+
+
+constexpr int kQT = kIH * kID * 2;  // bf16 query tile: 64 heads x 128 dims, 16 KiB
+
+__global__ __launch_bounds__(256, 1) void warmup_dk_kernel(const uint8_t* __restrict__ q8, const float* __restrict__ qs,
+                                                           const uint8_t* __restrict__ k8, const float* __restrict__ w,
+                                                           const float* __restrict__ g, int64_t ld_g, int n_q,
+                                                           int n_kv, int n_split, float* __restrict__ dk) {
+  __shared__ __attribute__((aligned(1024))) char qt0[kQT];
+  __shared__ __attribute__((aligned(1024))) char qt1[kQT];
+  __shared__ __attribute__((aligned(16))) float cf0[kIH], cf1[kIH];  // w q_scale per head
+  __shared__ float gq0[128], gq1[128];                                // g of the workgroup's keys
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s_base = 128 * blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int off = n_kv - n_q;  // pos_t = t + off
+  const int t_first = max(0, s_base - off);
+  const int span = n_q - t_first;
+  if (span <= 0) return;  // whole workgroup: no query sees these keys
+  const int per = (span + n_split - 1) / n_split;
+  const int t_lo = t_first + split * per, t_hi = min(n_q, t_lo + per);
+  if (t_lo >= t_hi) return;
+  const int s_lane = s_base + 32 * wave + (lane & 31);
+
+  // K (B operand of D = Q . K^T): lane holds key s_lane, dims 16ks + 8(l/32) .. +8, as bf16
+  v8bf kf[kID / 16];
+  {
+    const uint8_t* kp = k8 + ((size_t)b * n_kv + min(s_lane, n_kv - 1)) * kID + 8 * (lane >> 5);
+#pragma unroll
+    for (int k2 = 0; k2 < kID / 32; k2++) {
+      const u32x2 c0 = *(const u32x2*)(kp + 32 * k2);
+      const u32x2 c1 = *(const u32x2*)(kp + 32 * k2 + 16);
+      unsigned int o[8];
+      codes_to_bf16((u32x4){c0[0], c0[1], c1[0], c1[1]}, o);
+      kf[2 * k2] = __builtin_bit_cast(v8bf, (u32x4){o[0], o[1], o[2], o[3]});
+      kf[2 * k2 + 1] = __builtin_bit_cast(v8bf, (u32x4){o[4], o[5], o[6], o[7]});
+    }
+  }
+  int qoff[kID / 16], toff[4][2];
+#pragma unroll
+  for (int k = 0; k < kID / 16; k++) qoff[k] = frag_offset(lane, k);
+  tr_offsets(lane, toff);
+  v16f acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
+
+  // staging of query t: thread -> head row tid/4, codes 32 (tid%4) .. +32; threads < 64 the head's
+  // w q_scale; threads 64..191 g of key s_base + tid - 64 (zero past t's position)
+  const int st_h = tid >> 2, st_c = tid & 3;
+  u32x4 st_a, st_b;
+  float st_v = 0.f;
+  auto stage_load = [&](int t) {
+    const size_t row = (size_t)b * n_q + t;
+    const uint8_t* qp = q8 + (row * kIH + st_h) * kID + 32 * st_c;
+    st_a = *(const u32x4*)qp;
+    st_b = *(const u32x4*)(qp + 16);
+    if (tid < kIH) {
+      st_v = w[row * kIH + tid] * qs[row * kIH + tid];
+    } else if (tid < kIH + 128) {
+      const int s = s_base + tid - kIH;
+      const int pos = t + off;
+      const float gv = g[row * ld_g + min(s, pos)];
+      st_v = (s <= pos) ? gv : 0.f;
+    }
+  };
+  auto stage_store = [&](char* tile, float* cf, float* gq) {
+    store_row_chunk(tile, st_h, 2 * st_c, st_a);
+    store_row_chunk(tile, st_h, 2 * st_c + 1, st_b);
+    if (tid < kIH) cf[tid] = st_v;
+    else if (tid < kIH + 128) gq[tid - kIH] = st_v;
+  };
+  auto query = [&](const char* tile, const float* cf, const float* gq) {
+    // D[head][key]: lane = key s_lane, value r of block hb = head 32hb + 8(r/4) + 4(l/32) + r%4
+    v16f d[2];
+#pragma unroll
+    for (int k = 0; k < kID / 16; k++)
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        const v8bf qf = *(const v8bf*)(tile + hb * 32 * (kID * 2) + qoff[k]);
+        d[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[k], k == 0 ? (v16f){} : d[hb], 0, 0, 0);
+      }
+    const float gv = gq[32 * wave + (lane & 31)];
+    unsigned int pk[2][8];
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++) {
+      float cv[16];
+#pragma unroll
+      for (int qd = 0; qd < 4; qd++) {
+        const v4f v = *(const v4f*)(cf + 32 * hb + 8 * qd + 4 * (lane >> 5));
+#pragma unroll
+        for (int e = 0; e < 4; e++) cv[4 * qd + e] = v[e];
+      }
+      float m[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) m[r] = d[hb][r] > 0.f ? gv * cv[r] : 0.f;
+#pragma unroll
+      for (int g8 = 0; g8 < 8; g8++) pk[hb][g8] = pack_bf16x2(m[2 * g8], m[2 * g8 + 1]);
+    }
+    // dk^T[dim][key] += Q^T[dim][heads] . N[heads][key], four 16-head halves
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+      for (int kh = 0; kh < 2; kh++) {
+        u32x2 vr[4][2];
+        tr_frags(tile, toff, 32 * hb + 16 * kh, vr);
+        const v8bf nf = __builtin_bit_cast(v8bf, (u32x4){pk[hb][4 * kh], pk[hb][4 * kh + 1], pk[hb][4 * kh + 2],
+                                                         pk[hb][4 * kh + 3]});
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const v8bf qf = __builtin_bit_cast(v8bf, (u32x4){vr[db][0][0], vr[db][0][1], vr[db][1][0], vr[db][1][1]});
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, nf, acc[db], 0, 0, 0);
+        }
+      }
+  };
+
+  stage_load(t_lo);
+  stage_store(qt0, cf0, gq0);
+  stage_load(min(t_lo + 1, t_hi - 1));
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; t += 2) {
+    stage_store(qt1, cf1, gq1);  // query t+1 (its buffers were last read for query t-1)
+    stage_load(min(t + 2, t_hi - 1));
+    query(qt0, cf0, gq0);
+    __syncthreads();
+    stage_store(qt0, cf0, gq0);  // query t+2
+    stage_load(min(t + 3, t_hi - 1));
+    if (t + 1 < t_hi) query(qt1, cf1, gq1);
+    __syncthreads();
+  }
+  if (s_lane < n_kv) {
+    float* dkp = dk + ((size_t)b * n_kv + s_lane) * kID + 4 * (lane >> 5);
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int qd = 0; qd < 4; qd++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) atomicAdd(dkp + 32 * db + 8 * qd + e, acc[db][4 * qd + e]);
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) x[i] = 0.f;
+}
+
 }  // namespace
 
 hipError_t launch_warmup_forward(const uint16_t* q, const uint16_t* kv, const float* lse, int B, int n_q, int n_kv,
@@ -176,4 +566,27 @@ hipError_t launch_warmup_forward(const uint16_t* q, const uint16_t* kv, const fl
   return hipGetLastError();
 }
 
+hipError_t launch_warmup_backward(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
+                                  const float* w, const float* g, int64_t ld_g, int B, int n_q, int n_kv, float* dq,
+                                  float* dw, float* dk, hipStream_t stream) {
+  const int n_quad = (n_q + 3) / 4;
+  hipLaunchKernelGGL(warmup_dq_kernel, dim3(n_quad, B), dim3(256), 0, stream, q8, qs, k8, ks, w, g, ld_g, n_q, n_kv,
+                     n_quad, dq, dw);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n_dk = (size_t)B * n_kv * kID;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>((n_dk + 255) / 256, 4096)), dim3(256), 0, stream,
+                     dk, n_dk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // parts of the query range per key block: about 512 workgroups in all, at least 8 queries each
+  const int n_kblk = (n_kv + 127) / 128;
+  int n_split = (512 + n_kblk * B - 1) / (n_kblk * B);
+  n_split = std::max(1, std::min(n_split, n_q / 8));
+  hipLaunchKernelGGL(warmup_dk_kernel, dim3(n_kblk, n_split, B), dim3(256), 0, stream, q8, qs, k8, w, g, ld_g, n_q,
+                     n_kv, n_split, dk);
+  return hipGetLastError();
+}
+
 }  // namespace dsa
+

@@ -40,6 +40,7 @@ SIGNATURES = {
     "dsa_masked_mha_attn": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
     "dsa_masked_mha_workspace_size": ([_I, _I, _I], _SZ),
     "dsa_warmup_loss": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64, _P, _I64, _P, _P], _I),
+    "dsa_warmup_indexer_backward": ([_P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "dsa_mla_absorb_q": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "dsa_mla_out_proj": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
 }
@@ -206,6 +207,21 @@ def warmup_loss(q, kv, lse, scores, sm_scale: float, target=None, loss=None, str
                                  _ptr(scores), scores.shape[-1], _ptr(target), target.shape[-1], _ptr(loss),
                                  _stream(stream)))
     return loss, target
+
+
+def warmup_indexer_backward(q_i, q_i_scale, k_i, k_i_scale, w, grad, stream=None):
+    """Gradients of the warm-up loss through the fp8 indexer, given grad = dL/dI [B, n_q, ld] (f32).
+    Returns (dq_i [B, n_q, 64, 128], dw [B, n_q, 64], dk_i [B, n_kv, 128]) f32."""
+    _dev(q_i, q_i_scale, k_i, k_i_scale, w, grad)
+    B, nq, H_I, d_I = q_i.shape
+    n_kv = k_i.shape[1]
+    dq = torch.empty((B, nq, H_I, d_I), dtype=torch.float32, device=q_i.device)
+    dw = torch.empty((B, nq, H_I), dtype=torch.float32, device=q_i.device)
+    dk = torch.empty((B, n_kv, d_I), dtype=torch.float32, device=q_i.device)
+    _check(lib().dsa_warmup_indexer_backward(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w),
+                                             _ptr(grad), grad.shape[-1], B, nq, n_kv, H_I, d_I, _dtype_code(q_i),
+                                             _ptr(dq), _ptr(dw), _ptr(dk), _stream(stream)))
+    return dq, dw, dk
 
 
 def mla_absorb_q(q_mha, w_ukt, q_mqa=None, stream=None):

@@ -192,6 +192,40 @@ def test_projection_validation(L):
     assert a(FAKE, FAKE, FAKE2, 2**30, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_UNSUPPORTED    # grid
 
 
+def test_warmup_validation(L):
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_FP8_E4M3
+    f = L.dsa_warmup_loss
+    ok = [FAKE, FAKE, FAKE, 1, 64, 100, 128, 576, 0.04, DSA_BF16, FAKE2, 100, FAKE2, 100, FAKE2, None]
+    a = list(ok); a[4] = 101
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # n_q > n_kv
+    a = list(ok); a[6] = 64
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # H other than 128
+    a = list(ok); a[11] = 99
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # ld_scores < n_kv
+    a = list(ok); a[8] = float("inf")
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # non-finite scale
+    a = list(ok); a[1] = ctypes.c_void_p(0x10008)
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned kv
+    a = list(ok); a[3] = 70000
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # grid
+    b = L.dsa_warmup_indexer_backward
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 64, 100, 64, 128, DSA_FP8_E4M3, FAKE2, FAKE2, FAKE2, None]
+    a = list(ok); a[8] = 0
+    assert b(*a) == DSA_ERR_INVALID_ARG                              # no queries
+    a = list(ok); a[10] = 32
+    assert b(*a) == DSA_ERR_UNSUPPORTED                              # H_I other than 64
+    a = list(ok); a[12] = DSA_BF16
+    assert b(*a) == DSA_ERR_UNSUPPORTED                              # fp8 only
+    a = list(ok); a[5] = None
+    assert b(*a) == DSA_ERR_INVALID_ARG                              # null grad
+    a = list(ok); a[6] = 99
+    assert b(*a) == DSA_ERR_INVALID_ARG                              # ld_grad < n_kv
+    a = list(ok); a[13] = ctypes.c_void_p(0x20004)
+    assert b(*a) == DSA_ERR_INVALID_ARG                              # misaligned dq_i
+    a = list(ok); a[7] = 70000
+    assert b(*a) == DSA_ERR_UNSUPPORTED                              # grid
+
+
 def test_forward_validation(L):
     from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_WORKSPACE, DSA_FP8_E4M3
     n_q, n_kv, k = 64, 100, 32

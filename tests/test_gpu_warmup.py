@@ -76,3 +76,88 @@ def test_warmup_loss_vs_oracle(orc, dsa, B, L, n_q):
             sm_i = g_o[r, :n] + p_o[r, :n]
             assert np.all(np.abs(gs[b, r, :n] - g_o[r, :n]) <= 2e-3 * (sm_i + p_o[r, :n]) + 1e-7), (b, r)
         np.testing.assert_allclose(gl[b], l_o, rtol=2e-3, atol=1e-5)
+
+
+def backward_bounds(orc, xi, b, g, pos):
+    """Sums of the magnitudes of every term of dq, dw and dk (float64), from the dequantised inputs: the
+    scale of the rounding of each term (bf16 operands of the second products, fp32 accumulation)."""
+    qh = orc.dequant_e4m3(xi["q8"][b].numpy(), xi["qs"][b].numpy()).astype(np.float64)
+    kh = orc.dequant_e4m3(xi["k8"][b].numpy(), xi["ks"][b].numpy()).astype(np.float64)
+    w = xi["w"][b].numpy().astype(np.float64)
+    S = kh.shape[0]
+    d = np.einsum("rhd,sd->rhs", qh, kh)
+    vis = np.arange(S)[None, :] <= pos[:, None]
+    ga = np.where(vis, np.abs(g[:, :S].astype(np.float64)), 0.0)
+    on = (d > 0) * ga[:, None, :]                                   # [R, H, S]: |g| [d > 0]
+    bq = np.einsum("rhs,sd->rhd", on, np.abs(kh)) * np.abs(w)[:, :, None]
+    bw = np.einsum("rhs,rhs->rh", on, np.maximum(d, 0))
+    bk = np.einsum("rhs,rhd->sd", on * np.abs(w)[:, :, None], np.abs(qh))
+    return bq, bw, bk
+
+
+def run_backward(dsa, xi, g):
+    return [t.cpu().numpy() for t in dsa.warmup_indexer_backward(
+        xi["q8"].to(DEV), xi["qs"].to(DEV), xi["k8"].to(DEV), xi["ks"].to(DEV), xi["w"].to(DEV), g.to(DEV))]
+
+
+# several key blocks and query parts with ragged ends, fewer queries than keys, fewer than 8 queries
+@pytest.mark.parametrize("B,L,n_q,exact", [(2, 256, 256, True), (1, 333, 100, True), (1, 70, 3, True),
+                                           (1, 600, 600, True), (2, 300, 170, False), (1, 129, 129, False)])
+def test_warmup_backward_vs_oracle(orc, dsa, B, L, n_q, exact):
+    """dq, dw and dk against the oracle.  With exact=True, g holds multiples of 2^-10 below 2^-5: every
+    bf16 operand and every product is then exact and only the fp32 summation order differs (the bound is
+    2^-20 of the sum of the terms' magnitudes).  Otherwise g is a general float: the second products round
+    g k_scale and g w q_scale to bf16 (relative error at most 2^-9 per term), so the bound is 2^-8 of that
+    sum.  dw is an fp32 sum of exact products in both cases.  Entries of g past each query's position are
+    NaN and must not be read."""
+    xi = exact_indexer_inputs(B, L, n_q, seed=3 * L + n_q)
+    gen = torch.Generator().manual_seed(L + 7)
+    ld = L + 3
+    if exact:
+        g = torch.randint(-31, 32, (B, n_q, ld), generator=gen).float() / 1024.0
+    else:
+        g = torch.randn((B, n_q, ld), generator=gen) * 1e-3
+    pos = np.arange(L - n_q, L, dtype=np.int64)
+    for r, p in enumerate(pos):
+        g[:, r, p + 1:] = float("nan")
+    dq, dw, dk = run_backward(dsa, xi, g)
+    rel = 2.0 ** -20 if exact else 2.0 ** -8
+    for b in range(B):
+        gb = g[b].numpy()
+        q_o, w_o, k_o = orc.warmup_backward(orc.dequant_e4m3(xi["q8"][b].numpy(), xi["qs"][b].numpy()),
+                                            xi["w"][b].numpy(),
+                                            orc.dequant_e4m3(xi["k8"][b].numpy(), xi["ks"][b].numpy()),
+                                            np.nan_to_num(gb, nan=0.0), pos)
+        bq, bw, bk = backward_bounds(orc, xi, b, np.nan_to_num(gb, nan=0.0), pos)
+        assert np.all(np.abs(dq[b] - q_o) <= rel * bq + 1e-30), (b, np.max(np.abs(dq[b] - q_o) - rel * bq))
+        assert np.all(np.abs(dw[b] - w_o) <= 2.0 ** -20 * bw + 1e-30), (b, np.max(np.abs(dw[b] - w_o)))
+        assert np.all(np.abs(dk[b] - k_o) <= rel * bk + 1e-30), (b, np.max(np.abs(dk[b] - k_o) - rel * bk))
+        assert np.abs(q_o).max() > 0 and np.abs(k_o).max() > 0
+
+
+def test_warmup_backward_full_8k(orc, dsa):
+    """8192 queries over 8192 keys, the benchmark's launch configuration: dq and dw on sampled query rows,
+    dk on sampled keys (each as a one-key problem over every query that sees it).  Exact inputs as above."""
+    L = 8192
+    xi = exact_indexer_inputs(1, L, L, seed=81)
+    g = torch.randint(-31, 32, (1, L, L), generator=torch.Generator().manual_seed(82)).float() / 1024.0
+    dq, dw, dk = run_backward(dsa, xi, g)
+    qh = orc.dequant_e4m3(xi["q8"][0].numpy(), xi["qs"][0].numpy())
+    kh = orc.dequant_e4m3(xi["k8"][0].numpy(), xi["ks"][0].numpy())
+    w, gb = xi["w"][0].numpy(), g[0].numpy()
+    rows = np.array([0, 1, 31, 32, 127, 2048, 4097, 8000, 8190, 8191])
+    q_o, w_o, _ = orc.warmup_backward(qh[rows], w[rows], kh, gb[rows], rows.astype(np.int64))
+    d = np.matmul(qh[rows].astype(np.float64), kh.T.astype(np.float64))        # [rows, 64, 8192]
+    on = (d > 0) * np.where(np.arange(L)[None, :] <= rows[:, None], np.abs(gb[rows]), 0.0)[:, None, :]
+    bq = np.matmul(on, np.abs(kh).astype(np.float64)) * np.abs(w[rows])[:, :, None]
+    bw = np.sum(on * np.maximum(d, 0), axis=2)
+    assert np.all(np.abs(dq[0][rows] - q_o) <= 2.0 ** -20 * bq + 1e-30)
+    assert np.all(np.abs(dw[0][rows] - w_o) <= 2.0 ** -20 * bw + 1e-30)
+    for s in (0, 1, 127, 128, 3000, 8191):
+        t = np.arange(s, L)
+        _, _, k_o = orc.warmup_backward(qh[t], w[t], kh[s:s + 1], gb[t][:, s:s + 1].copy(),
+                                        np.zeros(len(t), np.int64))
+        dts = np.matmul(qh[t], kh[s])                                            # [T, 64]
+        wt = (dts > 0) * np.abs(gb[t, s])[:, None] * np.abs(w[t])
+        bk = np.einsum("th,thd->d", wt.astype(np.float64), np.abs(qh[t]).astype(np.float64))
+        assert np.all(np.abs(dk[0][s] - k_o[0]) <= 2.0 ** -20 * bk + 1e-30), s
