@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--no-proj", action="store_true", help="skip the MQA-mode projection measurement")
+    ap.add_argument("--no-warmup-loss", action="store_true", help="skip the indexer warm-up loss measurement")
     ap.add_argument("--mha-lens", default="4096,8192,12288,16384",
                     help="prefill lengths of the masked-MHA vs sparse-MQA attention sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -284,7 +285,70 @@ def main():
         out["masked_mha"] = masked_mha_sweep([int(v) for v in args.mha_lens.split(",")], k, dev, stream)
     if args.only in (None, "prefill") and not args.no_proj:
         out["mla_projections"] = projections_bench(args.prefill_len, dev, stream)
+    if args.only in (None, "prefill") and not args.no_warmup_loss:
+        out["warmup_loss"] = warmup_bench(args.prefill_len, dev, stream)
     print(json.dumps(out), flush=True)
+
+
+def warmup_bench(L, dev, stream):
+    """One indexer warm-up step on a prefill of L tokens: index scores (fp8), the loss (target from the main
+    attention: 128 heads x 576 over every causal pair, bf16; KL; gradient) and the gradients through the
+    indexer (dq, dw: 2 x 64 x 128 x 2 flop per pair; dk the same).  The main attention's log-sum-exp is an
+    input (the frozen main model's dense forward pass produces it), made beforehand with the attention kernel
+    over the full causal selection."""
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    print(f"[bench] indexer warm-up step at {L} tokens", file=sys.stderr, flush=True)
+    x = synth.prefill(L, seed=0, device=dev, n_needles=max(1, L // 128), needle_layout="random")
+    pos = torch.arange(L, device=dev)[:, None]
+    s_ = torch.arange(L, device=dev)[None, :]
+    idx = torch.where(s_ <= pos, s_, torch.full_like(s_, -1)).to(torch.int32)[None]
+    del pos, s_
+    _, lse = dsa.sparse_mla_attn(x["q"][None], x["kv"][None], idx, 512, x["sm_scale"])
+    del idx
+    torch.cuda.empty_cache()
+    scores = torch.empty((1, L, L), dtype=torch.float32, device=dev)
+    target = torch.empty_like(scores)
+    loss = torch.empty((1, L), dtype=torch.float32, device=dev)
+    dq = torch.empty((1, L, 64, 128), dtype=torch.float32, device=dev)
+    dw = torch.empty((1, L, 64), dtype=torch.float32, device=dev)
+    dk = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ts = [[], [], []]
+    for rep in range(6):
+        ev[0].record(stream)
+        dsa.indexer_scores(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None], scores)
+        ev[1].record(stream)
+        dsa.warmup_loss(x["q"][None], x["kv"][None], lse, scores, x["sm_scale"], target=target, loss=loss)
+        ev[2].record(stream)
+        dsa.warmup_indexer_backward(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None],
+                                    x["w"][None], scores, dq=dq, dw=dw, dk=dk)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            for i in range(3):
+                ts[i].append(ev[i].elapsed_time(ev[i + 1]))
+    t_i, t_l, t_b = (sorted(v)[len(v) // 2] for v in ts)
+    pairs = L * (L + 1) // 2
+    tgt_flop = pairs * 2 * 128 * 576
+    bwd_flop = pairs * 2 * (2 * 64 * 128 * 2)
+    res = {"workload": f"1x{L} tokens, dense causal; indexer 64x128 fp8, main attention 128 heads x 576 bf16",
+           "ms": round(t_i + t_l + t_b, 4),
+           "stages_ms": {"indexer": round(t_i, 4), "loss": round(t_l, 4), "backward": round(t_b, 4)},
+           "tokens_per_s": round(L / ((t_i + t_l + t_b) * 1e-3), 1),
+           "indexer_TFLOP/s": round(pairs * IDX_FLOP_PER_PAIR / (t_i * 1e-3) / 1e12, 1),
+           "loss_target_TFLOP/s": round(tgt_flop / (t_l * 1e-3) / 1e12, 1),
+           "backward_TFLOP/s": round(bwd_flop / (t_b * 1e-3) / 1e12, 1)}
+    res["roofline"] = {"bound": "mfma", "kernel": "loss (target product)", "achieved": res["loss_target_TFLOP/s"],
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(res["loss_target_TFLOP/s"] / PEAK_BF16_TFLOPS, 4)}
+    res["backward_roofline"] = {"bound": "mfma", "achieved": res["backward_TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(res["backward_TFLOP/s"] / PEAK_BF16_TFLOPS, 4)}
+    del x, lse, scores, target, loss, dq, dw, dk
+    torch.cuda.empty_cache()
+    return res
 
 
 def projections_bench(L, dev, stream):

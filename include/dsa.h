@@ -174,7 +174,7 @@ size_t dsa_masked_mha_workspace_size(int B, int n_q, int n_kv);
  * aligned), lse [B][n_q][H] fp32; scores [B][n_q][ld_scores] fp32 holds the index scores I on entry
  * (as dsa_indexer_scores writes them) and the gradient on return; target [B][n_q][ld_target] fp32
  * receives the target; loss [B][n_q] fp32.  Entries past pos_t are neither read nor written.
- * bf16 with H = 128 and d_qk = 576 only.
+ * bf16 with H = 128 and d_qk = 576 only, n_kv <= 2^21 (DSA_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------------ */
 dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, int B, int n_q, int n_kv, int H,
                              int d_qk, float sm_scale, dsa_dtype_t dtype, float* scores, int64_t ld_scores,

@@ -277,7 +277,7 @@ dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, in
   if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: bad sizes");
   if (dtype != DSA_BF16 || H != 128 || d_qk != 576)
     return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: supports bf16 with H=128, d_qk=576 (got %d, %d)", H, d_qk);
-  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: grid too large");
+  if (B > 65535 || n_kv > (1 << 21)) return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: B <= 65535, n_kv <= 2^21");
   if (!q || !kv || !lse || !scores || !target || !loss) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: null pointer");
   if (ld_scores < n_kv || ld_target < n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: ld below n_kv");
   if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: sm_scale must be finite");
@@ -294,7 +294,7 @@ dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale
   if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_backward: bad sizes");
   if (dtype != DSA_FP8_E4M3 || H_I != 64 || d_I != 128)
     return fail(DSA_ERR_UNSUPPORTED, "warmup_backward: supports fp8 e4m3 with H_I=64, d_I=128");
-  if (B > 65535) return fail(DSA_ERR_UNSUPPORTED, "warmup_backward: grid too large");
+  if (B > 65535 || n_kv > (1 << 21)) return fail(DSA_ERR_UNSUPPORTED, "warmup_backward: B <= 65535, n_kv <= 2^21");
   if (!q_i || !q_i_scale || !k_i || !k_i_scale || !w || !grad || !dq_i || !dw || !dk_i)
     return fail(DSA_ERR_INVALID_ARG, "warmup_backward: null pointer");
   if (ld_grad < n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_backward: ld_grad below n_kv");

@@ -209,15 +209,18 @@ def warmup_loss(q, kv, lse, scores, sm_scale: float, target=None, loss=None, str
     return loss, target
 
 
-def warmup_indexer_backward(q_i, q_i_scale, k_i, k_i_scale, w, grad, stream=None):
+def warmup_indexer_backward(q_i, q_i_scale, k_i, k_i_scale, w, grad, dq=None, dw=None, dk=None, stream=None):
     """Gradients of the warm-up loss through the fp8 indexer, given grad = dL/dI [B, n_q, ld] (f32).
     Returns (dq_i [B, n_q, 64, 128], dw [B, n_q, 64], dk_i [B, n_kv, 128]) f32."""
-    _dev(q_i, q_i_scale, k_i, k_i_scale, w, grad)
+    _dev(q_i, q_i_scale, k_i, k_i_scale, w, grad, dq, dw, dk)
     B, nq, H_I, d_I = q_i.shape
     n_kv = k_i.shape[1]
-    dq = torch.empty((B, nq, H_I, d_I), dtype=torch.float32, device=q_i.device)
-    dw = torch.empty((B, nq, H_I), dtype=torch.float32, device=q_i.device)
-    dk = torch.empty((B, n_kv, d_I), dtype=torch.float32, device=q_i.device)
+    if dq is None:
+        dq = torch.empty((B, nq, H_I, d_I), dtype=torch.float32, device=q_i.device)
+    if dw is None:
+        dw = torch.empty((B, nq, H_I), dtype=torch.float32, device=q_i.device)
+    if dk is None:
+        dk = torch.empty((B, n_kv, d_I), dtype=torch.float32, device=q_i.device)
     _check(lib().dsa_warmup_indexer_backward(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w),
                                              _ptr(grad), grad.shape[-1], B, nq, n_kv, H_I, d_I, _dtype_code(q_i),
                                              _ptr(dq), _ptr(dw), _ptr(dk), _stream(stream)))

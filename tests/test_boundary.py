@@ -208,6 +208,8 @@ def test_warmup_validation(L):
     assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned kv
     a = list(ok); a[3] = 70000
     assert f(*a) == DSA_ERR_UNSUPPORTED                              # grid
+    a = list(ok); a[5] = (1 << 21) + 1; a[11] = a[13] = a[5]
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # 32-bit latent row offsets
     b = L.dsa_warmup_indexer_backward
     ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 64, 100, 64, 128, DSA_FP8_E4M3, FAKE2, FAKE2, FAKE2, None]
     a = list(ok); a[8] = 0

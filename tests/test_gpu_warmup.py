@@ -48,7 +48,7 @@ def dense_idx(L, n_q):
     return torch.where(s <= pos, s, torch.full_like(s, -1)).to(torch.int32)
 
 
-@pytest.mark.parametrize("B,L,n_q", [(2, 256, 256), (1, 333, 100)])
+@pytest.mark.parametrize("B,L,n_q", [(2, 256, 256), (1, 333, 100), (1, 150, 77)])  # odd n_q: a lone last query
 def test_warmup_loss_vs_oracle(orc, dsa, B, L, n_q):
     xi = exact_indexer_inputs(B, L, n_q, seed=L)
     xs = [synth.prefill(L, seed=10 + b, device=DEV, n_q=n_q) for b in range(B)]
