@@ -61,6 +61,7 @@ def _load():
         lib.oracle_warmup_target.argtypes = [P, P, I64, P, I, I, ctypes.c_double, P, I64]
         lib.oracle_warmup_loss.argtypes = [P, P, I64, P, I64, I64, P, P, I64]
         lib.oracle_warmup_backward.argtypes = [P, P, P, P, I64, P, I, I, I64, I64, P, P, P]
+        lib.oracle_sparse_attn_backward.argtypes = [P, P, P, I64, I, I, I, I, ctypes.c_double, P, I64, P, P, P]
         lib.oracle_threads.restype = I
         _lib = lib
     return _lib
@@ -266,3 +267,44 @@ def warmup_backward(q: np.ndarray, w: np.ndarray, k: np.ndarray, g: np.ndarray, 
                                    _p(dk))
     return dq, dw, dk
 
+
+
+def sparse_attn_backward(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, d_v: int, sm_scale: float,
+                         dout: np.ndarray):
+    """Gradients of the MQA-mode sparse attention (sparse training stage), all in double.
+
+    q [R, H, d_qk], kv [S, d_qk], dout [R, H, d_v] float32, idx [R, k] int32 (-1 skipped).
+    Returns (dq [R, H, d_qk], dkv [S, d_qk], pbar [R, k]) float64: dL/dq, dL/dkv (the key and value
+    gradients summed on the shared latent row) for dL/dout = dout, and the head mean of the attention
+    probabilities of each selected entry (the indexer's target in that stage)."""
+    q = _c(q, np.float32)
+    kv = _c(kv, np.float32)
+    idx = _c(idx, np.int32)
+    dout = _c(dout, np.float32)
+    R, H, d_qk = q.shape
+    S = kv.shape[0]
+    k = idx.shape[1]
+    assert idx.shape[0] == R and kv.shape[1] == d_qk and dout.shape == (R, H, d_v) and 0 < d_v <= d_qk
+    assert idx.size == 0 or idx.max() < S
+    dq = np.empty((R, H, d_qk), np.float64)
+    dkv = np.empty((S, d_qk), np.float64)
+    pbar = np.empty((R, k), np.float64)
+    _load().oracle_sparse_attn_backward(_p(q), _p(kv), _p(idx), R, H, d_qk, d_v, k, float(sm_scale), _p(dout), S,
+                                        _p(dq), _p(dkv), _p(pbar))
+    return dq, dkv, pbar
+
+
+def sparse_kl_loss(pbar: np.ndarray, idx: np.ndarray, scores: np.ndarray, pos: np.ndarray):
+    """The indexer loss of the sparse training stage: L_t = KL(p_t || softmax(I_t)) over s <= pos_t, with p_t
+    the head mean of the sparse attention (pbar on the selected entries, 0 elsewhere).
+
+    pbar [R, k] float64, idx [R, k] int32 (-1 skipped), scores [R, ld] float32.
+    Returns (loss [R], g [R, ld]) float64 with g = softmax(I) - p over s <= pos (0 past it)."""
+    pbar = _c(pbar, np.float64)
+    idx = _c(idx, np.int32)
+    R, ld = scores.shape
+    p = np.zeros((R, ld), np.float64)
+    for r in range(R):
+        ok = idx[r] >= 0
+        np.add.at(p[r], idx[r][ok], pbar[r][ok])
+    return warmup_loss(p, scores, pos)

@@ -22,7 +22,11 @@
  *   - top-k ties go to the lower index, -0 equals +0, rows with fewer than k candidates keep
  *     all of them, selections are emitted in ascending index order, padded with -1;
  *   - attention: K is the whole latent row (d_qk columns), V is its first d_v columns,
- *     softmax scale is an explicit argument; everything in double.
+ *     softmax scale is an explicit argument; everything in double;
+ *   - sparse training stage: the main model's gradient is the chain rule through that attention
+ *     (the key and value gradients add on the shared latent row); the indexer's target there is the
+ *     head mean of the sparse attention probabilities (zero outside the selection), and its loss keeps
+ *     the warm-up form, KL to the softmax of the index scores over every causal key.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC dsa_oracle.c -o liboracle.so -lm
  * OpenMP only distributes independent rows over threads; it changes no arithmetic.
@@ -389,3 +393,79 @@ void oracle_warmup_backward(const float* q, const float* w, const float* k, cons
   }
 }
 
+
+/* ---------------------------------------------------------------- sparse training backward
+ * Sparse training stage (velog summary, Continued Pre-Training, Stage 2): the whole main model trains
+ * through the top-k selection, so its gradient passes through the attention of oracle_sparse_attn only.
+ * Given dout = dL/dout for every (row, head), the chain rule through the softmax over the selected
+ * entries i (s_i = idx[r][i] != -1):
+ *   z_i   = sm_scale q . kv[s_i],   P_i = exp(z_i) / sum_j exp(z_j)
+ *   dP_i  = dout . kv[s_i][0:d_v]
+ *   dz_i  = P_i (dP_i - sum_j P_j dP_j)                      (softmax Jacobian)
+ *   dq    = sm_scale sum_i dz_i kv[s_i]
+ *   dkv[s_i][0:d_qk] += sm_scale dz_i q,   dkv[s_i][0:d_v] += P_i dout    (K and V share the row)
+ * The same stage trains the indexer alone, on its own loss; its target for row r is the head mean of
+ * the attention probabilities, pbar[r][i] = (1/H) sum_h P_i (0 for skipped entries).
+ * q [n_rows][H][d_qk], kv [n_kv][d_qk], idx [n_rows][k], dout [n_rows][H][d_v]; dq [n_rows][H][d_qk],
+ * dkv [n_kv][d_qk] (overwritten), pbar [n_rows][k]; all in double.  OpenMP threads each sum their rows'
+ * dkv terms apart and the partial sums are added at the end (only the order of the double sums differs).
+ */
+void oracle_sparse_attn_backward(const float* q, const float* kv, const int32_t* idx, int64_t n_rows, int H,
+                                 int d_qk, int d_v, int k, double sm_scale, const float* dout, int64_t n_kv,
+                                 double* dq, double* dkv, double* pbar) {
+  for (int64_t e = 0; e < n_kv * (int64_t)d_qk; e++) dkv[e] = 0.0;
+  for (int64_t e = 0; e < n_rows * (int64_t)k; e++) pbar[e] = 0.0;
+#pragma omp parallel
+  {
+    double* part = (double*)calloc((size_t)(n_kv * (int64_t)d_qk), sizeof(double));
+    double* z = (double*)malloc((size_t)k * sizeof(double));
+    double* dp = (double*)malloc((size_t)k * sizeof(double));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+    for (int64_t r = 0; r < n_rows; r++) {
+      for (int h = 0; h < H; h++) {
+        const float* qh = q + (r * H + h) * (int64_t)d_qk;
+        const float* doh = dout + (r * H + h) * (int64_t)d_v;
+        const int32_t* sel = idx + r * (int64_t)k;
+        double* dqh = dq + (r * H + h) * (int64_t)d_qk;
+        for (int e = 0; e < d_qk; e++) dqh[e] = 0.0;
+        double m = -INFINITY;
+        for (int i = 0; i < k; i++) {
+          if (sel[i] < 0) continue;
+          const float* c = kv + (int64_t)sel[i] * d_qk;
+          double dot = 0.0, dv = 0.0;
+          for (int e = 0; e < d_qk; e++) dot += (double)qh[e] * (double)c[e];
+          for (int e = 0; e < d_v; e++) dv += (double)doh[e] * (double)c[e];
+          z[i] = sm_scale * dot;
+          dp[i] = dv;
+          if (z[i] > m) m = z[i];
+        }
+        if (m == -INFINITY) continue;  /* nothing selected: no gradient */
+        double l = 0.0;
+        for (int i = 0; i < k; i++)
+          if (sel[i] >= 0) l += exp(z[i] - m);
+        double pdp = 0.0;  /* sum_j P_j dP_j */
+        for (int i = 0; i < k; i++)
+          if (sel[i] >= 0) pdp += exp(z[i] - m) / l * dp[i];
+        for (int i = 0; i < k; i++) {
+          if (sel[i] < 0) continue;
+          const double p = exp(z[i] - m) / l;
+          const double dz = p * (dp[i] - pdp);
+          const float* c = kv + (int64_t)sel[i] * d_qk;
+          double* acc = part + (int64_t)sel[i] * d_qk;
+          for (int e = 0; e < d_qk; e++) {
+            dqh[e] += sm_scale * dz * (double)c[e];
+            acc[e] += sm_scale * dz * (double)qh[e];
+          }
+          for (int e = 0; e < d_v; e++) acc[e] += p * (double)doh[e];
+#pragma omp atomic
+          pbar[r * k + i] += p / H;
+        }
+      }
+    }
+#pragma omp critical
+    for (int64_t e = 0; e < n_kv * (int64_t)d_qk; e++) dkv[e] += part[e];
+    free(part);
+    free(z);
+    free(dp);
+  }
+}

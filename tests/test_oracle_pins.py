@@ -539,6 +539,139 @@ def test_warmup_gradients_match_finite_differences(orc):
         assert abs(num(k, idx) - dk[idx]) < 1e-6 * max(1.0, abs(dk[idx])), ("dk", idx)
 
 
+def _sparse_idx(rng, R, S, k, pos):
+    """Distinct causal entries per row in random order, some rows padded with -1."""
+    idx = np.full((R, k), -1, np.int32)
+    for r, ps in enumerate(pos):
+        n = min(k, int(ps) + 1) - (r % 3 == 1)
+        idx[r, :n] = rng.choice(int(ps) + 1, size=n, replace=False)
+        rng.shuffle(idx[r])
+    return idx
+
+
+def test_sparse_backward_matches_autograd(orc):
+    """dq, dkv and the head mean of P against torch autograd of the same attention in double on the CPU
+    (gather of the selected latent rows, masked softmax, P V, L = sum dout . out)."""
+    rng = np.random.default_rng(70)
+    R, S, H, d_qk, d_v, k = 5, 13, 3, 10, 7, 6
+    q = rng.standard_normal((R, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((S, d_qk)).astype(np.float32)
+    dout = rng.standard_normal((R, H, d_v)).astype(np.float32)
+    pos = np.arange(S - R, S, dtype=np.int64)
+    idx = _sparse_idx(rng, R, S, k, pos)
+    sm = 0.41
+    dq, dkv, pbar = orc.sparse_attn_backward(q, kv, idx, d_v, sm, dout)
+    qt = torch.from_numpy(q).double().requires_grad_(True)
+    kvt = torch.from_numpy(kv).double().requires_grad_(True)
+    it = torch.from_numpy(idx).long()
+    rows = kvt[it.clamp(min=0)]                                   # [R, k, d_qk]
+    logits = torch.einsum("rhd,rkd->rhk", qt, rows) * sm
+    logits = logits.masked_fill((it < 0)[:, None, :], -math.inf)
+    prob = torch.softmax(logits, dim=-1)
+    out = torch.einsum("rhk,rkd->rhd", prob, rows[:, :, :d_v])
+    (out * torch.from_numpy(dout).double()).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dkv, kvt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(pbar, prob.mean(dim=1).detach().numpy(), rtol=1e-12, atol=1e-15)
+    # the forward these gradients belong to is the (separately pinned) oracle attention
+    o_ref, _ = orc.sparse_attn(q, kv, idx, d_v, sm)
+    np.testing.assert_allclose(out.detach().numpy(), o_ref, rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_backward_finite_differences(orc):
+    """Directional derivatives of L = sum dout . out(q, kv) in random directions (central differences of a
+    double evaluation of the oracle's own forward definition)."""
+    rng = np.random.default_rng(71)
+    R, S, H, d_qk, d_v, k = 4, 9, 2, 8, 5, 5
+    q = rng.standard_normal((R, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((S, d_qk)).astype(np.float32)
+    dout = rng.standard_normal((R, H, d_v)).astype(np.float32)
+    pos = np.arange(S - R, S, dtype=np.int64)
+    idx = _sparse_idx(rng, R, S, k, pos)
+    sm = 0.5
+    dq, dkv, _ = orc.sparse_attn_backward(q, kv, idx, d_v, sm, dout)
+
+    def loss(qq, kk):
+        tot = 0.0
+        for r in range(R):
+            sel = idx[r][idx[r] >= 0]
+            z = sm * qq[r] @ kk[sel].T                              # [H, n]
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            pr = e / e.sum(axis=1, keepdims=True)
+            tot += float((dout[r].astype(np.float64) * (pr @ kk[sel][:, :d_v])).sum())
+        return tot
+
+    qd, kd = q.astype(np.float64), kv.astype(np.float64)
+    eps = 1e-6
+    for trial in range(3):
+        u = rng.standard_normal(q.shape)
+        v = rng.standard_normal(kv.shape)
+        num_q = (loss(qd + eps * u, kd) - loss(qd - eps * u, kd)) / (2 * eps)
+        num_k = (loss(qd, kd + eps * v) - loss(qd, kd - eps * v)) / (2 * eps)
+        assert abs(num_q - (dq * u).sum()) < 1e-6 * max(1.0, abs(num_q)), trial
+        assert abs(num_k - (dkv * v).sum()) < 1e-6 * max(1.0, abs(num_k)), trial
+    # keys nobody selects get no gradient
+    unseen = np.setdiff1d(np.arange(S), idx[idx >= 0])
+    assert np.all(dkv[unseen] == 0.0)
+
+
+def test_sparse_backward_closed_forms(orc):
+    rng = np.random.default_rng(72)
+    H, d_qk, d_v = 3, 6, 4
+    q = rng.standard_normal((2, H, d_qk)).astype(np.float32)
+    dout = rng.standard_normal((2, H, d_v)).astype(np.float32)
+    kv = rng.standard_normal((5, d_qk)).astype(np.float32)
+    # one selected entry: P = 1, dz = 0 -> dq = 0, dkv = (sum_h dout, 0); padding only: no gradient
+    idx = np.array([[3, -1, -1], [-1, -1, -1]], np.int32)
+    dq, dkv, pbar = orc.sparse_attn_backward(q, kv, idx, d_v, 0.3, dout)
+    assert np.all(dq == 0.0)
+    np.testing.assert_allclose(dkv[3, :d_v], dout[0].astype(np.float64).sum(0), rtol=1e-15)
+    assert np.all(dkv[3, d_v:] == 0.0) and np.all(np.delete(dkv, 3, axis=0) == 0.0)
+    np.testing.assert_allclose(pbar, [[1.0, 0.0, 0.0], [0.0, 0.0, 0.0]], rtol=1e-15)
+    # identical rows: P uniform, every dP equal, so dz = 0: dq = 0 and dkv[s] = (1/n) sum_h dout on [0, d_v)
+    kv_same = np.tile(kv[:1], (5, 1))
+    idx = np.array([[0, 2, 4], [1, 3, -1]], np.int32)
+    dq, dkv, pbar = orc.sparse_attn_backward(q, kv_same, idx, d_v, 0.3, dout)
+    assert np.abs(dq).max() < 1e-14
+    for r, n in ((0, 3), (1, 2)):
+        for s in idx[r][idx[r] >= 0]:
+            np.testing.assert_allclose(dkv[s, :d_v], dout[r].astype(np.float64).sum(0) / n, rtol=1e-12)
+            assert np.abs(dkv[s, d_v:]).max() < 1e-14
+        np.testing.assert_allclose(pbar[r][idx[r] >= 0], 1.0 / n, rtol=1e-14)
+
+
+def test_sparse_kl_loss(orc):
+    """Stage-2 indexer loss: p is the head mean on the selected entries, zero elsewhere; KL >= 0, zero with
+    gradient zero when softmax(I) equals p on a full selection; g sums to zero over each row."""
+    rng = np.random.default_rng(73)
+    R, S, k = 4, 8, 4
+    pos = np.arange(S - R, S, dtype=np.int64)
+    idx = _sparse_idx(rng, R, S, k, pos)
+    pbar = np.zeros((R, k))
+    for r in range(R):
+        ok = idx[r] >= 0
+        v = rng.random(ok.sum())
+        pbar[r, ok] = v / v.sum()
+    scores = rng.standard_normal((R, S)).astype(np.float32)
+    loss, g = orc.sparse_kl_loss(pbar, idx, scores, pos)
+    assert np.all(loss >= 0.0)
+    for r, ps in enumerate(pos):
+        assert abs(g[r, :ps + 1].sum()) < 1e-12
+        p = np.zeros(ps + 1)
+        p[idx[r][idx[r] >= 0]] = pbar[r][idx[r] >= 0]
+        li = scores[r, :ps + 1].astype(np.float64)
+        li = li - np.log(np.exp(li).sum())
+        ok = p > 0
+        assert abs(loss[r] - (p[ok] * (np.log(p[ok]) - li[ok])).sum()) < 1e-12
+        np.testing.assert_allclose(g[r, :ps + 1], np.exp(li) - p, atol=1e-15)
+    # a selection of every causal key with I = log p: KL = 0 and g = 0
+    pos1 = np.array([3], np.int64)
+    p1 = np.array([[0.1, 0.2, 0.3, 0.4]])
+    l1, g1 = orc.sparse_kl_loss(p1, np.array([[2, 0, 3, 1]], np.int32), np.log(p1[:, [1, 3, 0, 2]]).astype(np.float32),
+                                pos1)
+    assert abs(l1[0]) < 1e-7 and np.abs(g1).max() < 1e-7
+
+
 # ------------------------------------------------------------------ composition
 
 def test_forward_tiny_config_is_self_consistent(orc):
