@@ -199,6 +199,44 @@ dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale
                                          dsa_dtype_t dtype, float* dq_i, float* dw, float* dk_i, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Sparse training stage (velog summary, Continued Pre-Training, Stage 2): the whole model trains
+ * through the top-k selection; the indexer is detached from the main model and trained on its own loss.
+ *
+ * dsa_sparse_mla_backward -- gradients of dsa_sparse_mla_attn.  With P[t][h][j] the attention
+ * probabilities over the valid entries of idx[t] (exp(sm_scale q . kv[s_j] - lse)), dP = dout . V and
+ * D[t][h] = dout . out:
+ *
+ *   dS      = P (dP - D)
+ *   dq[t][h]  = sm_scale sum_j dS_j kv[s_j]                              (576 columns)
+ *   dkv[s]    = sum_{t,h,j: s_j = s} sm_scale dS_j q[t][h] + [P_j dout[t][h], 0]   (K and V share the row)
+ *   pbar[t][j] = (1/H) sum_h P_j      (the indexer's target in this stage; 0 for invalid entries)
+ *
+ * Inputs as dsa_sparse_mla_attn (q [B][n_q][128][576], kv [B][n_kv][576] bf16, idx [B][n_q][k] int32 with
+ * entries -1 or >= n_kv ignored, as there, and valid entries distinct), plus its outputs out
+ * [B][n_q][128][512] bf16 and lse [B][n_q][128] fp32, and dout [B][n_q][128][512] bf16; q, kv, out, dout
+ * 16-byte aligned.  Outputs fp32: dq [B][n_q][128][576], dkv [B][n_kv][576] (overwritten: zeroed, then
+ * accumulated with atomics, so the summation order varies between calls), pbar [B][n_q][k] (may be NULL).
+ * P and dS pass through the workspace as bf16 (the second products round them, as the forward rounds P).
+ * bf16, H = 128, d_qk = 576, d_v = 512, k <= 2048, n_kv <= 2^21 only (DSA_ERR_UNSUPPORTED otherwise).
+ * The workspace (256-byte aligned) holds P and dS of up to 512 query rows at a time.
+ */
+size_t dsa_sparse_mla_backward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
+                                              dsa_dtype_t dtype);
+dsa_status_t dsa_sparse_mla_backward(const void* q, const void* kv, const int32_t* idx, const void* out,
+                                     const float* lse, const void* dout, int B, int n_q, int n_kv, int H,
+                                     int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t dtype, float* dq,
+                                     float* dkv, float* pbar, void* workspace, size_t ws_bytes, void* stream);
+
+/* dsa_sparse_kl_loss -- the indexer loss of this stage, in the warm-up form with the sparse target:
+ * p[t] = pbar[t] scattered to the entries idx[t] (0 elsewhere), loss[t] = KL(p[t] || softmax(I[t])) over
+ * s <= pos_t, and scores[t][s] <- softmax(I[t])_s - p[t][s] (the gradient with respect to I, for
+ * dsa_warmup_indexer_backward).  scores [B][n_q][ld_scores] fp32 (index scores in), pbar [B][n_q][k] fp32,
+ * idx as above (entries outside [0, pos_t] are outside the loss and ignored), loss [B][n_q] fp32.
+ */
+dsa_status_t dsa_sparse_kl_loss(float* scores, int64_t ld_scores, const float* pbar, const int32_t* idx, int B,
+                                int n_q, int n_kv, int k, float* loss, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * MQA-mode projections either side of dsa_sparse_mla_attn (velog summary, section 1.3: MLA in MQA
  * mode shares each latent entry across the query heads, so the key up-projection W_UK is absorbed
  * into the query and the value up-projection W_UV is applied after attention).  Per head h of each

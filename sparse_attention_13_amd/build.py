@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "masked_mha.hip", "mla_proj.hip", "warmup.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "masked_mha.hip", "mla_proj.hip", "warmup.hip", "sparse_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -108,6 +108,16 @@ hipError_t launch_warmup_forward(const uint16_t* q, const uint16_t* kv, const fl
 hipError_t launch_warmup_backward(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
                                   const float* w, const float* g, int64_t ld_g, int B, int n_q, int n_kv, float* dq,
                                   float* dw, float* dk, hipStream_t stream);
+// Sparse training backward (bf16, H = 128, d_qk = 576, d_v = 512, k <= 2048): dq [rows][128][576] and dkv
+// [B][n_kv][576] fp32 (dkv zeroed, then accumulated), pbar [rows][k] (optional); ws_p, ws_s hold
+// sbwd_chunk_rows(rows) * k_pad * 128 bf16 each, k_pad = k rounded up to a multiple of 32.
+int sbwd_chunk_rows(int rows);
+hipError_t launch_sparse_backward(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const uint16_t* out,
+                                  const float* lse, const uint16_t* dout, int B, int n_q, int n_kv, int k,
+                                  float sm_scale, float* dq, float* dkv, float* pbar, uint16_t* ws_p,
+                                  uint16_t* ws_s, hipStream_t stream);
+hipError_t launch_sparse_kl(float* scores, int64_t ld_s, const float* pbar, const int32_t* idx, int B, int n_q,
+                            int n_kv, int k, float* loss, hipStream_t stream);
 // Masked MHA mode (bf16, d_qk = 192, d_v = 128): mask words per query row, and the two launches
 // (mask from the selection, then dense attention under it).  mask: [B][n_q][mha_mask_words(n_kv)] u32.
 int mha_mask_words(int n_kv);

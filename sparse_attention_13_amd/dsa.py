@@ -41,6 +41,10 @@ SIGNATURES = {
     "dsa_masked_mha_workspace_size": ([_I, _I, _I], _SZ),
     "dsa_warmup_loss": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64, _P, _I64, _P, _P], _I),
     "dsa_warmup_indexer_backward": ([_P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "dsa_sparse_mla_backward_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "dsa_sparse_mla_backward": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _SZ,
+                                 _P], _I),
+    "dsa_sparse_kl_loss": ([_P, _I64, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "dsa_mla_absorb_q": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "dsa_mla_out_proj": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
 }
@@ -225,6 +229,47 @@ def warmup_indexer_backward(q_i, q_i_scale, k_i, k_i_scale, w, grad, dq=None, dw
                                              _ptr(grad), grad.shape[-1], B, nq, n_kv, H_I, d_I, _dtype_code(q_i),
                                              _ptr(dq), _ptr(dw), _ptr(dk), _stream(stream)))
     return dq, dw, dk
+
+
+def sparse_mla_backward_workspace_size(B, n_q, n_kv, k):
+    return int(lib().dsa_sparse_mla_backward_workspace_size(B, n_q, n_kv, 128, 576, 512, k, DSA_BF16))
+
+
+def sparse_mla_backward(q, kv, idx, out, lse, dout, sm_scale: float, dq=None, dkv=None, pbar=None, workspace=None,
+                        with_pbar: bool = True, stream=None):
+    """Gradients of sparse_mla_attn: q [B, n_q, 128, 576], kv [B, n_kv, 576], out/dout [B, n_q, 128, 512] bf16,
+    lse [B, n_q, 128] f32, idx [B, n_q, k] int32.  Returns (dq [B, n_q, 128, 576], dkv [B, n_kv, 576],
+    pbar [B, n_q, k] or None) f32."""
+    _dev(q, kv, idx, out, lse, dout, dq, dkv, pbar, workspace)
+    B, nq, H, d_qk = q.shape
+    n_kv, k = kv.shape[1], idx.shape[-1]
+    if dq is None:
+        dq = torch.empty((B, nq, H, d_qk), dtype=torch.float32, device=q.device)
+    if dkv is None:
+        dkv = torch.empty((B, n_kv, d_qk), dtype=torch.float32, device=q.device)
+    if pbar is None and with_pbar:
+        pbar = torch.empty((B, nq, k), dtype=torch.float32, device=q.device)
+    ws = lib().dsa_sparse_mla_backward_workspace_size(B, nq, n_kv, H, d_qk, out.shape[-1], k, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().dsa_sparse_mla_backward(_ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(dout), B, nq, n_kv,
+                                         H, d_qk, out.shape[-1], k, float(sm_scale), _dtype_code(q), _ptr(dq),
+                                         _ptr(dkv), _ptr(pbar) if pbar is not None else None, _ptr(workspace),
+                                         workspace.numel(), _stream(stream)))
+    return dq, dkv, pbar
+
+
+def sparse_kl_loss(scores, pbar, idx, n_kv=None, loss=None, stream=None):
+    """Stage-2 indexer loss: scores [B, n_q, ld] f32 (index scores in, gradient softmax(I) - p out), pbar and
+    idx [B, n_q, k].  Returns loss [B, n_q] f32."""
+    _dev(scores, pbar, idx, loss)
+    B, nq, ld = scores.shape
+    n_kv = ld if n_kv is None else n_kv
+    if loss is None:
+        loss = torch.empty((B, nq), dtype=torch.float32, device=scores.device)
+    _check(lib().dsa_sparse_kl_loss(_ptr(scores), ld, _ptr(pbar), _ptr(idx), B, nq, n_kv, idx.shape[-1], _ptr(loss),
+                                    _stream(stream)))
+    return loss
 
 
 def mla_absorb_q(q_mha, w_ukt, q_mqa=None, stream=None):

@@ -19,6 +19,10 @@ written below, so a seed and a device reproduce the same bytes):
   ReLU removes.  Non-needle keys are plain N(0,1).
 * ``decode``: B sequences with one query each at the last position of S cached tokens, per-sequence
   seeds (seed + b), no needles, same dtypes and distributions as ``prefill``.
+* ``selection``: a top-k-shaped selection drawn directly (numpy Generator): for query t at position
+  pos = L - n_q + t, n = min(k, pos + 1) distinct keys in [0, pos], ascending, -1 padded; all keys when
+  n = pos + 1, else the n/4 most recent keys plus (n - n/4) drawn uniformly from the rest.
+* ``sparse_grad``: dout ~ N(0,1) in bf16, the upstream gradient of the attention output.
 """
 from __future__ import annotations
 
@@ -175,3 +179,28 @@ def bf16_bits(x: torch.Tensor):
 def u8(x: torch.Tensor):
     """A uint8 tensor on the host, as numpy."""
     return x.detach().contiguous().cpu().numpy()
+
+
+def selection(L: int, n_q: int, k: int, seed: int = 0, B: int = 1):
+    """A selection with the shape and structure of the top-k output (see the module notes), as numpy
+    int32 [B, n_q, k]: it stands in for an indexer-driven selection where the oracle cannot afford to
+    recompute the index scores."""
+    import numpy as np
+    gen = np.random.default_rng(int(seed) + 3000017)
+    out = np.full((B, n_q, k), -1, np.int32)
+    for b in range(B):
+        for t in range(n_q):
+            pos = L - n_q + t
+            n = min(k, pos + 1)
+            if n == pos + 1:
+                out[b, t, :n] = np.arange(n, dtype=np.int32)
+                continue
+            w = n // 4
+            far = gen.choice(pos + 1 - w, size=n - w, replace=False)
+            out[b, t, :n] = np.sort(np.concatenate([far, np.arange(pos + 1 - w, pos + 1)])).astype(np.int32)
+    return out
+
+
+def sparse_grad(shape, seed: int = 0, device="cpu"):
+    """dout ~ N(0,1) as bf16 with the given shape."""
+    return _randn(tuple(shape), _gen(int(seed) + 4000037, device), device, torch.bfloat16)

@@ -13,7 +13,12 @@ Tolerances:
   * attention outputs: |gpu - oracle| <= 2e-2 + 1e-2 * |oracle| (bf16 outputs); the log-sum-exp, kept in
     fp32, must be within 2e-4 absolute (a dropped or duplicated key moves it by about 1/k);
   * projections (bf16 products with fp32 accumulation): |gpu - oracle| <= 1e-3 + 8e-3 * |oracle|; bit-exact
-    on exact-integer inputs whose sums bf16 represents.
+    on exact-integer inputs whose sums bf16 represents;
+  * sparse backward: |gpu - oracle| <= 2^-7 * M, elementwise, where M is the sum of the magnitudes of the
+    terms that make the element (sparse_bwd_magnitudes): the GPU rounds P and sm_scale dS to bf16 before
+    the second products (2^-9 relative each) and forms D = dout . out from the bf16 output (2^-9 of
+    sum |dout out|), all summed in fp32; 2^-7 is that with a factor 2 of margin.  pbar (fp32 sums of
+    fp32 P) within 1e-5 relative plus 1e-7.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ IDX_ROUND = 1e-5
 ATT_ABS, ATT_REL = 2e-2, 1e-2
 LSE_ABS = 2e-4
 PROJ_ABS, PROJ_REL = 1e-3, 8e-3  # bf16 output of an fp32-accumulated product: rounding <= 2^-9 relative
+BWD_REL = 2.0 ** -7
 
 
 def indexer_errors(gpu_rows: np.ndarray, ora_rows: np.ndarray, mag_rows: np.ndarray, absmag_rows: np.ndarray,
@@ -86,3 +92,34 @@ def attention_errors(gpu_out: np.ndarray, ora_out: np.ndarray, gpu_lse: np.ndarr
     ratio = float((d / (ATT_ABS + ATT_REL * np.abs(ora_out))).max()) if d.size else 0.0
     lse_err = float(np.abs(gpu_lse.astype(np.float64) - ora_lse).max()) if ora_lse.size else 0.0
     return ratio, float(d.max()) if d.size else 0.0, lse_err
+
+
+def sparse_bwd_magnitudes(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, dout: np.ndarray, sm_scale: float,
+                          d_v: int, rows=None):
+    """Term magnitudes for the sparse backward tolerance (float64, numpy): for each (row, head) with P and
+    dS = P (dP - D) over the valid entries and Dabs = sum_d |dout out|,
+      Mq[r][h]  = sm_scale sum_j (|dS_j| + P_j Dabs) |kv_j|
+      Mkv[s]   += sm_scale (|dS_j| + P_j Dabs) |q[r][h]| + P_j |[dout[r][h], 0]|
+    over the given rows (all by default).  q [R, H, d], kv [S, d], idx [R, k], dout [R, H, d_v] float32."""
+    R, H, d = q.shape
+    rows = range(R) if rows is None else rows
+    mq = np.zeros((len(list(rows)), H, d))
+    mkv = np.zeros(kv.shape)
+    for n, r in enumerate(rows):
+        sel = idx[r][idx[r] >= 0]
+        if len(sel) == 0:
+            continue
+        kr = kv[sel].astype(np.float64)
+        qr = q[r].astype(np.float64)
+        dr = dout[r].astype(np.float64)
+        z = sm_scale * qr @ kr.T
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dp = dr @ kr[:, :d_v].T
+        dabs = np.abs(dr * (p @ kr[:, :d_v])).sum(axis=1, keepdims=True)   # [H, 1]
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        t = sm_scale * (np.abs(ds) + p * dabs)                        # [H, n]
+        mq[n] = t @ np.abs(kr)
+        mkv[sel] += t.T @ np.abs(qr)
+        mkv[sel, :d_v] += p.T @ np.abs(dr)
+    return mq, mkv

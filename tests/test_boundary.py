@@ -38,7 +38,8 @@ def test_header_declares_the_path():
               "dsa_forward_decode",
               "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
               "dsa_last_error", "dsa_version", "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size",
-              "dsa_mla_absorb_q", "dsa_mla_out_proj"]:
+              "dsa_mla_absorb_q", "dsa_mla_out_proj", "dsa_warmup_loss", "dsa_warmup_indexer_backward",
+              "dsa_sparse_mla_backward", "dsa_sparse_mla_backward_workspace_size", "dsa_sparse_kl_loss"]:
         assert n in names
 
 
@@ -226,6 +227,51 @@ def test_warmup_validation(L):
     assert b(*a) == DSA_ERR_INVALID_ARG                              # misaligned dq_i
     a = list(ok); a[7] = 70000
     assert b(*a) == DSA_ERR_UNSUPPORTED                              # grid
+
+
+def test_sparse_backward_validation_and_workspace(L):
+    from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE,
+                                             DSA_F32)
+    wsz = L.dsa_sparse_mla_backward_workspace_size
+    # P and dS of min(rows, 512) query rows, bf16, entries padded to a multiple of 32
+    assert wsz(1, 300, 400, 128, 576, 512, 64, DSA_BF16) == 2 * 300 * 64 * 128 * 2
+    assert wsz(1, 300, 400, 128, 576, 512, 50, DSA_BF16) == 2 * 300 * 64 * 128 * 2
+    assert wsz(2, 8192, 8192, 128, 576, 512, 2048, DSA_BF16) == 2 * 512 * 2048 * 128 * 2
+    assert wsz(1, 300, 400, 128, 576, 512, 4096, DSA_BF16) == 0        # k beyond 2048
+    assert wsz(1, 300, 200, 128, 576, 512, 64, DSA_BF16) == 0          # n_q > n_kv
+    f = L.dsa_sparse_mla_backward
+    ws = wsz(1, 64, 100, 128, 576, 512, 32, DSA_BF16)
+    big = ctypes.c_void_p(0x40000)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 576, 512, 32, 0.04, DSA_BF16, FAKE2, FAKE2, None, big,
+          ws, None]
+    a = list(ok); a[19] = ws - 1
+    assert f(*a) == DSA_ERR_WORKSPACE                                # too small
+    a = list(ok); a[18] = ctypes.c_void_p(0x40010)
+    assert f(*a) == DSA_ERR_WORKSPACE                                # misaligned
+    a = list(ok); a[18] = None
+    assert f(*a) == DSA_ERR_WORKSPACE                                # missing
+    a = list(ok); a[12] = 4096
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # k beyond 2048
+    a = list(ok); a[14] = DSA_F32
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # bf16 only
+    a = list(ok); a[9] = 64
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # H other than 128
+    a = list(ok); a[7] = 101
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # n_q > n_kv
+    a = list(ok); a[3] = None
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # null out
+    a = list(ok); a[13] = float("nan")
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # non-finite scale
+    a = list(ok); a[5] = ctypes.c_void_p(0x10002)
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned dout
+    g = L.dsa_sparse_kl_loss
+    ok = [FAKE, 100, FAKE, FAKE, 1, 64, 100, 32, FAKE2, None]
+    a = list(ok); a[1] = 99
+    assert g(*a) == DSA_ERR_INVALID_ARG                              # ld below n_kv
+    a = list(ok); a[2] = None
+    assert g(*a) == DSA_ERR_INVALID_ARG                              # null pbar
+    a = list(ok); a[4] = 70000
+    assert g(*a) == DSA_ERR_UNSUPPORTED                              # grid
 
 
 def test_forward_validation(L):

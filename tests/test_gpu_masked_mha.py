@@ -98,19 +98,16 @@ def test_masked_mha_ignored_entries_and_empty_rows(orc, dsa):
 
 
 def test_masked_mha_full_8k(orc, dsa):
-    """Prefill of 8192 tokens, 128 heads, k = 2048 from the indexer and top-k of the same sequence, in the
-    benchmark's launch configuration; rows sampled across query tiles, including rows that keep every
+    """Prefill of 8192 tokens, 128 heads, k = 2048, in the benchmark's launch configuration, on a seeded
+    top-k-shaped selection drawn on the host (the oracle cannot afford the full index scores, and its
+    inputs never come from the GPU); rows sampled across query tiles, including rows that keep every
     causal key (t < 2048) and rows whose mask leaves a quarter of them."""
     L, k_sel = 8192, 2048
-    x = synth.prefill(L, seed=0, device=DEV, n_needles=64, with_mla=False)
     m = synth.mha_heads(L, seed=0, device=DEV)
-    scores = torch.empty((1, L, L), device=DEV)
-    dsa.indexer_scores(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None], scores)
-    idx = dsa.topk(scores, L, k_sel)
-    del scores
+    gi = synth.selection(L, L, k_sel, seed=2)[0]
+    idx = torch.from_numpy(gi).to(DEV)[None]
     out, lse = dsa.masked_mha_attn(m["q"][None], m["k"][None], m["v"][None], idx, m["sm_scale"])
     torch.cuda.synchronize()
-    gi = idx[0].cpu().numpy()
     parity.assert_idx_wellformed(gi, np.arange(L, dtype=np.int64), k_sel)
     rows = np.array([0, 1, 63, 127, 128, 2047, 2048, 2049, 4095, 5000, 8064, 8191])
     check_rows(orc, m["q"], m["k"], m["v"], gi, out[0], lse[0], rows, m["sm_scale"], "8k")
