@@ -214,11 +214,12 @@ dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale
  * Inputs as dsa_sparse_mla_attn (q [B][n_q][128][576], kv [B][n_kv][576] bf16, idx [B][n_q][k] int32 with
  * entries -1 or >= n_kv ignored, as there, and valid entries distinct), plus its outputs out
  * [B][n_q][128][512] bf16 and lse [B][n_q][128] fp32, and dout [B][n_q][128][512] bf16; q, kv, out, dout
- * 16-byte aligned.  Outputs fp32: dq [B][n_q][128][576], dkv [B][n_kv][576] (overwritten: zeroed, then
- * accumulated with atomics, so the summation order varies between calls), pbar [B][n_q][k] (may be NULL).
- * P and dS pass through the workspace as bf16 (the second products round them, as the forward rounds P).
- * bf16, H = 128, d_qk = 576, d_v = 512, k <= 2048, n_kv <= 2^21 only (DSA_ERR_UNSUPPORTED otherwise).
- * The workspace (256-byte aligned) holds P and dS of up to 512 query rows at a time.
+ * 16-byte aligned.  Outputs fp32: dq [B][n_q][128][576], dkv [B][n_kv][576] (overwritten; the order in
+ * which a key's terms are summed varies between calls), pbar [B][n_q][k] (may be NULL).  P, dS and each
+ * entry's dkv terms pass through the workspace as bf16 (the second products round P and dS, as the
+ * forward rounds P).  bf16, H = 128, d_qk = 576, d_v = 512, k <= 2048, n_kv <= 2^21, B n_kv <= 2^26 only
+ * (DSA_ERR_UNSUPPORTED otherwise).  The workspace (256-byte aligned) holds P, dS and the dkv terms of up
+ * to 512 query rows at a time and the per-key entry lists.
  */
 size_t dsa_sparse_mla_backward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
                                               dsa_dtype_t dtype);

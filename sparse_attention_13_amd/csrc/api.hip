@@ -271,17 +271,12 @@ dsa_status_t dsa_sparse_mla_attn(const void* q, const void* kv, const int32_t* i
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, p, workspace, (hipStream_t)stream);
 }
 
-static size_t sbwd_ws_bytes(int B, int n_q, int k) {
-  const size_t chunk = (size_t)dsa::sbwd_chunk_rows(B * n_q);
-  return 2 * chunk * (size_t)((k + 31) / 32 * 32) * 128 * 2;  // P and dS, entries padded to steps of 32
-}
-
 size_t dsa_sparse_mla_backward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
                                               dsa_dtype_t dtype) {
   if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv || k < 1 || k > 2048 || H != 128 || d_qk != 576 || d_v != 512 ||
-      dtype != DSA_BF16 || (int64_t)B * n_q > 0x7FFFFFFF)
+      dtype != DSA_BF16 || (int64_t)B * n_q > 0x7FFFFFFF || (int64_t)B * n_kv > (1 << 26))
     return 0;
-  return sbwd_ws_bytes(B, n_q, k);
+  return dsa::sbwd_workspace_bytes(B, n_q, n_kv, k);
 }
 
 dsa_status_t dsa_sparse_mla_backward(const void* q, const void* kv, const int32_t* idx, const void* out,
@@ -291,21 +286,19 @@ dsa_status_t dsa_sparse_mla_backward(const void* q, const void* kv, const int32_
   if (B < 1 || n_q < 1 || n_kv < 1 || n_q > n_kv || k < 1) return fail(DSA_ERR_INVALID_ARG, "sparse_backward: bad sizes");
   if (dtype != DSA_BF16 || H != 128 || d_qk != 576 || d_v != 512)
     return fail(DSA_ERR_UNSUPPORTED, "sparse_backward: supports bf16 with H=128, d_qk=576, d_v=512");
-  if (k > 2048 || n_kv > (1 << 21) || (int64_t)B * n_q > 0x7FFFFFFF)
-    return fail(DSA_ERR_UNSUPPORTED, "sparse_backward: k <= 2048, n_kv <= 2^21");
+  if (k > 2048 || n_kv > (1 << 21) || (int64_t)B * n_q > 0x7FFFFFFF || (int64_t)B * n_kv > (1 << 26))
+    return fail(DSA_ERR_UNSUPPORTED, "sparse_backward: k <= 2048, n_kv <= 2^21, B * n_kv <= 2^26");
   if (!q || !kv || !idx || !out || !lse || !dout || !dq || !dkv)
     return fail(DSA_ERR_INVALID_ARG, "sparse_backward: null pointer");
   if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "sparse_backward: sm_scale must be finite");
   if (!(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16) && aligned(dout, 16)))
     return fail(DSA_ERR_INVALID_ARG, "sparse_backward: q, kv, out, dout must be 16-byte aligned");
-  const size_t need = sbwd_ws_bytes(B, n_q, k);
+  const size_t need = dsa::sbwd_workspace_bytes(B, n_q, n_kv, k);
   if (workspace == nullptr || ws_bytes < need || !aligned(workspace, 256))
     return fail(DSA_ERR_WORKSPACE, "sparse_backward: workspace of %zu bytes (256-byte aligned) needed", need);
-  uint16_t* ws_p = (uint16_t*)workspace;
-  uint16_t* ws_s = ws_p + need / 4;
   return hip_status(dsa::launch_sparse_backward((const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)out, lse,
-                                                (const uint16_t*)dout, B, n_q, n_kv, k, sm_scale, dq, dkv, pbar, ws_p,
-                                                ws_s, (hipStream_t)stream),
+                                                (const uint16_t*)dout, B, n_q, n_kv, k, sm_scale, dq, dkv, pbar,
+                                                workspace, (hipStream_t)stream),
                     "dsa_sparse_mla_backward");
 }
 

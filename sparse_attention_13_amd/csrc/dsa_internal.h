@@ -109,13 +109,14 @@ hipError_t launch_warmup_backward(const uint8_t* q8, const float* qs, const uint
                                   const float* w, const float* g, int64_t ld_g, int B, int n_q, int n_kv, float* dq,
                                   float* dw, float* dk, hipStream_t stream);
 // Sparse training backward (bf16, H = 128, d_qk = 576, d_v = 512, k <= 2048): dq [rows][128][576] and dkv
-// [B][n_kv][576] fp32 (dkv zeroed, then accumulated), pbar [rows][k] (optional); ws_p, ws_s hold
-// sbwd_chunk_rows(rows) * k_pad * 128 bf16 each, k_pad = k rounded up to a multiple of 32.
+// [B][n_kv][576] fp32 (overwritten), pbar [rows][k] (optional); the workspace holds
+// sbwd_workspace_bytes(...) bytes (P, dS, the dkv terms of one chunk of query rows, the per-key lists).
 int sbwd_chunk_rows(int rows);
+size_t sbwd_workspace_bytes(int B, int n_q, int n_kv, int k);
 hipError_t launch_sparse_backward(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const uint16_t* out,
                                   const float* lse, const uint16_t* dout, int B, int n_q, int n_kv, int k,
-                                  float sm_scale, float* dq, float* dkv, float* pbar, uint16_t* ws_p,
-                                  uint16_t* ws_s, hipStream_t stream);
+                                  float sm_scale, float* dq, float* dkv, float* pbar, void* workspace,
+                                  hipStream_t stream);
 hipError_t launch_sparse_kl(float* scores, int64_t ld_s, const float* pbar, const int32_t* idx, int B, int n_q,
                             int n_kv, int k, float* loss, hipStream_t stream);
 // Masked MHA mode (bf16, d_qk = 192, d_v = 128): mask words per query row, and the two launches

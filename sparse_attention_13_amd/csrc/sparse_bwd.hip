@@ -22,8 +22,11 @@
 //                      (two buffers).  dq[128 x 192] += dS K on the 32x32x16 core, both operands by
 //                      transposing LDS reads; dkv[32 x 192] = dS^T Q + P^T dout on the 16x16x32 core,
 //                      with the Q and dout operands held in registers for the whole query (loaded once
-//                      through LDS).  dkv goes to HBM by fp32 atomics, one step late and after the next
-//                      copies are issued, so the wait for a tile never waits for an atomic.
+//                      through LDS).  Each entry's dkv terms go to HBM as bf16 rows, one step late and after
+//                      the next copies are issued, so the wait for a tile never waits for a store.
+//   dkv                without 576-wide atomics (fp32 atomics run at about 5e10 adds/s here, far below
+//                      what the scatter needs): the chunk's (query, entry) pairs are listed per key by a
+//                      counting sort, and one wave per key sums its pairs' rows into dkv.
 #include <algorithm>
 
 #include "dsa_internal.h"
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ ws_p,
                                                             const uint16_t* __restrict__ ws_s, int r0, int n_rows,
                                                             int n_q, int n_kv, int k, float* __restrict__ dq,
-                                                            float* __restrict__ dkv) {
+                                                            uint16_t* __restrict__ contrib) {
   // step buffers as separate LDS objects: reads of one never wait for copies into another
   __shared__ __attribute__((aligned(1024))) char kt0[kGK];
   __shared__ __attribute__((aligned(1024))) char kt1[kGK];
@@ -431,17 +434,16 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
     for (int r = 0; r < 16; r++) acc_q[j][r] = 0.f;
   v4f acc_k[3];
 
-  // dkv += the previous step's tiles: lane (G, jj) of tile j holds entries 16eb + 4G + i, column 16n + jj;
-  // an invalid entry adds 0 to row 0, so the instruction count is fixed
-  auto flush = [&](int selv) {
+  // the previous step's dkv terms -> contrib[entry][576] (bf16): lane (G, jj) of tile j holds entries
+  // 16eb + 4G + i, column 16n + jj; twelve stores per wave, whatever the entries
+  uint16_t* cr = contrib + (size_t)rr * (32 * n_steps) * kBD + d0 + jj;
+  auto flush = [&](int step_i) {
 #pragma unroll
     for (int j = 0; j < 3; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int s = __shfl(selv, 16 * eb + 4 * G + i);
-        const float v = s >= 0 ? acc_k[j][i] : 0.f;
-        float* dst = dkv + ((size_t)b * n_kv + max(s, 0)) * kBD + d0 + 16 * (nq0 + j) + jj;
-        __builtin_amdgcn_global_atomic_fadd_f32(dst, v);
+        const int e = 32 * step_i + 16 * eb + 4 * G + i;
+        cr[(size_t)e * kBD + 16 * (nq0 + j)] = f32_to_bf16_bits(acc_k[j][i]);
       }
   };
 
@@ -488,11 +490,11 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
   issue(0, sel_of(0), kt0, st0, pt0);
   vm_wait0();
   lds_bar();
-  // step i: copies of step i+1 (other buffers, last read in step i-1), the atomics of step i-1, the
-  // products of step i; then wait for the copies only (the 12 atomics may still be in flight)
+  // step i: copies of step i+1 (other buffers, last read in step i-1), the stores of step i-1, the
+  // products of step i; then wait for the copies only (the 12 stores may still be in flight)
   auto step = [&](int i, const char* ktb, const char* stb, const char* ptb, char* ktn, char* stn, char* ptn) {
     if (i + 1 < n_steps) issue(i + 1, sel_of(i + 1), ktn, stn, ptn);
-    if (i > 0) flush(sel_of(i - 1));
+    if (i > 0) flush(i - 1);
     compute(ktb, stb, ptb);
     if (i > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     else vm_wait0();
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
     step(i, kt0, st0, pt0, kt1, st1, pt1);
     if (i + 1 < n_steps) step(i + 1, kt1, st1, pt1, kt0, st0, pt0);
   }
-  flush(sel_of(n_steps - 1));
+  flush(n_steps - 1);
 
   // dq: lane = column 32n + l%32, registers = heads 32hb + 8(r/4) + 4(l/32) + r%4
 #pragma unroll
@@ -561,6 +563,110 @@ __global__ __launch_bounds__(256) void sparse_kl_kernel(float* __restrict__ scor
   if (threadIdx.x == 0) loss[row] = kl;
 }
 
+// ------------------------------------------------------------------------------------------------ dkv
+// dkv[key] = the sum of contrib over the (query, entry) pairs that select the key, without atomics on
+// the 576-wide rows: the pairs of a chunk are listed per key (a counting sort: count, scan, fill) and one
+// wave per key sums its list.  key = b * n_kv + s.
+
+__global__ __launch_bounds__(256) void sbwd_count_kernel(const int32_t* __restrict__ idx, int r0, int n_rows, int n_q,
+                                                         int n_kv, int k, int* __restrict__ count) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)n_rows * k) return;
+  const int rr = (int)(i / k), e = (int)(i - (size_t)rr * k);
+  const int row = r0 + rr, b = row / n_q;
+  const int s = idx[(size_t)row * k + e];
+  if (s >= 0 && s < n_kv) atomicAdd(&count[(size_t)b * n_kv + s], 1);
+}
+
+// offs = exclusive prefix sum of count (one workgroup), count reset to zero for the fill's cursors
+__global__ __launch_bounds__(1024) void sbwd_scan_kernel(int* __restrict__ count, int* __restrict__ offs, int n) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = min(n, tid * per), e = min(n, a + per);
+  int sum = 0;
+  for (int i = a; i < e; i++) sum += count[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int i = a; i < e; i++) {
+    offs[i] = run;
+    run += count[i];
+    count[i] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void sbwd_fill_kernel(const int32_t* __restrict__ idx, int r0, int n_rows, int n_q,
+                                                        int n_kv, int k, int k_pad, const int* __restrict__ offs,
+                                                        int* __restrict__ count, int* __restrict__ list) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)n_rows * k) return;
+  const int rr = (int)(i / k), e = (int)(i - (size_t)rr * k);
+  const int row = r0 + rr, b = row / n_q;
+  const int s = idx[(size_t)row * k + e];
+  if (s >= 0 && s < n_kv) {
+    const size_t key = (size_t)b * n_kv + s;
+    list[offs[key] + atomicAdd(&count[key], 1)] = rr * k_pad + e;
+  }
+}
+
+// one wave per key: dkv[key] += sum of its pairs' contrib rows (lane l: columns 8l .. 8l+7, lanes < 8 also
+// 512 + 8l ..); count[key] back to zero for the next chunk
+__global__ __launch_bounds__(256) void sbwd_reduce_kernel(const uint16_t* __restrict__ contrib,
+                                                          const int* __restrict__ offs, int* __restrict__ count,
+                                                          const int* __restrict__ list, int n_keys,
+                                                          float* __restrict__ dkv) {
+  const int lane = threadIdx.x & 63;
+  const int key = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (key >= n_keys) return;
+  const int n = count[key];
+  if (n == 0) return;
+  const int* lp = list + offs[key];
+  float a0[8], a1[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) a0[e] = a1[e] = 0.f;
+  auto add = [&](const u32x4 v, float (&acc)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      acc[2 * e] += __uint_as_float(v[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  };
+  int p = 0;
+  for (; p + 4 <= n; p += 4) {
+    u32x4 v[4], w[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const uint16_t* row = contrib + (size_t)lp[p + u] * kBD;
+      v[u] = *(const u32x4*)(row + 8 * lane);
+      if (lane < 8) w[u] = *(const u32x4*)(row + kBV + 8 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      add(v[u], a0);
+      if (lane < 8) add(w[u], a1);
+    }
+  }
+  for (; p < n; p++) {
+    const uint16_t* row = contrib + (size_t)lp[p] * kBD;
+    add(*(const u32x4*)(row + 8 * lane), a0);
+    if (lane < 8) add(*(const u32x4*)(row + kBV + 8 * lane), a1);
+  }
+  float* d = dkv + (size_t)key * kBD;
+#pragma unroll
+  for (int e = 0; e < 8; e++) d[8 * lane + e] += a0[e];
+  if (lane < 8)
+#pragma unroll
+    for (int e = 0; e < 8; e++) d[kBV + 8 * lane + e] += a1[e];
+  if (lane == 0) count[key] = 0;
+}
+
 __global__ __launch_bounds__(256) void sbwd_zero_kernel(float* __restrict__ x, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) x[i] = 0.f;
 }
@@ -569,25 +675,57 @@ __global__ __launch_bounds__(256) void sbwd_zero_kernel(float* __restrict__ x, s
 
 int sbwd_chunk_rows(int rows) { return rows < 512 ? rows : 512; }
 
+size_t sbwd_workspace_bytes(int B, int n_q, int n_kv, int k) {
+  const size_t chunk = (size_t)sbwd_chunk_rows(B * n_q), k_pad = (size_t)(k + 31) / 32 * 32;
+  const size_t n_keys = (size_t)B * n_kv;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return 2 * up(chunk * k_pad * kBH * 2) + up(chunk * k_pad * kBD * 2) + up(chunk * k_pad * 4) + 2 * up(n_keys * 4);
+}
+
 hipError_t launch_sparse_backward(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const uint16_t* out,
                                   const float* lse, const uint16_t* dout, int B, int n_q, int n_kv, int k,
-                                  float sm_scale, float* dq, float* dkv, float* pbar, uint16_t* ws_p,
-                                  uint16_t* ws_s, hipStream_t stream) {
-  const size_t n_dkv = (size_t)B * n_kv * kBD;
+                                  float sm_scale, float* dq, float* dkv, float* pbar, void* workspace,
+                                  hipStream_t stream) {
+  const int rows = B * n_q;
+  const int chunk = sbwd_chunk_rows(rows);
+  const int k_pad = (k + 31) / 32 * 32;
+  const size_t n_keys = (size_t)B * n_kv;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = (char*)workspace;
+  uint16_t* ws_p = (uint16_t*)w;
+  w += up((size_t)chunk * k_pad * kBH * 2);
+  uint16_t* ws_s = (uint16_t*)w;
+  w += up((size_t)chunk * k_pad * kBH * 2);
+  uint16_t* contrib = (uint16_t*)w;
+  w += up((size_t)chunk * k_pad * kBD * 2);
+  int* list = (int*)w;
+  w += up((size_t)chunk * k_pad * 4);
+  int* count = (int*)w;
+  w += up(n_keys * 4);
+  int* offs = (int*)w;
+
+  const size_t n_dkv = n_keys * kBD;
   hipLaunchKernelGGL(sbwd_zero_kernel, dim3((unsigned)std::min<size_t>((n_dkv + 255) / 256, 4096)), dim3(256), 0,
                      stream, dkv, n_dkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = B * n_q;
-  const int chunk = sbwd_chunk_rows(rows);
+  hipLaunchKernelGGL(sbwd_zero_kernel, dim3((unsigned)std::min<size_t>((n_keys + 255) / 256, 4096)), dim3(256), 0,
+                     stream, (float*)count, n_keys);  // int zero == float zero
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   for (int r0 = 0; r0 < rows; r0 += chunk) {
     const int n = std::min(chunk, rows - r0);
+    const unsigned n_ent = (unsigned)(((size_t)n * k + 255) / 256);
+    hipLaunchKernelGGL(sbwd_count_kernel, dim3(n_ent), dim3(256), 0, stream, idx, r0, n, n_q, n_kv, k, count);
     hipLaunchKernelGGL(sbwd_probs_kernel, dim3(n), dim3(512), 0, stream, q, kv, idx, out, lse, dout, r0, n_q, n_kv,
                        k, sm_scale, ws_p, ws_s, pbar);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sbwd_grads_kernel, dim3((n + 7) / 8 * 8 * 3), dim3(512), 0, stream, q, kv, idx, dout,
-                       (const uint16_t*)ws_p, (const uint16_t*)ws_s, r0, n, n_q, n_kv, k, dq, dkv);
+                       (const uint16_t*)ws_p, (const uint16_t*)ws_s, r0, n, n_q, n_kv, k, dq, contrib);
+    hipLaunchKernelGGL(sbwd_scan_kernel, dim3(1), dim3(1024), 0, stream, count, offs, (int)n_keys);
+    hipLaunchKernelGGL(sbwd_fill_kernel, dim3(n_ent), dim3(256), 0, stream, idx, r0, n, n_q, n_kv, k, k_pad,
+                       (const int*)offs, count, list);
+    hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)((n_keys + 3) / 4)), dim3(256), 0, stream,
+                       (const uint16_t*)contrib, (const int*)offs, count, (const int*)list, (int)n_keys, dkv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -233,10 +233,14 @@ def test_sparse_backward_validation_and_workspace(L):
     from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE,
                                              DSA_F32)
     wsz = L.dsa_sparse_mla_backward_workspace_size
-    # P and dS of min(rows, 512) query rows, bf16, entries padded to a multiple of 32
-    assert wsz(1, 300, 400, 128, 576, 512, 64, DSA_BF16) == 2 * 300 * 64 * 128 * 2
-    assert wsz(1, 300, 400, 128, 576, 512, 50, DSA_BF16) == 2 * 300 * 64 * 128 * 2
-    assert wsz(2, 8192, 8192, 128, 576, 512, 2048, DSA_BF16) == 2 * 512 * 2048 * 128 * 2
+    # P, dS (bf16, 128 heads) and the dkv terms (bf16, 576 columns) of min(rows, 512) query rows with the
+    # entries padded to a multiple of 32, the chunk's entry list, per-key counts and offsets; 256-B regions
+    def expect(rows, k_pad, n_keys):
+        up = lambda x: (x + 255) // 256 * 256
+        return 2 * up(rows * k_pad * 256) + up(rows * k_pad * 1152) + up(rows * k_pad * 4) + 2 * up(n_keys * 4)
+    assert wsz(1, 300, 400, 128, 576, 512, 64, DSA_BF16) == expect(300, 64, 400)
+    assert wsz(1, 300, 400, 128, 576, 512, 50, DSA_BF16) == expect(300, 64, 400)
+    assert wsz(2, 8192, 8192, 128, 576, 512, 2048, DSA_BF16) == expect(512, 2048, 16384)
     assert wsz(1, 300, 400, 128, 576, 512, 4096, DSA_BF16) == 0        # k beyond 2048
     assert wsz(1, 300, 200, 128, 576, 512, 64, DSA_BF16) == 0          # n_q > n_kv
     f = L.dsa_sparse_mla_backward
