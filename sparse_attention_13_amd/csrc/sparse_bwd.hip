@@ -79,25 +79,12 @@ __device__ __forceinline__ void gather_step(const char* __restrict__ kvb, const 
 
 constexpr int kBMaxK = 2048;
 
-// Four K/V fragments of k-steps 4M .. 4M+3 (lane addresses a[j] = tile + kb[j], immediate offset 128M),
-// read in one asm block that completes them: the kernel itself establishes that the tile's copies have
-// landed (wait, then barrier), and an ordinary load here would make the compiler wait for the copies
-// into the other tile.
+// Four K/V fragments of k-steps 4M .. 4M+3 (lane addresses a[j] = tile + kb[j], offset 128M).  The two
+// roles run separate loops, so the compiler sees no copy in flight into the tile being read.
 template <int M>
 __device__ __forceinline__ void rd4(const unsigned int (&a)[4], v8bf (&x)[4]) {
-  u32x4 y0, y1, y2, y3;
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n\t"
-      "ds_read_b128 %1, %5 offset:%8\n\t"
-      "ds_read_b128 %2, %6 offset:%8\n\t"
-      "ds_read_b128 %3, %7 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3)
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(128 * M));
-  x[0] = __builtin_bit_cast(v8bf, y0);
-  x[1] = __builtin_bit_cast(v8bf, y1);
-  x[2] = __builtin_bit_cast(v8bf, y2);
-  x[3] = __builtin_bit_cast(v8bf, y3);
+#pragma unroll
+  for (int j = 0; j < 4; j++) x[j] = *(const v8bf*)((const char*)(lds_void_b*)(uintptr_t)a[j] + 128 * M);
 }
 
 template <int NM, int M = 0>
@@ -277,31 +264,16 @@ constexpr int kGStage = kBH * kGRow;     // 49152 B: Q or dout columns of the qu
 __device__ __forceinline__ int swz_k(int r) { return 4 * ((r >> 1) & 1); }
 __device__ __forceinline__ int swz_q(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
 
+// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) and two 16-byte LDS reads.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 __device__ __forceinline__ void tr2(const char* a0, const char* a1, u32x2& x0, u32x2& x1) {
-  const unsigned int p0 = (unsigned int)(uintptr_t)(lds_void_b*)a0;
-  const unsigned int p1 = (unsigned int)(uintptr_t)(lds_void_b*)a1;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %2\n\t"
-      "ds_read_b64_tr_b16 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1)
-      : "v"(p0), "v"(p1));
+  x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_void_b*)a0));
+  x1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_void_b*)a1));
 }
-// Two 16-byte LDS reads completed inside the asm block.  The tiles they read were filled by LDS copies
-// whose completion the kernel establishes itself (wait, then barrier); an ordinary load here would make
-// the compiler wait for every copy in flight, including those into the other buffer.
 __device__ __forceinline__ void rd2(const char* a0, const char* a1, v8bf& x0, v8bf& x1) {
-  const unsigned int p0 = (unsigned int)(uintptr_t)(lds_void_b*)a0;
-  const unsigned int p1 = (unsigned int)(uintptr_t)(lds_void_b*)a1;
-  u32x4 y0, y1;
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(y0), "=&v"(y1)
-      : "v"(p0), "v"(p1));
-  x0 = __builtin_bit_cast(v8bf, y0);
-  x1 = __builtin_bit_cast(v8bf, y1);
+  x0 = *(const v8bf*)a0;
+  x1 = *(const v8bf*)a1;
 }
 __device__ __forceinline__ v8bf as_frag(const u32x2 x0, const u32x2 x1) {
   return __builtin_bit_cast(v8bf, (u32x4){x0[0], x0[1], x1[0], x1[1]});
@@ -616,17 +588,18 @@ __global__ __launch_bounds__(256) void sbwd_fill_kernel(const int32_t* __restric
   }
 }
 
-// one wave per key: dkv[key] += sum of its pairs' contrib rows (lane l: columns 8l .. 8l+7, lanes < 8 also
-// 512 + 8l ..); count[key] back to zero for the next chunk
+// one workgroup per key: its four waves take every fourth pair of the key's list (lane l: columns 8l ..
+// 8l+7, lanes < 8 also 512 + 8l ..), the partial sums meet in LDS and dkv[key] += their sum; count[key]
+// back to zero for the next chunk
 __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const uint16_t* __restrict__ contrib,
                                                           const int* __restrict__ offs, int* __restrict__ count,
                                                           const int* __restrict__ list, int n_keys,
                                                           float* __restrict__ dkv) {
-  const int lane = threadIdx.x & 63;
-  const int key = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (key >= n_keys) return;
+  __shared__ __attribute__((aligned(16))) float red[4][kBD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int key = (int)blockIdx.x;
   const int n = count[key];
-  if (n == 0) return;
+  if (n == 0) return;  // whole workgroup
   const int* lp = list + offs[key];
   float a0[8], a1[8];
 #pragma unroll
@@ -638,12 +611,12 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const uint16_t* __rest
       acc[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
     }
   };
-  int p = 0;
-  for (; p + 4 <= n; p += 4) {
+  int p = wave;
+  for (; p + 12 < n; p += 16) {
     u32x4 v[4], w[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const uint16_t* row = contrib + (size_t)lp[p + u] * kBD;
+      const uint16_t* row = contrib + (size_t)lp[p + 4 * u] * kBD;
       v[u] = *(const u32x4*)(row + 8 * lane);
       if (lane < 8) w[u] = *(const u32x4*)(row + kBV + 8 * lane);
     }
@@ -653,18 +626,21 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const uint16_t* __rest
       if (lane < 8) add(w[u], a1);
     }
   }
-  for (; p < n; p++) {
+  for (; p < n; p += 4) {
     const uint16_t* row = contrib + (size_t)lp[p] * kBD;
     add(*(const u32x4*)(row + 8 * lane), a0);
     if (lane < 8) add(*(const u32x4*)(row + kBV + 8 * lane), a1);
   }
+  *(v4f*)&red[wave][8 * lane] = (v4f){a0[0], a0[1], a0[2], a0[3]};
+  *(v4f*)&red[wave][8 * lane + 4] = (v4f){a0[4], a0[5], a0[6], a0[7]};
+  if (lane < 8) {
+    *(v4f*)&red[wave][kBV + 8 * lane] = (v4f){a1[0], a1[1], a1[2], a1[3]};
+    *(v4f*)&red[wave][kBV + 8 * lane + 4] = (v4f){a1[4], a1[5], a1[6], a1[7]};
+  }
+  __syncthreads();
   float* d = dkv + (size_t)key * kBD;
-#pragma unroll
-  for (int e = 0; e < 8; e++) d[8 * lane + e] += a0[e];
-  if (lane < 8)
-#pragma unroll
-    for (int e = 0; e < 8; e++) d[kBV + 8 * lane + e] += a1[e];
-  if (lane == 0) count[key] = 0;
+  for (int c = threadIdx.x; c < kBD; c += 256) d[c] += red[0][c] + red[1][c] + red[2][c] + red[3][c];
+  if (threadIdx.x == 0) count[key] = 0;
 }
 
 __global__ __launch_bounds__(256) void sbwd_zero_kernel(float* __restrict__ x, size_t n) {
@@ -724,7 +700,7 @@ hipError_t launch_sparse_backward(const uint16_t* q, const uint16_t* kv, const i
     hipLaunchKernelGGL(sbwd_scan_kernel, dim3(1), dim3(1024), 0, stream, count, offs, (int)n_keys);
     hipLaunchKernelGGL(sbwd_fill_kernel, dim3(n_ent), dim3(256), 0, stream, idx, r0, n, n_q, n_kv, k, k_pad,
                        (const int*)offs, count, list);
-    hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)((n_keys + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)n_keys), dim3(256), 0, stream,
                        (const uint16_t*)contrib, (const int*)offs, count, (const int*)list, (int)n_keys, dkv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
