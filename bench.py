@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--no-proj", action="store_true", help="skip the MQA-mode projection measurement")
     ap.add_argument("--no-warmup-loss", action="store_true", help="skip the indexer warm-up loss measurement")
+    ap.add_argument("--no-sparse-bwd", action="store_true", help="skip the sparse training backward measurement")
     ap.add_argument("--mha-lens", default="4096,8192,12288,16384",
                     help="prefill lengths of the masked-MHA vs sparse-MQA attention sweep ('' to skip)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -287,7 +288,60 @@ def main():
         out["mla_projections"] = projections_bench(args.prefill_len, dev, stream)
     if args.only in (None, "prefill") and not args.no_warmup_loss:
         out["warmup_loss"] = warmup_bench(args.prefill_len, dev, stream)
+    if args.only in (None, "prefill") and not args.no_sparse_bwd:
+        out["sparse_backward"] = sparse_backward_bench(args.prefill_len, k, dev, stream)
     print(json.dumps(out), flush=True)
+
+
+SBWD_FLOP_PER_ENTRY = 2 * 128 * (576 + 512 + 576 + 576 + 512)  # S, dP, dq, dK, dV per selected entry
+
+
+def sparse_backward_bench(L, k, dev, stream):
+    """The sparse training stage's backward through the attention on a prefill of L tokens with k selected
+    entries per query (a host-drawn top-k-shaped selection): dq and dkv (and the head-mean target) from
+    dout, given the forward's out and lse.  Matrix-core work per selected entry: S, dP, dq, dK and dV over
+    128 heads (SBWD_FLOP_PER_ENTRY); HBM traffic beyond it: P and dS (512 B per entry) and the entry's
+    dkv terms (1152 B per entry), each written once and read once."""
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    print(f"[bench] sparse backward at {L} tokens, k={k}", file=sys.stderr, flush=True)
+    x = synth.prefill(L, seed=0, device=dev)
+    idx = torch.from_numpy(synth.selection(L, L, k, seed=1)).to(dev)
+    mq_ws = dsa.lib().dsa_sparse_mla_attn_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16)
+    ws_f = torch.empty(max(mq_ws, 256), dtype=torch.uint8, device=dev)
+    out, lse = dsa.sparse_mla_attn(x["q"][None], x["kv"][None], idx, 512, x["sm_scale"], workspace=ws_f)
+    dout = synth.sparse_grad((1, L, 128, 512), seed=0, device=dev)
+    ws = torch.empty(dsa.sparse_mla_backward_workspace_size(1, L, L, k), dtype=torch.uint8, device=dev)
+    dq = torch.empty((1, L, 128, 576), dtype=torch.float32, device=dev)
+    dkv = torch.empty((1, L, 576), dtype=torch.float32, device=dev)
+    pbar = torch.empty((1, L, k), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf, tb = [], []
+    for rep in range(5):
+        ev[0].record(stream)
+        dsa.sparse_mla_attn(x["q"][None], x["kv"][None], idx, 512, x["sm_scale"], out=out, lse=lse, workspace=ws_f)
+        ev[1].record(stream)
+        dsa.sparse_mla_backward(x["q"][None], x["kv"][None], idx, out, lse, dout, x["sm_scale"], dq=dq, dkv=dkv,
+                                pbar=pbar, workspace=ws)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            tf.append(ev[0].elapsed_time(ev[1]))
+            tb.append(ev[1].elapsed_time(ev[2]))
+    t_f, t_b = sorted(tf)[len(tf) // 2], sorted(tb)[len(tb) // 2]
+    entries = sum(min(k, t + 1) for t in range(L))
+    tflops = entries * SBWD_FLOP_PER_ENTRY / (t_b * 1e-3) / 1e12
+    res = {"workload": f"1x{L} tokens, k={k}, 128 heads, d_qk=576, d_v=512, bf16 (host-drawn selection)",
+           "forward_ms": round(t_f, 4), "backward_ms": round(t_b, 4), "backward_over_forward": round(t_b / t_f, 2),
+           "tokens_per_s": round(L / (t_b * 1e-3), 1), "TFLOP/s": round(tflops, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+           "workspace_bytes": int(ws.numel())}
+    del x, idx, out, lse, dout, ws, ws_f, dq, dkv, pbar
+    torch.cuda.empty_cache()
+    return res
 
 
 def warmup_bench(L, dev, stream):
