@@ -260,29 +260,16 @@ __device__ __forceinline__ void store_row_chunk(char* tile, int r, int c, const 
 // Transposing reads of a bf16 tile (256-byte rows): for the 16-row half at row r0, the A operand of
 // four 32-column blocks (as V^T in attention): out[db][0] rows r0 + 0..7, out[db][1] rows r0 + 8..15.
 // toff[db][rd]: the lane's byte offset for column block db and 8-row half rd (the swizzle differs).
+typedef short v4s_w __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_w lds_v4s_w;
 __device__ __forceinline__ void tr_frags(const char* tile, const int (&toff)[4][2], int r0, u32x2 (&vr)[4][2]) {
   const char* base = tile + r0 * (kID * 2);
-  const unsigned int a0 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[0][0]);
-  const unsigned int a1 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[0][1]);
-  const unsigned int a2 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[1][0]);
-  const unsigned int a3 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[1][1]);
-  const unsigned int a4 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[2][0]);
-  const unsigned int a5 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[2][1]);
-  const unsigned int a6 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[3][0]);
-  const unsigned int a7 = (unsigned int)(uintptr_t)(lds_void_w*)(base + toff[3][1]);
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vr[0][0]), "=&v"(vr[0][1]), "=&v"(vr[1][0]), "=&v"(vr[1][1]), "=&v"(vr[2][0]), "=&v"(vr[2][1]),
-        "=&v"(vr[3][0]), "=&v"(vr[3][1])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7));
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int rd = 0; rd < 2; rd++)
+      vr[db][rd] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_w*)(lds_void_w*)(base + toff[db][rd])));
 }
 
 // Lane offsets for tr_frags: rows 8rd + 4(G>>1) + (j>>2), columns 32db + 16(G&1) + 4(j&3) (G = l/16, j = l%16).
@@ -375,26 +362,28 @@ __global__ __launch_bounds__(128 * Q, 2) void warmup_dq_kernel(const uint8_t* __
   // < 64Q also fetch g k_scale of (query tid/64, key tid%64), zero past the query's position
   constexpr int kRowsPer = 8 * Q;
   const int st_r = tid >> 4, st_c = tid & 15;
+  // (the loads are issued by every thread, in bounds, and their values are only combined at the store, so
+  // no wait for them falls before the block's products)
   u32x2 st_codes[kDqKeys / kRowsPer];
-  float st_gk = 0.f;
+  float st_g = 0.f, st_k = 0.f;
+  bool st_ok = false;
   auto stage_load = [&](int i) {
 #pragma unroll
     for (int u = 0; u < kDqKeys / kRowsPer; u++) {
       const int s = min(kDqKeys * i + kRowsPer * u + st_r, n_kv - 1);
       st_codes[u] = *(const u32x2*)(kb + (size_t)s * kID + 8 * st_c);
     }
-    if (tid < 64 * Q) {
-      const int qt = min(t0 + (tid >> 6), n_q - 1);
-      const int key = kDqKeys * i + (tid & 63);
-      const int kc = min(key, n_kv - 1);
-      const float gv = g[((size_t)b * n_q + qt) * ld_g + min(kc, n_kv - n_q + qt)];
-      st_gk = (key <= n_kv - n_q + qt) ? gv * ksb[kc] : 0.f;
-    }
+    const int qt = min(t0 + ((tid >> 6) & (Q - 1)), n_q - 1);
+    const int key = kDqKeys * i + (tid & 63);
+    const int kc = min(key, n_kv - 1);
+    st_g = g[((size_t)b * n_q + qt) * ld_g + min(kc, n_kv - n_q + qt)];
+    st_k = ksb[kc];
+    st_ok = key <= n_kv - n_q + qt;
   };
   auto stage_store = [&](char* tile, float (*gk)[kDqKeys]) {
 #pragma unroll
     for (int u = 0; u < kDqKeys / kRowsPer; u++) store_row_half(tile, kRowsPer * u + st_r, st_c, st_codes[u]);
-    if (tid < 64 * Q) gk[tid >> 6][tid & 63] = st_gk;
+    if (tid < 64 * Q) gk[tid >> 6][tid & 63] = st_ok ? st_g * st_k : 0.f;
   };
 
   auto sub = [&](const char* tile, const float* gkq) {
@@ -525,8 +514,11 @@ __global__ __launch_bounds__(64 * KW, 2) void warmup_dk_kernel(const uint8_t* __
   // codes 16 (j%8) ..); threads < 64 the head's w q_scale; threads 64 .. 64 + 32KW g of key s_base + tid - 64
   // (zero past t's position)
   constexpr int kU = 8 / KW;
+  // (every thread issues its loads, in bounds, and the values are only combined at the store, so no wait
+  // for them falls before the query's products)
   u32x4 st_q[kU];
-  float st_v = 0.f;
+  float st_x = 0.f, st_y = 0.f;
+  bool st_ok = false;
   auto stage_load = [&](int t) {
     const size_t row = (size_t)b * n_q + t;
 #pragma unroll
@@ -534,14 +526,13 @@ __global__ __launch_bounds__(64 * KW, 2) void warmup_dk_kernel(const uint8_t* __
       const int j = kU * tid + u;
       st_q[u] = *(const u32x4*)(q8 + (row * kIH + (j >> 3)) * kID + 16 * (j & 7));
     }
-    if (tid < kIH) {
-      st_v = w[row * kIH + tid] * qs[row * kIH + tid];
-    } else if (tid < kIH + 32 * KW) {
-      const int s = s_base + tid - kIH;
-      const int pos = t + off;
-      const float gv = g[row * ld_g + min(s, pos)];
-      st_v = (s <= pos) ? gv : 0.f;
-    }
+    const int s = s_base + tid - kIH;
+    const int pos = t + off;
+    const float* px = tid < kIH ? w + row * kIH + tid : g + row * ld_g + max(0, min(s, pos));
+    const float* py = tid < kIH ? qs + row * kIH + tid : px;
+    st_x = *px;
+    st_y = *py;
+    st_ok = s <= pos;
   };
   auto stage_store = [&](char* tile, float* cf, float* gq) {
 #pragma unroll
@@ -549,8 +540,8 @@ __global__ __launch_bounds__(64 * KW, 2) void warmup_dk_kernel(const uint8_t* __
       const int j = kU * tid + u;
       store_row_chunk(tile, j >> 3, j & 7, st_q[u]);
     }
-    if (tid < kIH) cf[tid] = st_v;
-    else if (tid < kIH + 32 * KW) gq[tid - kIH] = st_v;
+    if (tid < kIH) cf[tid] = st_x * st_y;
+    else if (tid < kIH + 32 * KW) gq[tid - kIH] = st_ok ? st_x : 0.f;
   };
   auto query = [&](const char* tile, const float* cf, const float* gq) {
     // D[head][key]: lane = key s_lane, value r of block hb = head 32hb + 8(r/4) + 4(l/32) + r%4
