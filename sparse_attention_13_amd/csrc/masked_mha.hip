@@ -99,24 +99,15 @@ struct MhaState {
 
 // V^T fragments of one 16-key half (rows r0 .. r0+15 of the tile) for the four 32-column blocks:
 // eight transposing reads completed inside the block.
+typedef short v4s_m __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_m lds_v4s_m;
 __device__ __forceinline__ void vt_frags(const char* vt, const int (&voff)[4], int r0, u32x2 (&vr)[4][2]) {
-  const unsigned int b0 = (unsigned int)(uintptr_t)(lds_void_t*)(vt + voff[0] + r0 * 256);
-  const unsigned int b1 = (unsigned int)(uintptr_t)(lds_void_t*)(vt + voff[1] + r0 * 256);
-  const unsigned int b2 = (unsigned int)(uintptr_t)(lds_void_t*)(vt + voff[2] + r0 * 256);
-  const unsigned int b3 = (unsigned int)(uintptr_t)(lds_void_t*)(vt + voff[3] + r0 * 256);
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:0\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:0\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:0\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vr[0][0]), "=&v"(vr[0][1]), "=&v"(vr[1][0]), "=&v"(vr[1][1]), "=&v"(vr[2][0]), "=&v"(vr[2][1]),
-        "=&v"(vr[3][0]), "=&v"(vr[3][1])
-      : "v"(b0), "v"(b1), "v"(b2), "v"(b3));
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int rd = 0; rd < 2; rd++)
+      vr[db][rd] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                 (lds_v4s_m*)(lds_void_t*)(vt + voff[db] + r0 * 256 + 2048 * rd)));
 }
 
 // One key tile for this wave's QB x 32 queries (query block qb: queries 32qb + l%32 of the wave's).
