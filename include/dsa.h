@@ -190,8 +190,9 @@ dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, in
  *
  * Inputs as dsa_indexer_scores (fp8 e4m3 codes, fp32 scales, H_I = 64, d_I = 128); grad
  * [B][n_q][ld_grad] fp32 (entries past pos_t are not read).  Outputs fp32: dq_i [B][n_q][64][128]
- * (16-byte aligned), dw [B][n_q][64], dk_i [B][n_kv][128] (overwritten).  The ReLU decision is taken on
- * the codes' dot product in fp32 (the scales are positive).
+ * (16-byte aligned), dw [B][n_q][64], dk_i [B][n_kv][128] (overwritten: zeroed, then parts of the queries
+ * added with fp32 atomics, so the order of its sums varies between calls).  The ReLU decision is taken on
+ * the codes' dot product in fp32 (the scales are positive).  n_kv <= 2^21.
  */
 dsa_status_t dsa_warmup_indexer_backward(const void* q_i, const float* q_i_scale, const void* k_i,
                                          const float* k_i_scale, const float* w, const float* grad,
