@@ -22,8 +22,10 @@
 //                      (two buffers).  dq[128 x 192] += dS K on the 32x32x16 core, both operands by
 //                      transposing LDS reads; dkv[32 x 192] = dS^T Q + P^T dout on the 16x16x32 core,
 //                      with the Q and dout operands held in registers for the whole query (loaded once
-//                      through LDS).  Each entry's dkv terms go to HBM as bf16 rows, one step late and after
-//                      the next copies are issued, so the wait for a tile never waits for a store.
+//                      through LDS); the products are formed transposed so that each lane holds four
+//                      consecutive columns of one entry.  Each entry's dkv terms go to HBM as bf16 rows,
+//                      one step late and after the next copies are issued, so the wait for a tile never
+//                      waits for a store.
 //   dkv                without 576-wide atomics (fp32 atomics run at about 5e10 adds/s here, far below
 //                      what the scatter needs): the chunk's (query, entry) pairs are listed per key by a
 //                      counting sort, and one wave per key sums its pairs' rows into dkv.
@@ -391,7 +393,8 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
       toff_k[j][rd] = r * kGRow + 16 * (ck ^ swz_k(r)) + 8 * (jj & 1);
     }
   }
-  // dkv tiles: entry block eb = w/4 (16 entries); A operand rows 16eb + l%16, heads 32kk + 8G .. +8
+  // dkv tiles: entry block eb = w/4 (16 entries); the dS and P fragments (B operand): entry 16eb + l%16,
+  // heads 32kk + 8G .. +8
   const int eb = wave >> 2;
   const int ar = 16 * eb + jj;
   int aoff[4];
@@ -406,17 +409,16 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
     for (int r = 0; r < 16; r++) acc_q[j][r] = 0.f;
   v4f acc_k[3];
 
-  // the previous step's dkv terms -> contrib[entry][576] (bf16): lane (G, jj) of tile j holds entries
-  // 16eb + 4G + i, column 16n + jj; twelve stores per wave, whatever the entries
-  uint16_t* cr = contrib + (size_t)rr * (32 * n_steps) * kBD + d0 + jj;
+  // the previous step's dkv terms -> contrib[entry][576] (bf16).  The products are formed transposed
+  // (Q^T and dout^T as the A operand, the dS and P tiles as B), so lane (G, jj) of tile j holds entry
+  // 16eb + jj and the four consecutive columns 16n + 4G .. +4: one 8-byte store per tile, three per wave.
+  uint16_t* cr = contrib + (size_t)rr * (32 * n_steps) * kBD + d0 + 4 * G;
   auto flush = [&](int step_i) {
+    const int e = 32 * step_i + 16 * eb + jj;
 #pragma unroll
     for (int j = 0; j < 3; j++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int e = 32 * step_i + 16 * eb + 4 * G + i;
-        cr[(size_t)e * kBD + 16 * (nq0 + j)] = f32_to_bf16_bits(acc_k[j][i]);
-      }
+      *(u32x2*)(cr + (size_t)e * kBD + 16 * (nq0 + j)) =
+          (u32x2){pack_bf16x2(acc_k[j][0], acc_k[j][1]), pack_bf16x2(acc_k[j][2], acc_k[j][3])};
   };
 
   auto compute = [&](const char* ktb, const char* stb, const char* ptb) {
@@ -442,8 +444,8 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
         rd2(stb + aoff[kk], ptb + aoff[kk], as, ap);
 #pragma unroll
         for (int j = 0; j < 3; j++) {
-          acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, bq[j][kk], acc_k[j], 0, 0, 0);
-          acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bo[j][kk], acc_k[j], 0, 0, 0);
+          acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[j][kk], as, acc_k[j], 0, 0, 0);
+          acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bo[j][kk], ap, acc_k[j], 0, 0, 0);
         }
       }
     } else {
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
         v8bf as, ap;
         rd2(stb + aoff[kk], ptb + aoff[kk], as, ap);
 #pragma unroll
-        for (int j = 0; j < 3; j++) acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as, bq[j][kk], acc_k[j], 0, 0, 0);
+        for (int j = 0; j < 3; j++) acc_k[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[j][kk], as, acc_k[j], 0, 0, 0);
       }
     }
   };
@@ -463,12 +465,12 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
   vm_wait0();
   lds_bar();
   // step i: copies of step i+1 (other buffers, last read in step i-1), the stores of step i-1, the
-  // products of step i; then wait for the copies only (the 12 stores may still be in flight)
+  // products of step i; then wait for the copies only (the 3 stores may still be in flight)
   auto step = [&](int i, const char* ktb, const char* stb, const char* ptb, char* ktn, char* stn, char* ptn) {
     if (i + 1 < n_steps) issue(i + 1, sel_of(i + 1), ktn, stn, ptn);
     if (i > 0) flush(i - 1);
     compute(ktb, stb, ptb);
-    if (i > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    if (i > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 3);
     else vm_wait0();
     lds_bar();
   };
