@@ -384,15 +384,32 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   int* misc = (int*)(smem + kOffMisc);
   int* sel_l = (int*)(smem + kOffSel);
 
+  // Q^T fragments of this wave's 32 heads: lane holds head 32w + l%32, dims 16ks + 8(l/32) .. +8.
+  // Issued first, so that their latency overlaps that of the selection's loads below.
+  v8bf qf[kDQK / 16];
+  {
+    const uint16_t* qh = q + (row * kH + 32 * wave + (lane & 31)) * kDQK + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kDQK / 16; ks++) qf[ks] = *(const v8bf*)(qh + 16 * ks);
+  }
+
   // this workgroup's part of the selection -> LDS (invalid entries as -1), and its extent
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   {
+    // all of a thread's loads in flight at once (e_n <= kMaxSel = 8 x 256)
     int last = -1;
-    for (int e = tid; e < e_n; e += 256) {
-      const int v = sel[e_begin + e];
-      const bool ok = valid_entry(v, n_kv);
-      sel_l[e] = ok ? v : -1;
+    int v[kMaxSel / 256];
+#pragma unroll
+    for (int u = 0; u < kMaxSel / 256; u++) {
+      const int e = tid + 256 * u;
+      v[u] = e < e_n ? sel[e_begin + e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxSel / 256; u++) {
+      const int e = tid + 256 * u;
+      const bool ok = e < e_n && valid_entry(v[u], n_kv);
+      if (e < e_n) sel_l[e] = ok ? v[u] : -1;
       if (ok) last = e;
     }
     for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
@@ -401,14 +418,6 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   __syncthreads();
   const int n_span = misc[0] + 1;
   const int n_steps = (n_span + kNB - 1) / kNB;
-
-  // Q^T fragments of this wave's 32 heads: lane holds head 32w + l%32, dims 16ks + 8(l/32) .. +8
-  v8bf qf[kDQK / 16];
-  {
-    const uint16_t* qh = q + (row * kH + 32 * wave + (lane & 31)) * kDQK + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < kDQK / 16; ks++) qf[ks] = *(const v8bf*)(qh + 16 * ks);
-  }
 
   v16f o[4][4];  // O^T blocks [d block][head block]
 #pragma unroll
@@ -458,21 +467,38 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   }
   __syncthreads();
   if (n_split == 1) {
+    // O goes out through LDS (the tiles are free after the last step): 64 heads at a time are written
+    // as bf16 rows of 1040 B, then every wave stores 16 whole 1 KiB head rows, 16 bytes per lane, instead
+    // of 8-byte pieces spread over 32 rows per instruction
+    char* stg = smem + kOffBuf;
+    constexpr int kStgRow = 1040;
+    static_assert(64 * kStgRow <= kNBuf * kTileBytes, "staging fits in the tiles");
 #pragma unroll
-    for (int hb = 0; hb < 4; hb++) {
-      const int h = 32 * hb + (lane & 31);
-      const float lh = l_l[h];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      uint16_t* op = out + (row * kH + h) * kDV + 128 * wave + 4 * (lane >> 5);
+    for (int pass = 0; pass < 2; pass++) {
 #pragma unroll
-      for (int db = 0; db < 4; db++)
+      for (int hh = 0; hh < 2; hh++) {
+        const int hb = 2 * pass + hh;
+        const float lh = l_l[32 * hb + (lane & 31)];
+        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+        char* rowp = stg + (32 * hh + (lane & 31)) * kStgRow + (128 * wave + 4 * (lane >> 5)) * 2;
 #pragma unroll
-        for (int qd = 0; qd < 4; qd++) {
-          u32x2 v;
-          v[0] = pack_bf16x2(o[db][hb][4 * qd + 0] * inv, o[db][hb][4 * qd + 1] * inv);
-          v[1] = pack_bf16x2(o[db][hb][4 * qd + 2] * inv, o[db][hb][4 * qd + 3] * inv);
-          *(u32x2*)(op + 32 * db + 8 * qd) = v;
-        }
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+          for (int qd = 0; qd < 4; qd++) {
+            u32x2 v;
+            v[0] = pack_bf16x2(o[db][hb][4 * qd + 0] * inv, o[db][hb][4 * qd + 1] * inv);
+            v[1] = pack_bf16x2(o[db][hb][4 * qd + 2] * inv, o[db][hb][4 * qd + 3] * inv);
+            *(u32x2*)(rowp + (32 * db + 8 * qd) * 2) = v;
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int hl = 16 * wave + r;
+        const u32x4 v = *(const u32x4*)(stg + hl * kStgRow + lane * 16);
+        *(u32x4*)(out + (row * kH + 64 * pass + hl) * kDV + 8 * lane) = v;
+      }
+      __syncthreads();
     }
     if (lse && lane < 32) {
       const float lh = l_run;
