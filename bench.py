@@ -61,8 +61,8 @@ def parse():
 # counter for a plain copy of known size (`bench.py --calib-copy`).  Valid only for the kernel source it
 # was measured on: the sha256 of that source is stored with it and checked at run time.
 MEASURED_TRAFFIC = {
-    "prefill.sparse_mla": {"bytes_per_launch": 14229728870,  # 9.873 GB read + 4.357 GB written
-                           "src_sha256": "fc0b3f3b77c8fef14489ec716aca41e6c8fb3d5c4c662932f6566fe9185085aa",
+    "prefill.sparse_mla": {"bytes_per_launch": 14618671104,  # 10.240 GB read + 4.379 GB written
+                           "src_sha256": "300f7827b9dbb67ab2b3ea0d0d8ffc4fb3135f3a32de04bc26ff2e0ec7e90368",
                            "profile": "profiles/dsa_kernels_prefill32k_hbm_traffic.md"},
 }
 KERNEL_SOURCES = {
