@@ -552,27 +552,67 @@ __global__ __launch_bounds__(256) void sbwd_count_kernel(const int32_t* __restri
   if (s >= 0 && s < n_kv) atomicAdd(&count[(size_t)b * n_kv + s], 1);
 }
 
-// offs = exclusive prefix sum of count (one workgroup), count reset to zero for the fill's cursors
+// offs = exclusive prefix sum of count (one workgroup), count reset to zero for the fill's cursors.
+// Thread t owns the contiguous entries [t*per, t*per + per), per a multiple of 32, read 32 at a time
+// with every load in flight (16-byte loads: the workspace arrays are 256-byte aligned); the thread
+// totals are scanned with wave shuffles and one exchange across the 16 waves.
+__device__ __forceinline__ void scan_load32(const int* __restrict__ p, int i, int e, int (&v)[32]) {
+  if (i + 32 <= e) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int4 q = *(const int4*)(p + i + 4 * u);
+      v[4 * u] = q.x; v[4 * u + 1] = q.y; v[4 * u + 2] = q.z; v[4 * u + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; j++) v[j] = i + j < e ? p[i + j] : 0;
+  }
+}
 __global__ __launch_bounds__(1024) void sbwd_scan_kernel(int* __restrict__ count, int* __restrict__ offs, int n) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (((n + 1023) / 1024) + 31) & ~31;
   const int a = min(n, tid * per), e = min(n, a + per);
   int sum = 0;
-  for (int i = a; i < e; i++) sum += count[i];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  for (int i = a; i < e; i += 32) {
+    int v[32];
+    scan_load32(count, i, e, v);
+#pragma unroll
+    for (int j = 0; j < 32; j++) sum += v[j];
   }
-  int run = part[tid] - sum;
-  for (int i = a; i < e; i++) {
-    offs[i] = run;
-    run += count[i];
-    count[i] = 0;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w2 = 0; w2 < wave; w2++) run += wsum[w2];
+  for (int i = a; i < e; i += 32) {
+    int v[32];
+    scan_load32(count, i, e, v);
+    int o[32];
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+      o[j] = run;
+      run += v[j];
+    }
+    if (i + 32 <= e) {
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        *(int4*)(offs + i + 4 * u) = make_int4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
+        *(int4*)(count + i + 4 * u) = make_int4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; j++)
+        if (i + j < e) {
+          offs[i + j] = o[j];
+          count[i + j] = 0;
+        }
+    }
   }
 }
 
