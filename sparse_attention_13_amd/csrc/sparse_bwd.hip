@@ -127,9 +127,18 @@ __global__ __launch_bounds__(512, 1) void sbwd_probs_kernel(const uint16_t* __re
 
   // the row's selection: valid latent row or -1 (also past k, up to the last step's end); as in the
   // forward attention, an entry is valid when it names a key row, whatever the query's position
-  for (int e = tid; e < 32 * n_steps; e += 512) {
-    const int s = e < k ? idx[(size_t)row * k + e] : -1;
-    sel_l[e] = (s >= 0 && s < n_kv) ? s : -1;
+  {
+    int sv[kBMaxK / 512];  // all of a thread's loads in flight at once (k <= kBMaxK)
+#pragma unroll
+    for (int u = 0; u < kBMaxK / 512; u++) {
+      const int e = tid + 512 * u;
+      sv[u] = e < k ? idx[(size_t)row * k + e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBMaxK / 512; u++) {
+      const int e = tid + 512 * u;
+      if (e < 32 * n_steps) sel_l[e] = (sv[u] >= 0 && sv[u] < n_kv) ? sv[u] : -1;
+    }
   }
   // S waves: Q (A operand of S = Q K^T): lane holds head 32hw + l%32, dims 16ks + 8(l/32) .. +8.
   // dP waves: dout of the same heads, first 32 k-steps.
@@ -314,9 +323,18 @@ __global__ __launch_bounds__(512, 1) void sbwd_grads_kernel(const uint16_t* __re
   // ---- prologue: Q and dout columns d0 .. d0+191 of the 128 heads through LDS into B-operand registers
   // of the 16x16x32 products: wave w, column block n = 3(w%4) + j (16 wide), k-step kk (32 heads):
   // lane (G, jj) holds column 16n + jj, heads 32kk + 8G .. +8.
-  for (int e = tid; e < 32 * n_steps; e += 512) {
-    const int s = e < k ? idx[(size_t)row * k + e] : -1;
-    sel_l[e] = (s >= 0 && s < n_kv) ? s : -1;
+  {
+    int sv[kBMaxK / 512];  // all of a thread's loads in flight at once (k <= kBMaxK)
+#pragma unroll
+    for (int u = 0; u < kBMaxK / 512; u++) {
+      const int e = tid + 512 * u;
+      sv[u] = e < k ? idx[(size_t)row * k + e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBMaxK / 512; u++) {
+      const int e = tid + 512 * u;
+      if (e < 32 * n_steps) sel_l[e] = (sv[u] >= 0 && sv[u] < n_kv) ? sv[u] : -1;
+    }
   }
   const int nq0 = 3 * (wave & 3);  // first 16-wide column block of the wave's dkv tiles
   v8bf bq[3][4], bo[3][4];
