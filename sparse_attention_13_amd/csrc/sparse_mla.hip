@@ -505,22 +505,36 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
       lse[row * kH + 32 * wave + lane] = lh > 0.f ? (m_run + log2f(lh)) * kLn2 : -INFINITY;
     }
   } else {
-    // partial result of this split: normalised O (fp32) and its log-sum-exp
+    // partial result of this split: normalised O (fp32) and its log-sum-exp.  Through LDS as in the
+    // single-split case: 32 heads at a time as fp32 rows of 2064 B, then every wave stores 8 whole
+    // 2 KiB head rows, 16 bytes per lane and instruction
+    char* stg = smem + kOffBuf;
+    constexpr int kStgRowF = 2064;
+    static_assert(32 * kStgRowF <= kNBuf * kTileBytes, "staging fits in the tiles");
     float* pbase = part + ((row * n_split + split) * kH) * kDV;
 #pragma unroll
     for (int hb = 0; hb < 4; hb++) {
-      const int h = 32 * hb + (lane & 31);
-      const float lh = l_l[h];
+      const float lh = l_l[32 * hb + (lane & 31)];
       const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      float* op = pbase + (size_t)h * kDV + 128 * wave + 4 * (lane >> 5);
+      char* rowp = stg + (lane & 31) * kStgRowF + (128 * wave + 4 * (lane >> 5)) * 4;
 #pragma unroll
       for (int db = 0; db < 4; db++)
 #pragma unroll
         for (int qd = 0; qd < 4; qd++) {
-          v4f v = {o[db][hb][4 * qd] * inv, o[db][hb][4 * qd + 1] * inv, o[db][hb][4 * qd + 2] * inv,
-                   o[db][hb][4 * qd + 3] * inv};
-          *(v4f*)(op + 32 * db + 8 * qd) = v;
+          const v4f v = {o[db][hb][4 * qd] * inv, o[db][hb][4 * qd + 1] * inv, o[db][hb][4 * qd + 2] * inv,
+                         o[db][hb][4 * qd + 3] * inv};
+          *(v4f*)(rowp + (32 * db + 8 * qd) * 4) = v;
         }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 8; r++) {
+        const int hl = 8 * wave + r;
+        float* dst = pbase + (size_t)(32 * hb + hl) * kDV;
+        const char* src = stg + hl * kStgRowF;
+        *(v4f*)(dst + 4 * lane) = *(const v4f*)(src + 16 * lane);
+        *(v4f*)(dst + 256 + 4 * lane) = *(const v4f*)(src + 1024 + 16 * lane);
+      }
+      __syncthreads();
     }
     if (lane < 32) {
       const float lh = l_run;
