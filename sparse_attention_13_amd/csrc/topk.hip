@@ -12,7 +12,9 @@
 //     selected positions in ascending order (ballots over per-lane counts), so the result is sorted.
 // One workgroup (8 waves) selects from up to kKeyCap keys held in LDS: the first pass reads them from
 // memory (kLoadUnroll independent 16-byte loads per thread in flight), every later pass and the
-// compaction read LDS in 16-byte pieces, kLdsUnroll per lane in flight.
+// compaction read LDS in 16-byte pieces, kLdsUnroll per lane in flight.  Rows of at most 32768 keys
+// with aligned starts keep their keys in registers instead (topk_reg_kernel): the workgroup then needs
+// only about 34 KB of LDS and two of them share a compute unit.
 //
 // Rows that are longer than kKeyCap, or too few to fill the GPU, run in two stages.  Stage one cuts
 // each row into chunks and selects the top k of every chunk as (key, position) candidates; stage two
@@ -465,6 +467,242 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   }
 }
 
+// Rows of at most kRegKeys keys with 16-byte aligned starts: the same select, with every key held in
+// registers instead of LDS.  Wave w owns the segment [w*segw, w*segw + segw) (segw a multiple of 256,
+// at most 16 blocks of 256); lane l holds keys 256u + 4l .. +3 of its wave's block u.  LDS keeps only
+// the histograms, the candidate list and the staged output (about 34 KB), so two workgroups share a
+// compute unit and one's barriers and memory waits overlap the other's passes.
+constexpr int kRegBlocks = 16;
+constexpr int kRegKeys = kTkWaves * kRegBlocks * kSeg;  // 32768
+
+__global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 int n_q, int n_kv, int k, int32_t* __restrict__ idx) {
+  __shared__ unsigned int hist[kHistWords];   // histograms; then the candidates' positions; then the output
+  __shared__ unsigned int misc[kMiscWords];   // [64] scratch + [256] summed histogram
+  __shared__ unsigned int ckey[kHistWords];   // the candidates' keys
+  unsigned int* tot = misc + 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t = n_q - 1 - (int)blockIdx.x;  // longest rows first
+  const int b = blockIdx.y;
+  const int m = n_kv - n_q + t + 1;  // causal row length
+  const size_t rowid = (size_t)b * n_q + t;
+  int32_t* out_idx = idx + rowid * (size_t)k;
+  if (m <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out_idx[i] = (i < m) ? i : -1;
+    return;
+  }
+  const float* srow = scores + rowid * ld;
+  const int segw = ((m + kTkWaves * kSeg - 1) / (kTkWaves * kSeg)) * kSeg;  // <= kRegBlocks * kSeg
+  const int s0 = wave * segw;
+  const int s1 = min(m, s0 + segw);
+  const int nb = segw / kSeg;  // blocks per wave (uniform)
+
+  // ---- pass 0: the wave's keys into registers (every load in flight at once, clamped into the row),
+  // histogram of the top byte
+  unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
+  for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
+  u32x4 kr[kRegBlocks];
+  {
+    const int last4 = (m - 1) & ~3;
+#pragma unroll
+    for (int u = 0; u < kRegBlocks; u++) {
+      if (u < nb) {
+        const int i = min(s0 + kSeg * u + 4 * lane, last4);
+        kr[u] = __builtin_bit_cast(u32x4, *reinterpret_cast<const float4*>(srow + i));
+      } else {
+        kr[u] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __syncthreads();  // histogram cleared
+#pragma unroll
+  for (int u = 0; u < kRegBlocks; u++) {
+    if (u < nb) {
+      const int i = s0 + kSeg * u + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        // positions past the segment (values from a clamped load) hold key 0 and are never counted:
+        // every later pass tests i + e < s1 again
+        unsigned int key = 0u;
+        if (i + e < s1) {
+          key = score_key(__uint_as_float(kr[u][e]));
+          atomicAdd(&h[key >> 24], 1u);
+        }
+        kr[u][e] = key;
+      }
+    }
+  }
+  __syncthreads();
+  select_digit(hist, misc, tot, k, tid, wave, lane);
+  unsigned int prefix = misc[0];
+  int k_rem = k - (int)misc[1];
+  __syncthreads();
+
+  // one histogram pass over the registers for each digit in [first, last)
+  auto reg_hist_passes = [&](int first, int last) {
+#pragma unroll 1
+    for (int pass = first; pass < last; pass++) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kRegBlocks; u++) {
+        if (u < nb) {
+          const int i = s0 + kSeg * u + 4 * lane;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (i + e < s1 && (kr[u][e] >> (shift + 8)) == prefix) atomicAdd(&h[(kr[u][e] >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      select_digit(hist, misc, tot, k_rem, tid, wave, lane);
+      prefix = (prefix << 8) | misc[0];
+      k_rem -= (int)misc[1];
+      __syncthreads();  // misc is rewritten next
+    }
+  };
+  reg_hist_passes(1, 2);
+
+  // ---- candidates: keys on the 16-bit prefix, listed with their positions; keys above it counted
+  unsigned int* clist = hist;
+  unsigned int* ccount = misc + 20;
+  if (tid == 0) *ccount = 0u;
+  __syncthreads();
+  unsigned int n_above = 0;
+#pragma unroll
+  for (int u = 0; u < kRegBlocks; u++) {
+    if (u < nb) {
+      const int i = s0 + kSeg * u + 4 * lane;
+      unsigned int cmask = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool v = i + e < s1;
+        const unsigned int top = kr[u][e] >> 16;
+        n_above += (v && top > prefix) ? 1u : 0u;
+        cmask |= (v && top == prefix) ? 1u << e : 0u;
+      }
+      if (__ballot(cmask != 0) != 0) {
+        unsigned int slot = cmask ? atomicAdd(ccount, (unsigned int)__popc(cmask)) : 0u;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if (cmask & (1u << e)) {
+            if (slot < (unsigned int)kHistWords) {
+              clist[slot] = (unsigned int)(i + e);
+              ckey[slot] = kr[u][e];
+            }
+            slot++;
+          }
+        }
+      }
+    }
+  }
+  n_above = wave_sum(n_above);
+  __syncthreads();
+  const unsigned int n_cand = *ccount;
+  if (n_cand <= (unsigned int)kHistWords) {
+#pragma unroll 1
+    for (int pass = 2; pass < 4; pass++) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) tot[tid] = 0u;
+      __syncthreads();
+      for (unsigned int c = tid; c < n_cand; c += kTkThreads) {
+        const unsigned int key = ckey[c];
+        if ((key >> (shift + 8)) == prefix) atomicAdd(&tot[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      scan_digit(tot, misc, k_rem, wave, lane);
+      prefix = (prefix << 8) | misc[0];
+      k_rem -= (int)misc[1];
+      __syncthreads();
+    }
+    if (lane == 0) {
+      misc[2 + wave] = n_above;
+      misc[2 + kTkWaves + wave] = 0u;
+    }
+    __syncthreads();
+    for (unsigned int c = tid; c < n_cand; c += kTkThreads) {
+      const unsigned int key = ckey[c];
+      const unsigned int w = clist[c] / (unsigned int)segw;
+      if (key > prefix) atomicAdd(&misc[2 + w], 1u);
+      else if (key == prefix) atomicAdd(&misc[2 + kTkWaves + w], 1u);
+    }
+    __syncthreads();
+  } else {
+    reg_hist_passes(2, 4);
+    unsigned int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < kRegBlocks; u++) {
+      if (u < nb) {
+        const int i = s0 + kSeg * u + 4 * lane;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const bool v = i + e < s1;
+          n_gt += (v && kr[u][e] > prefix) ? 1u : 0u;
+          n_eq += (v && kr[u][e] == prefix) ? 1u : 0u;
+        }
+      }
+    }
+    n_gt = wave_sum(n_gt);
+    n_eq = wave_sum(n_eq);
+    if (lane == 0) {
+      misc[2 + wave] = n_gt;
+      misc[2 + kTkWaves + wave] = n_eq;
+    }
+    __syncthreads();
+  }
+  const unsigned int tau = prefix;  // the k-th largest key; k_rem keys equal to tau are taken
+
+  // ---- ordered compaction into the (free) histogram area, then k contiguous stores
+  unsigned int gt_before = 0, eq_before = 0;
+  for (int w2 = 0; w2 < wave; w2++) {
+    gt_before += misc[2 + w2];
+    eq_before += misc[2 + kTkWaves + w2];
+  }
+  unsigned int e_run = eq_before;
+  unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
+  unsigned int* stage = hist;  // [k] positions (k <= kHistWords - 1; the last word is the dummy slot)
+#pragma unroll
+  for (int u = 0; u < kRegBlocks; u++) {
+    if (u < nb) {
+      const int i = s0 + kSeg * u + 4 * lane;
+      unsigned int eq_mask = 0, gt_mask = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool v = i + e < s1;
+        gt_mask |= (v && kr[u][e] > tau) ? (1u << e) : 0u;
+        eq_mask |= (v && kr[u][e] == tau) ? (1u << e) : 0u;
+      }
+      unsigned int sel_mask = gt_mask;
+      if (__ballot(eq_mask != 0) != 0) {  // keys equal to tau: the first k_rem of them in row order
+        unsigned int e_before, e_total;
+        lane_scan3((unsigned int)__popc(eq_mask), &e_before, &e_total);
+        unsigned int er = e_run + e_before;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if (eq_mask & (1u << e)) {
+            if (er < (unsigned int)k_rem) sel_mask |= 1u << e;
+            er++;
+          }
+        }
+        e_run += e_total;
+      }
+      unsigned int s_before, s_total;
+      lane_scan3((unsigned int)__popc(sel_mask), &s_before, &s_total);
+      unsigned int op = p_run + s_before;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const bool sel = (sel_mask & (1u << e)) && op < (unsigned int)k;
+        stage[sel ? op : kHistWords - 1] = (unsigned int)(i + e);
+        op += (sel_mask >> e) & 1u;
+      }
+      p_run += s_total;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < k; j += kTkThreads) out_idx[j] = (int)stage[j];
+}
+
 // Fallback for rows the LDS-resident kernels cannot take: every pass re-reads the row from memory.
 __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* __restrict__ scores, int64_t ld,
                                                                    int n_q, int n_kv, int k,
@@ -631,6 +869,10 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   if (p.mode == TopkPlan::kUncached) {
     hipLaunchKernelGGL(topk_uncached_kernel, dim3(n_q, B), dim3(kTkThreads), lds_bytes(0), stream, scores, ld, n_q,
                        n_kv, k, idx);
+    return hipGetLastError();
+  }
+  if (p.mode == TopkPlan::kSingle && rows16 && n_kv <= kRegKeys && k < kHistWords) {
+    hipLaunchKernelGGL(topk_reg_kernel, dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld, n_q, n_kv, k, idx);
     return hipGetLastError();
   }
   if (p.mode == TopkPlan::kSingle) {

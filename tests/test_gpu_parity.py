@@ -189,6 +189,34 @@ def test_topk_adversarial_rows(orc, dsa):
     assert gi[0].tolist() == list(range(k))
 
 
+def test_topk_long_rows_many_rows_bit_exact(orc, dsa):
+    """Many rows of up to 32768 keys with aligned row starts (the register-resident kernel): whole
+    16-block wave segments, ragged row ends, and rows whose candidates overflow the list (ties)."""
+    n_kv, n_q, k = 32768, 260, 2048
+    ld = n_kv + 4
+    gen = np.random.default_rng(11)
+    s = gen.standard_normal((1, n_q, ld)).astype(np.float32)
+    pos = np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    for r in range(0, n_q, 13):
+        kind = (r // 13) % 4
+        if kind == 0:
+            s[0, r] = 0.25                                                   # all equal
+        elif kind == 1:
+            s[0, r] = gen.choice(np.array([-2.0, 0.0, 3.0, 3.0], np.float32), ld)  # long runs of ties
+        elif kind == 2:
+            s[0, r] = np.where(gen.random(ld) < 0.5, -0.0, 0.0)              # signed zeros
+        else:
+            s[0, r, ::2] = -np.inf                                           # -inf mixed in
+    for r, p in enumerate(pos):
+        s[0, r, p + 1:] = np.nan  # never to be read
+    idx = dsa.topk(torch.from_numpy(s).to(DEV), n_kv, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    oi, _ = orc.topk(s[0], pos, k)
+    for r in range(n_q):
+        assert np.array_equal(gi[r], oi[r]), r
+
+
 # ------------------------------------------------------------------------------------------ attention
 
 def _rand_idx(gen, n_kv, k, n_valid, interleave=False):
