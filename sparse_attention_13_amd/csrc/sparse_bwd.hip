@@ -657,7 +657,9 @@ __global__ __launch_bounds__(256) void sbwd_reduce_kernel(const uint16_t* __rest
                                                           float* __restrict__ dkv) {
   __shared__ __attribute__((aligned(16))) float red[4][kBD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int key = (int)blockIdx.x;
+  // the most-selected keys of a causal chunk are its most recent ones (the highest indices): they are
+  // dispatched first, so that the long sums do not start last and trail the grid
+  const int key = n_keys - 1 - (int)blockIdx.x;
   const int n = count[key];
   if (n == 0) return;  // whole workgroup
   const int* lp = list + offs[key];
