@@ -339,9 +339,17 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int32_t* __restrict
   for (int i = threadIdx.x; i < W; i += 256) words[i] = 0u;
   __syncthreads();
   const int32_t* sel = idx + row * k_sel;
-  for (int e = threadIdx.x; e < k_sel; e += 256) {
-    const int s = sel[e];
-    if (s >= 0 && s <= pos) atomicOr(&words[s >> 5], 1u << (s & 31));
+  // eight entries per thread and round, all loads in flight before the first is used
+  for (int e0 = 0; e0 < k_sel; e0 += 8 * 256) {
+    int sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int e = e0 + 256 * u + (int)threadIdx.x;
+      sv[u] = e < k_sel ? sel[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (sv[u] >= 0 && sv[u] <= pos) atomicOr(&words[sv[u] >> 5], 1u << (sv[u] & 31));
   }
   __syncthreads();
   uint32_t* mrow = mask + row * W;
