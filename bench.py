@@ -5,12 +5,15 @@ One step = one pass of the whole path over each workload the headline metric nam
   * prefill, 1 sequence of 32768 tokens (all tokens are queries), indexer H_I=64 x d_I=128 in fp8,
     top-2048 selection, sparse MLA (128 heads, 576/512) in bf16;
   * decode, 64 sequences x one query against 131072 cached tokens, same shapes.
-Each workload runs its three stages (indexer -> top-k -> sparse attention) on one stream through the
-C ABI, with HIP events between the stages; inputs are generated on the GPU before the timed region.
+Each workload is one call of the exported entry point (dsa_forward_prefill, dsa_forward_decode) on one
+stream, timed with HIP events around the call; inputs are generated on the GPU before the timed region.
+The same work is then run as separate stage calls (indexer -> top-k -> sparse attention) with events
+between them, for the per-kernel durations behind the roofline figures.
 
 Prints ONE JSON line: value = prefill tokens/s at 32K (whole job, one GPU); decode queries/s, per-stage
-times and roofline fractions are in the same line.  The oracle (plain C on the host cores) is timed on a
-bounded sample of rows and extrapolated with the per-row work model.
+times and roofline fractions, the prefill 8K and chunked 128K configurations, and a parity summary against
+the oracle are in the same line.  The oracle (plain C on the host cores) is timed on a bounded sample of
+rows and extrapolated with the per-row work model.
 """
 from __future__ import annotations
 
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--no-proj", action="store_true", help="skip the MQA-mode projection measurement")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the prefill 8K and chunked 128K measurements")
     ap.add_argument("--no-warmup-loss", action="store_true", help="skip the indexer warm-up loss measurement")
     ap.add_argument("--no-sparse-bwd", action="store_true", help="skip the sparse training backward measurement")
     ap.add_argument("--mha-lens", default="4096,8192,12288,16384",
@@ -118,6 +123,24 @@ def causal_work(L: int, n_q: int, k: int):
     return pairs, entries
 
 
+def prefill_roofline_ms(L: int, n_q: int, k: int) -> float:
+    """Roofline time of one prefill call (the last n_q of L tokens are queries): indexer flops at the FP8 peak,
+    the score matrix written and read plus the selection written at the HBM peak, attention flops at the bf16
+    peak."""
+    pairs, entries = causal_work(L, n_q, k)
+    return (pairs * IDX_FLOP_PER_PAIR / (PEAK_FP8_TFLOPS * 1e12) + (2 * pairs * 4 + n_q * k * 4) / (PEAK_HBM_GBS * 1e9)
+            + entries * ATT_FLOP_PER_ENTRY / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
+
+
+def decode_bytes(B: int, S: int, k: int):
+    """HBM bytes of one decode step per stage: indexer (keys, key scales, scores written, q and w), top-k
+    (scores read, selection written), attention (selected rows, selection read, q, out)."""
+    i_bytes = B * S * (128 + 4 + 4) + B * 64 * (128 + 8)
+    k_bytes = B * S * 4 + B * k * 4
+    a_bytes = B * k * 1152 + B * 128 * 576 * 2 + B * 128 * 512 * 2 + B * k * 4
+    return i_bytes, k_bytes, a_bytes
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,7 +150,6 @@ def main():
     if args.calib_copy:
         calib_copy()
         return
-    import numpy as np
     import torch
 
     from sparse_attention_13_amd import dsa, synth
@@ -137,104 +159,123 @@ def main():
     stream = torch.cuda.current_stream()
     k = args.k
     sm = 1.0 / math.sqrt(576)
-    result = {}
 
-    def timed(stages, steps):
-        """Run `stages` (list of (name, fn)) `steps` times with events between them; per-stage mean ms."""
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-        acc = [0.0] * len(stages)
+    def timed(calls, steps):
+        """Run `calls` (list of (name, fn)) `steps` times with events between them; per-call mean ms."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        acc = [0.0] * len(calls)
         for _ in range(steps):
             ev[0].record(stream)
-            for i, (_, fn) in enumerate(stages):
+            for i, (_, fn) in enumerate(calls):
                 fn()
                 ev[i + 1].record(stream)
             torch.cuda.synchronize()
-            for i in range(len(stages)):
+            for i in range(len(calls)):
                 acc[i] += ev[i].elapsed_time(ev[i + 1])
-        return {name: acc[i] / steps for i, (name, _) in enumerate(stages)}
+        return {name: acc[i] / max(steps, 1) for i, (name, _) in enumerate(calls)}
 
-    # ------------------------------------------------------------------ prefill workload
+    # ------------------------------------------------------------------ prefill workload (32K, all tokens queries)
     pre = None
     if args.only in (None, "prefill"):
         L = args.prefill_len
         print(f"[bench] generating prefill inputs L={L}", file=sys.stderr, flush=True)
         x = synth.prefill(L, seed=0, device=dev, n_needles=256, needle_layout="random")
+        q8, qs, k8, ks, w = (x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None])
+        q, kv = x["q"][None], x["kv"][None]
+        out = torch.empty((1, L, 128, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        idx_f = torch.empty((1, L, k), dtype=torch.int32, device=dev)
+        fws = torch.empty(dsa.forward_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16), dtype=torch.uint8,
+                          device=dev)
+        # stage-by-stage buffers (the per-kernel breakdown and the parity sample)
         ld = ((L + 63) // 64) * 64
         scores = torch.empty((1, L, ld), dtype=torch.float32, device=dev)
         idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
-        out = torch.empty((1, L, 128, 512), dtype=torch.bfloat16, device=dev)
-        lse = torch.empty((1, L, 128), dtype=torch.float32, device=dev)
+        s_out = torch.empty_like(out)
+        s_lse = torch.empty_like(lse)
         tk_ws = torch.empty(max(dsa.topk_workspace_size(1, L, L, k), 256), dtype=torch.uint8, device=dev)
         ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(1, L, L, 128, 576, 512, k, dsa.DSA_BF16)
         ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
-        q8, qs, k8, ks, w = (x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None])
-        q, kv = x["q"][None], x["kv"][None]
-        pre_stages = [
-            ("indexer", lambda: dsa.indexer_scores(q8, qs, k8, ks, w, scores)),
-            ("topk", lambda: dsa.topk(scores, L, k, idx=idx, workspace=tk_ws)),
-            ("sparse_mla", lambda: dsa.sparse_mla_attn(q, kv, idx, 512, sm, out=out, lse=lse, workspace=ws)),
-        ]
-        pre = dict(L=L, stages=pre_stages, x=x, idx=idx, out=out, lse=lse)
+        pre = dict(L=L, x=x, idx=idx, out=s_out, lse=s_lse, scores=scores,
+                   forward=("prefill", lambda: dsa.forward(q8, qs, k8, ks, w, q, kv, k, 512, sm, out=out, lse=lse,
+                                                           idx_out=idx_f, workspace=fws)),
+                   stages=[("prefill.indexer", lambda: dsa.indexer_scores(q8, qs, k8, ks, w, scores)),
+                           ("prefill.topk", lambda: dsa.topk(scores, L, k, idx=idx, workspace=tk_ws)),
+                           ("prefill.sparse_mla", lambda: dsa.sparse_mla_attn(q, kv, idx, 512, sm, out=s_out, lse=s_lse,
+                                                                              workspace=ws))])
 
-    # ------------------------------------------------------------------ decode workload
+    # ------------------------------------------------------------------ decode workload (64 x 1 query over 128K)
     dec = None
     if args.only in (None, "decode"):
         B, S = args.decode_batch, args.decode_len
         print(f"[bench] generating decode inputs B={B} S={S}", file=sys.stderr, flush=True)
         y = synth.decode(B, S, seed=0, device=dev)
+        d_out = torch.empty((B, 128, 512), dtype=torch.bfloat16, device=dev)
+        d_lse = torch.empty((B, 128), dtype=torch.float32, device=dev)
+        d_idx_f = torch.empty((B, k), dtype=torch.int32, device=dev)
+        d_fws = torch.empty(dsa.forward_workspace_size(B, 1, S, 128, 576, 512, k, dsa.DSA_BF16), dtype=torch.uint8,
+                            device=dev)
         ld = ((S + 63) // 64) * 64
-        d_scores = torch.empty((B, 1, ld), dtype=torch.float32, device=dev)
-        d_idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
-        d_out = torch.empty((B, 1, 128, 512), dtype=torch.bfloat16, device=dev)
-        d_lse = torch.empty((B, 1, 128), dtype=torch.float32, device=dev)
-        d_tk_ws = torch.empty(max(dsa.topk_workspace_size(B, 1, S, k), 256), dtype=torch.uint8, device=dev)
-        ws_n = dsa.lib().dsa_sparse_mla_attn_workspace_size(B, 1, S, 128, 576, 512, k, dsa.DSA_BF16)
+        d_scores = torch.empty((B, ld), dtype=torch.float32, device=dev)
+        d_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+        s_dout = torch.empty_like(d_out)
+        s_dlse = torch.empty_like(d_lse)
+        d_tk_ws = torch.empty(max(int(dsa.lib().dsa_topk_decode_workspace_size(B, S, k)), 256), dtype=torch.uint8,
+                              device=dev)
+        ws_n = int(dsa.lib().dsa_sparse_mla_attn_decode_workspace_size(B, S, 128, 576, 512, k, dsa.DSA_BF16))
         d_ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
-        yq8, yqs, yk8, yks, yw = (y["q8"][:, None], y["q_scale"][:, None], y["k8"], y["k_scale"], y["w"][:, None])
-        yq, ykv = y["q"][:, None], y["kv"]
-        dec_stages = [
-            ("indexer", lambda: dsa.indexer_scores(yq8, yqs, yk8, yks, yw, d_scores)),
-            ("topk", lambda: dsa.topk(d_scores, S, k, idx=d_idx, workspace=d_tk_ws)),
-            ("sparse_mla", lambda: dsa.sparse_mla_attn(yq, ykv, d_idx, 512, sm, out=d_out, lse=d_lse, workspace=d_ws)),
-        ]
-        dec = dict(B=B, S=S, stages=dec_stages, y=y, idx=d_idx, out=d_out, lse=d_lse)
+        yq8, yqs, yk8, yks, yw, yq, ykv = y["q8"], y["q_scale"], y["k8"], y["k_scale"], y["w"], y["q"], y["kv"]
+        dec = dict(B=B, S=S, y=y, idx=d_idx, out=s_dout, lse=s_dlse, scores=d_scores,
+                   forward=("decode", lambda: dsa.forward(yq8, yqs, yk8, yks, yw, yq, ykv, k, 512, sm, decode=True,
+                                                          out=d_out, lse=d_lse, idx_out=d_idx_f, workspace=d_fws)),
+                   stages=[("decode.indexer", lambda: dsa.indexer_scores_decode(yq8, yqs, yk8, yks, yw, d_scores)),
+                           ("decode.topk", lambda: dsa.topk_decode(d_scores, S, k, idx=d_idx, workspace=d_tk_ws)),
+                           ("decode.sparse_mla", lambda: dsa.sparse_mla_attn_decode(yq, ykv, d_idx, 512, sm,
+                                                                                    out=s_dout, lse=s_dlse,
+                                                                                    workspace=d_ws))])
 
-    stages_all = (pre["stages"] if pre else []) + (dec["stages"] if dec else [])
-    names = [("prefill." if pre and i < 3 else "decode.") + n for i, (n, _) in enumerate(stages_all)]
-    stages_named = list(zip(names, [f for _, f in stages_all]))
-
+    # ------------------------------------------------------------------ the timed steps: the forward entry points
+    step_calls = [w_["forward"] for w_ in (pre, dec) if w_]
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    timed(stages_named, max(args.warmup, 0)) if args.warmup > 0 else None
+    if args.warmup > 0:
+        timed(step_calls, args.warmup)
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    st = timed(stages_named, args.steps)
+    st = timed(step_calls, args.steps)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    wall = (time.perf_counter() - t0) / max(args.steps, 1) * 1e3
+    # per-stage breakdown: the same work as separate stage calls (one kernel launch per stage at these shapes,
+    # except the split attention and top-k at decode), events between them
+    stage_calls = (pre["stages"] if pre else []) + (dec["stages"] if dec else [])
+    print(f"[bench] stage breakdown, {args.steps} steps", file=sys.stderr, flush=True)
+    timed(stage_calls, 1)
+    sst = timed(stage_calls, args.steps)
 
-    out = {"metric": "DSA prefill tokens/s at 32K ctx + decode queries/s at 128K ctx; % roofline",
+    res = {"metric": "DSA prefill tokens/s at 32K ctx + decode queries/s at 128K ctx; % roofline",
            "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(sum(st.values()), 4), "wall_ms_per_step": round(wall, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16",
            "data": "synthetic (seeded; N(0,1) inputs, fp8 e4m3 indexer with amax scales, needles)",
            "config": {"workload": ("prefill 1x32768 tokens (all queries) + decode 64x1 query over 131072 "
-                                   "cached tokens; H_I=64 d_I=128 fp8, k=2048, 128 heads d_qk=576 d_v=512 bf16")}}
+                                   "cached tokens; H_I=64 d_I=128 fp8, k=2048, 128 heads d_qk=576 d_v=512 bf16"),
+                      "timed": "dsa_forward_prefill + dsa_forward_decode per step"}}
     rooflines = {}
     if pre:
         L = pre["L"]
         pairs, entries = causal_work(L, L, k)
-        t_i, t_k, t_a = st["prefill.indexer"], st["prefill.topk"], st["prefill.sparse_mla"]
-        t_tot = t_i + t_k + t_a
+        t_fwd = st["prefill"]
+        t_i, t_k, t_a = sst["prefill.indexer"], sst["prefill.topk"], sst["prefill.sparse_mla"]
         idx_tf = pairs * IDX_FLOP_PER_PAIR / (t_i * 1e-3) / 1e12
         tk_bytes = pairs * 4 + L * k * 4
         tk_gbs = tk_bytes / (t_k * 1e-3) / 1e9
         att_tf = entries * ATT_FLOP_PER_ENTRY / (t_a * 1e-3) / 1e12
-        roof_ms = (pairs * IDX_FLOP_PER_PAIR / (PEAK_FP8_TFLOPS * 1e12) + tk_bytes / (PEAK_HBM_GBS * 1e9)
-                   + entries * ATT_FLOP_PER_ENTRY / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
-        out["value"] = round(L / (t_tot * 1e-3), 1)
-        out["prefill"] = {"tokens_per_s": out["value"], "ms": round(t_tot, 4),
-                          "roofline_ms": round(roof_ms, 4), "frac_of_roofline": round(roof_ms / t_tot, 4),
+        roof_ms = prefill_roofline_ms(L, L, k)
+        res["value"] = round(L / (t_fwd * 1e-3), 1)
+        res["prefill"] = {"tokens_per_s": res["value"], "ms": round(t_fwd, 4), "roofline_ms": round(roof_ms, 4),
+                          "frac_of_roofline": round(roof_ms / t_fwd, 4),
                           "stages_ms": {"indexer": round(t_i, 4), "topk": round(t_k, 4), "sparse_mla": round(t_a, 4)},
+                          "stages_sum_ms": round(t_i + t_k + t_a, 4),
                           "indexer": {"TFLOP/s": round(idx_tf, 1), "frac_fp8_peak": round(idx_tf / PEAK_FP8_TFLOPS, 4)},
                           "topk": {"GB/s": round(tk_gbs, 1), "frac_hbm": round(tk_gbs / PEAK_HBM_GBS, 4)},
                           "sparse_mla": {"TFLOP/s": round(att_tf, 1),
@@ -249,48 +290,106 @@ def main():
                                                  "frac": round(att_tf / PEAK_BF16_TFLOPS, 4), "traffic": None})
     if dec:
         B, S = dec["B"], dec["S"]
-        t_i, t_k, t_a = st["decode.indexer"], st["decode.topk"], st["decode.sparse_mla"]
-        t_tot = t_i + t_k + t_a
-        i_bytes = B * S * (128 + 4 + 4) + B * 64 * (128 + 8)
-        k_bytes = B * S * 4 + B * k * 4
-        a_bytes = B * k * 1152 + B * 128 * 576 * 2 + B * 128 * 512 * 2 + B * k * 4
+        t_fwd = st["decode"]
+        t_i, t_k, t_a = sst["decode.indexer"], sst["decode.topk"], sst["decode.sparse_mla"]
+        i_bytes, k_bytes, a_bytes = decode_bytes(B, S, k)
         roof_ms = (i_bytes + k_bytes + a_bytes) / (PEAK_HBM_GBS * 1e9) * 1e3
         i_gbs = i_bytes / (t_i * 1e-3) / 1e9
         a_gbs = a_bytes / (t_a * 1e-3) / 1e9
-        out["decode"] = {"queries_per_s": round(B / (t_tot * 1e-3), 1), "unit": "queries/s", "ms": round(t_tot, 4),
-                         "roofline_ms": round(roof_ms, 4), "frac_of_hbm_roofline": round(roof_ms / t_tot, 4),
+        res["decode"] = {"queries_per_s": round(B / (t_fwd * 1e-3), 1), "unit": "queries/s", "ms": round(t_fwd, 4),
+                         "roofline_ms": round(roof_ms, 4), "frac_of_hbm_roofline": round(roof_ms / t_fwd, 4),
                          "stages_ms": {"indexer": round(t_i, 4), "topk": round(t_k, 4), "sparse_mla": round(t_a, 4)},
+                         "stages_sum_ms": round(t_i + t_k + t_a, 4),
                          "indexer": {"GB/s": round(i_gbs, 1), "frac_hbm": round(i_gbs / PEAK_HBM_GBS, 4)},
-                         "topk": {"GB/s": round(k_bytes / (t_k * 1e-3) / 1e9, 1)},
+                         "topk": {"GB/s": round(k_bytes / (t_k * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(k_bytes / (t_k * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                          "sparse_mla": {"GB/s": round(a_gbs, 1), "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4)}}
         rooflines["decode.indexer"] = (t_i, {"bound": "hbm", "achieved": round(i_gbs, 1), "peak": PEAK_HBM_GBS,
                                              "unit": "GB/s", "frac": round(i_gbs / PEAK_HBM_GBS, 4), "traffic": None})
-        if out["value"] is None:
-            out["value"] = out["decode"]["queries_per_s"]
-            out["unit"] = "queries/s"
+        if res["value"] is None:
+            res["value"] = res["decode"]["queries_per_s"]
+            res["unit"] = "queries/s"
     # dominant kernel = the stage with the largest time in the step
-    dom = max(rooflines.items(), key=lambda kv: kv[1][0]) if rooflines else None
+    dom = max(rooflines.items(), key=lambda kv_: kv_[1][0]) if rooflines else None
     if dom:
         roof = dict(dom[1][1], kernel=dom[0])
         roof["traffic"] = measured_traffic(dom[0]) if dom[0] in KERNEL_SOURCES else None
-        out["roofline"] = roof
+        res["roofline"] = roof
 
-    # ------------------------------------------------------------------ CPU oracle baseline (bounded sample)
+    # ------------------------------------------------------------------ CPU oracle baseline and parity sample
     if not args.no_cpu_baseline and pre:
-        out["cpu_baseline"] = cpu_baseline_prefill(pre, k, sm)
+        base, par = cpu_baseline_prefill(pre, k, sm)
+        res["cpu_baseline"] = base
+        res["parity"] = {"prefill_32k": par}
         if dec:
-            out["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, k, sm)
+            dbase, dpar = cpu_baseline_decode(dec, k, sm)
+            res["decode"]["cpu_baseline"] = dbase
+            res["parity"]["decode_128k"] = dpar
+    del pre, dec
+    torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------------ further prefill configurations
+    if args.only in (None, "prefill") and not args.no_extra_prefill:
+        res["prefill_8k"] = prefill_leg(8192, 1, k, dev, stream, max(args.steps, 3), n_needles=64, layout="random")
+        res["chunked_128k"] = prefill_leg(131072, 16, k, dev, stream, max(2, args.steps // 4), n_needles=1024,
+                                          layout="even")
     # ------------------------------------------------------------------ masked MHA mode (short prefill)
     if args.only in (None, "prefill") and args.mha_lens:
-        out["masked_mha"] = masked_mha_sweep([int(v) for v in args.mha_lens.split(",")], k, dev, stream)
+        res["masked_mha"] = masked_mha_sweep([int(v) for v in args.mha_lens.split(",")], k, dev, stream)
     if args.only in (None, "prefill") and not args.no_proj:
-        out["mla_projections"] = projections_bench(args.prefill_len, dev, stream)
+        res["mla_projections"] = projections_bench(args.prefill_len, dev, stream)
     if args.only in (None, "prefill") and not args.no_warmup_loss:
-        out["warmup_loss"] = warmup_bench(args.prefill_len, dev, stream)
+        res["warmup_loss"] = warmup_bench(args.prefill_len, dev, stream)
     if args.only in (None, "prefill") and not args.no_sparse_bwd:
-        out["sparse_backward"] = sparse_backward_bench(args.prefill_len, k, dev, stream)
-    print(json.dumps(out), flush=True)
+        res["sparse_backward"] = sparse_backward_bench(args.prefill_len, k, dev, stream)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_leg(L, n_chunks, k, dev, stream, steps, n_needles, layout):
+    """One prefill of L tokens as n_chunks calls of dsa_forward_prefill (chunk c: queries c*L/n_chunks ..
+    (c+1)*L/n_chunks - 1 over the keys 0 .. (c+1)*L/n_chunks - 1), timed per whole prefill with events around
+    the calls; reported with the roofline of the same calls."""
+    import torch
+
+    from sparse_attention_13_amd import dsa, synth
+
+    C = L // n_chunks
+    print(f"[bench] prefill leg L={L} in {n_chunks} call(s) of {C} queries", file=sys.stderr, flush=True)
+    x = synth.prefill(L, seed=0, device=dev, n_needles=n_needles, needle_layout=layout)
+    sm = 1.0 / math.sqrt(576)
+    out = torch.empty((1, C, 128, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, C, 128), dtype=torch.float32, device=dev)
+    fws = torch.empty(dsa.forward_workspace_size(1, C, L, 128, 576, 512, k, dsa.DSA_BF16), dtype=torch.uint8,
+                      device=dev)
+    views = []
+    for c in range(n_chunks):
+        lo, hi = c * C, (c + 1) * C
+        views.append((x["q8"][None, lo:hi], x["q_scale"][None, lo:hi], x["k8"][None, :hi], x["k_scale"][None, :hi],
+                      x["w"][None, lo:hi], x["q"][None, lo:hi], x["kv"][None, :hi]))
+
+    def run():
+        for v in views:
+            dsa.forward(*v, k, 512, sm, out=out, lse=lse, workspace=fws)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        ev[0].record(stream)
+        run()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ts.append(ev[0].elapsed_time(ev[1]))
+    t = sorted(ts)[len(ts) // 2]
+    roof = sum(prefill_roofline_ms((c + 1) * C, C, k) for c in range(n_chunks))
+    res = {"workload": (f"prefill 1x{L} tokens as {n_chunks} dsa_forward_prefill call(s) of {C} queries; "
+                        f"{n_needles} needles ({layout}); indexer 64x128 fp8, k={k}, 128 heads 576/512 bf16"),
+           "ms": round(t, 4), "tokens_per_s": round(L / (t * 1e-3), 1), "roofline_ms": round(roof, 4),
+           "frac_of_roofline": round(roof / t, 4), "steps": steps}
+    del x, views, out, lse, fws
+    torch.cuda.empty_cache()
+    return res
 
 
 SBWD_FLOP_PER_ENTRY = 2 * 128 * (576 + 512 + 576 + 576 + 512)  # S, dP, dq, dK, dV per selected entry
@@ -515,12 +614,38 @@ def masked_mha_sweep(lens, k, dev, stream):
     return res
 
 
+def _parity_summary(oracle, parity, g_scores, o_scores, mag, absmag, gi, res, g_out, g_lse, pos):
+    """Parity of the GPU's stage outputs on the sampled rows against the oracle's own run on the same rows:
+    indexer score errors (the asserted magnitude-relative bound and the plain relative figure), the selection
+    under the band rule, and the attention on the rows whose selection is identical."""
+    rep = parity.indexer_report(g_scores, o_scores, mag, absmag, pos)
+    ok, exact = parity.topk_band_match(gi, res["idx"], res["scores"], res["kth"], pos)
+    same = [r for r in range(len(pos)) if (gi[r] == res["idx"][r]).all()]
+    ratio, mx, lse_err = parity.attention_errors(g_out[same], res["out"][same], g_lse[same], res["lse"][same])
+    return {"rows": int(len(pos)), "indexer_entries": rep["n"],
+            "indexer_worst_over_bound": round(rep["worst_bound_ratio"], 4),
+            "indexer_rel_err_wellcond": float(f"{rep['rel_wellcond']:.3g}"),
+            "indexer_frac_wellcond": round(rep["frac_wellcond"], 4),
+            "indexer_rel_err_q999_all": float(f"{rep['rel_q999']:.3g}"),
+            "selection_band_ok_rows": int(ok), "selection_identical_rows": int(exact),
+            "selection_band_exchange_rows": int(ok - exact), "attention_rows_compared": len(same),
+            "attention_worst_over_bound": round(ratio, 4), "attention_max_abs_err": float(f"{mx:.3g}"),
+            "lse_max_abs_err": float(f"{lse_err:.3g}"),
+            "pass": bool(rep["worst_bound_ratio"] <= 1.0 and rep["rel_wellcond"] <= parity.IDX_REL and ok == len(pos)
+                         and ratio <= 1.0 and lse_err <= parity.LSE_ABS)}
+
+
 def cpu_baseline_prefill(pre, k, sm):
+    """The oracle timed on a bounded sample of the 32K prefill's query rows (full path per row), extrapolated
+    to every row with the per-row work model; the same rows then give the parity summary of the GPU's stage
+    outputs (scores, selection, attention)."""
     import numpy as np
     import torch
 
     import oracle
     from sparse_attention_13_amd import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
     L, x = pre["L"], pre["x"]
     gen = np.random.default_rng(0)
     fixed = np.concatenate([np.arange(0, 64), np.arange(k - 32, k + 32), np.arange(L - 64, L)])
@@ -534,37 +659,58 @@ def cpu_baseline_prefill(pre, k, sm):
     qb = oracle.bf16_to_f32(synth.bf16_bits(x["q"][rsel]))
     kvb = oracle.bf16_to_f32(synth.bf16_bits(x["kv"]))
     t0 = time.perf_counter()
-    oracle.forward(q_i, w, k_i, qb, kvb, rows, k, 512, sm)
+    res = oracle.forward(q_i, w, k_i, qb, kvb, rows, k, 512, sm)
     t = time.perf_counter() - t0
     work = lambda p: IDX_FLOP_PER_PAIR * (p + 1) + ATT_FLOP_PER_ENTRY * min(k, p + 1)
     w_sample = sum(work(int(p)) for p in rows)
     w_total = sum(work(p) for p in range(L))
     full_s = t * w_total / w_sample
-    return {"value": round(L / full_s, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    base = {"value": round(L / full_s, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": (f"{len(rows)} of {L} query rows (first 64, 64 around position k-1, last 64, the rest "
-                       f"uniform), "
-                       f"{t:.1f} s, extrapolated to all rows by the per-row work model"),
+                       f"uniform), {t:.1f} s, extrapolated to all rows by the per-row work model"),
             "sample_seconds": round(t, 2)}
+    _, mag, absmag = oracle.indexer(q_i, w, k_i, rows, ld=L, with_mag=True)
+    g_scores = pre["scores"][0, rsel, :L].cpu().numpy()
+    par = _parity_summary(oracle, parity, g_scores, res["scores"][:, :L], mag, absmag, pre["idx"][0, rsel].cpu().numpy(),
+                          res, pre["out"][0, rsel].float().cpu().numpy(), pre["lse"][0, rsel].cpu().numpy(), rows)
+    par["workload"] = "prefill 32K, the stage calls' outputs on the cpu_baseline rows"
+    return base, par
 
 
 def cpu_baseline_decode(dec, k, sm):
+    """The oracle's full decode path for a bounded number of sequences, and the parity summary of the GPU's
+    decode stage outputs on them."""
     import numpy as np
 
     import oracle
     from sparse_attention_13_amd import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
     y, S = dec["y"], dec["S"]
     nb = min(12, dec["B"])
     t_total = 0.0
+    pos = np.array([S - 1], np.int64)
+    acc = []
     for b in range(nb):
         q_i = oracle.dequant_e4m3(synth.u8(y["q8"][b:b + 1]), y["q_scale"][b:b + 1].cpu().numpy())
         k_i = oracle.dequant_e4m3(synth.u8(y["k8"][b]), y["k_scale"][b].cpu().numpy())
         qb = oracle.bf16_to_f32(synth.bf16_bits(y["q"][b:b + 1]))
         kvb = oracle.bf16_to_f32(synth.bf16_bits(y["kv"][b]))
+        w = y["w"][b:b + 1].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.forward(q_i, y["w"][b:b + 1].cpu().numpy(), k_i, qb, kvb, np.array([S - 1], np.int64), k, 512, sm)
+        res = oracle.forward(q_i, w, k_i, qb, kvb, pos, k, 512, sm)
         t_total += time.perf_counter() - t0
-    return {"value": round(nb / t_total, 4), "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
+        _, mag, absmag = oracle.indexer(q_i, w, k_i, pos, ld=S, with_mag=True)
+        acc.append((dec["scores"][b:b + 1, :S].cpu().numpy(), res, mag, absmag, dec["idx"][b:b + 1].cpu().numpy(),
+                    dec["out"][b:b + 1].float().cpu().numpy(), dec["lse"][b:b + 1].cpu().numpy()))
+    base = {"value": round(nb / t_total, 4), "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{nb} of {dec['B']} sequences, full path, {t_total:.1f} s"}
+    cat = lambda i: np.concatenate([a[i] for a in acc])
+    res = {key: np.concatenate([a[1][key] for a in acc]) for key in ("scores", "kth", "idx", "out", "lse")}
+    par = _parity_summary(oracle, parity, cat(0), res["scores"], cat(2), cat(3), cat(4), res, cat(5), cat(6),
+                          np.full(nb, S - 1, np.int64))
+    par["workload"] = f"decode 64x131072, the decode stage calls' outputs for {nb} sequences"
+    return base, par
 
 
 if __name__ == "__main__":

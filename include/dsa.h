@@ -29,8 +29,12 @@
  *   and a status other than DSA_OK is returned.  dsa_last_error() returns a text of the last
  *   failure on the calling thread.  No C++ exception crosses the ABI.
  * fp8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities).  Row scales must be finite and > 0.
- * Threading.  All entry points are reentrant; the only mutable global state is the thread-local
- *   error text.
+ * Softmax scale.  Every attention, backward and warm-up entry point takes sm_scale, which must be
+ *   finite and > 0 (the scores are multiplied by it inside the exponent); anything else returns
+ *   DSA_ERR_INVALID_ARG with nothing enqueued.
+ * Threading.  All entry points are reentrant.  Mutable global state: the thread-local error text,
+ *   and a per-device record that the top-k kernels' opt-in to the full 160 KiB of LDS was made
+ *   (an idempotent runtime call; two threads racing on it only repeat it).
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -115,7 +119,7 @@ size_t dsa_topk_workspace_size(int B, int n_q, int n_kv, int k);
  * q [B][n_q][H][d_qk], kv [B][n_kv][d_qk] (one latent row per token, shared by all H heads),
  * idx [B][n_q][k] int32 with entries -1 (skipped) or in [0, n_kv) (entries outside are skipped too),
  * out [B][n_q][H][d_v] in `dtype`, lse [B][n_q][H] fp32 or NULL.  A row with no valid entry gets
- * out = 0 and lse = -inf.
+ * out = 0 and lse = -inf.  sm_scale finite and > 0.
  * dtype = DSA_BF16: q, kv, out are bf16 (fp32 accumulation).  Fast path H = 128, d_qk = 576,
  *   d_v = 512 (CDNA4 bf16 matrix cores).
  * dtype = DSA_F32: q, kv, out fp32 (generic kernel: H <= 64, d_qk <= 256, d_v <= d_qk).
@@ -292,6 +296,51 @@ dsa_status_t dsa_forward_decode(const void* q_i, const float* q_i_scale, const v
 /* Workspace bytes for dsa_forward_prefill (n_q queries) or dsa_forward_decode (n_q = 1). */
 size_t dsa_forward_workspace_size(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k,
                                   dsa_dtype_t attn_dtype);
+
+/* ------------------------------------------------------------------------------------------------
+ * Decode stage entry points: the three stages for B sequences with one new query each (n_q = 1) at
+ * position n_kv - 1.  Each computes exactly what its general counterpart computes with n_q = 1 (same
+ * sections of the pages, same layouts with the n_q dimension of size 1, same errors); they exist so a
+ * decode step can be driven stage by stage through the kernels tuned for few long rows (keys split over
+ * many workgroups, the selection in two stages, split-k attention with a merge).  The general calls pick
+ * the same kernels when n_q = 1.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_indexer_scores_decode(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                       const float* w, int B, int n_kv, int H_I, int d_I, dsa_dtype_t dtype,
+                                       float* scores, int64_t ld_scores, void* stream);
+dsa_status_t dsa_topk_decode(const float* scores, int64_t ld_scores, int B, int n_kv, int k, int32_t* idx,
+                             void* workspace, size_t ws_bytes, void* stream);
+size_t dsa_topk_decode_workspace_size(int B, int n_kv, int k);
+dsa_status_t dsa_sparse_mla_attn_decode(const void* q, const void* kv, const int32_t* idx, int B, int n_kv,
+                                        int H, int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t dtype,
+                                        void* out, float* lse, void* workspace, size_t ws_bytes,
+                                        void* stream);
+size_t dsa_sparse_mla_attn_decode_workspace_size(int B, int n_kv, int H, int d_qk, int d_v, int k,
+                                                 dsa_dtype_t dtype);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_forward_prefill_masked_mha -- the short-prefill form of the path (velog summary, section 3.3
+ * Inference Cost: short prefills run MHA mode with a mask that reproduces the sparse selection;
+ * notes.yuuk.io, section on inference cost): dsa_indexer_scores -> dsa_topk -> dsa_masked_mha_attn on
+ * one stream.  The result equals the attention over the selected entries, in MHA form.
+ *
+ * Indexer inputs and idx_out as in dsa_forward_prefill; attention inputs as in dsa_masked_mha_attn
+ * (q [B][n_q][H][192], k [B][n_kv][H][192], v [B][n_kv][H][128] bf16, out [B][n_q][H][128] bf16, lse
+ * [B][n_q][H] fp32 or NULL), k_sel selected entries per query, n_kv <= 524288.  Which mode serves a
+ * given prefill length is the caller's choice: masked MHA pays per causal (query, key) pair, the sparse
+ * MQA path (dsa_forward_prefill) per selected entry, and the measured crossing is a prefill length of
+ * about 9K tokens at k_sel = 2048.
+ * workspace: at least dsa_forward_prefill_masked_mha_workspace_size(...) bytes, 256-byte aligned (score
+ *   rows [B][n_q][ld] with ld = n_kv rounded up to 64, the selection, the top-k candidates and the
+ *   selection bitmask).
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_forward_prefill_masked_mha(const void* q_i, const float* q_i_scale, const void* k_i,
+                                            const float* k_i_scale, const float* w, const void* q, const void* k,
+                                            const void* v, int B, int n_q, int n_kv, int H_I, int d_I, int H,
+                                            int d_qk, int d_v, int k_sel, float sm_scale, dsa_dtype_t idx_dtype,
+                                            dsa_dtype_t attn_dtype, void* out, float* lse, int32_t* idx_out,
+                                            void* workspace, size_t ws_bytes, void* stream);
+size_t dsa_forward_prefill_masked_mha_workspace_size(int B, int n_q, int n_kv, int k_sel);
 
 #ifdef __cplusplus
 }

@@ -131,7 +131,8 @@ dsa_status_t plan_attn(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k
 dsa_status_t check_attn_ptrs(const void* q, const void* kv, const int32_t* idx, const void* out, float sm_scale,
                              const AttnPlan& p, const void* ws, size_t ws_bytes) {
   if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "attn: null q, kv, idx or out");
-  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "attn: sm_scale must be finite");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "attn: sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
   if (p.fast && !(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16)))
     return fail(DSA_ERR_INVALID_ARG, "attn: bf16 path needs 16-byte aligned q, kv and out");
   if (p.ws > 0) {
@@ -206,6 +207,27 @@ dsa_status_t forward(const void* q_i, const float* q_i_scale, const void* k_i, c
   if (st != DSA_OK) return st;
   return run_attn(q, kv, idx, B, n_q, n_kv, H, d_qk, d_v, k, sm_scale, out, lse, L.attn,
                   L.attn.ws ? ws + L.off_attn : nullptr, stream);
+}
+
+// Workspace of the masked-MHA-mode forward: scores, selection, top-k candidates, selection bitmask.
+struct MhaFwdLayout {
+  int64_t ld = 0;
+  size_t off_idx = 0, off_topk = 0, off_mask = 0, total = 0;
+  dsa::TopkPlan topk;
+};
+
+dsa_status_t plan_forward_mha(int B, int n_q, int n_kv, int k_sel, MhaFwdLayout* L) {
+  if (B < 1 || n_q < 1 || n_kv < 1 || k_sel < 1) return fail(DSA_ERR_INVALID_ARG, "forward_mha: sizes must be positive");
+  if (n_q > n_kv) return fail(DSA_ERR_INVALID_ARG, "forward_mha: n_q=%d exceeds n_kv=%d", n_q, n_kv);
+  if (k_sel > kMaxTopK) return fail(DSA_ERR_INVALID_ARG, "forward_mha: k=%d exceeds %d", k_sel, kMaxTopK);
+  if (n_kv > kMhaMaxKeys) return fail(DSA_ERR_UNSUPPORTED, "forward_mha: n_kv=%d exceeds %d", n_kv, kMhaMaxKeys);
+  L->ld = (int64_t)align_up((size_t)n_kv, 64);
+  L->off_idx = align_up((size_t)B * n_q * L->ld * sizeof(float), 256);
+  L->topk = dsa::plan_topk(B, n_q, n_kv, k_sel);
+  L->off_topk = align_up(L->off_idx + (size_t)B * n_q * k_sel * sizeof(int32_t), 256);
+  L->off_mask = L->off_topk + align_up(L->topk.ws, 256);
+  L->total = L->off_mask + align_up((size_t)B * n_q * dsa::mha_mask_words(n_kv) * 4, 256);
+  return DSA_OK;
 }
 
 }  // namespace
@@ -290,7 +312,8 @@ dsa_status_t dsa_sparse_mla_backward(const void* q, const void* kv, const int32_
     return fail(DSA_ERR_UNSUPPORTED, "sparse_backward: k <= 2048, n_kv <= 2^21, B * n_kv <= 2^26");
   if (!q || !kv || !idx || !out || !lse || !dout || !dq || !dkv)
     return fail(DSA_ERR_INVALID_ARG, "sparse_backward: null pointer");
-  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "sparse_backward: sm_scale must be finite");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "sparse_backward: sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
   if (!(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16) && aligned(dout, 16)))
     return fail(DSA_ERR_INVALID_ARG, "sparse_backward: q, kv, out, dout must be 16-byte aligned");
   const size_t need = dsa::sbwd_workspace_bytes(B, n_q, n_kv, k);
@@ -321,7 +344,8 @@ dsa_status_t dsa_warmup_loss(const void* q, const void* kv, const float* lse, in
   if (B > 65535 || n_kv > (1 << 21)) return fail(DSA_ERR_UNSUPPORTED, "warmup_loss: B <= 65535, n_kv <= 2^21");
   if (!q || !kv || !lse || !scores || !target || !loss) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: null pointer");
   if (ld_scores < n_kv || ld_target < n_kv) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: ld below n_kv");
-  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: sm_scale must be finite");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "warmup_loss: sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
   if (!(aligned(q, 16) && aligned(kv, 16))) return fail(DSA_ERR_INVALID_ARG, "warmup_loss: q, kv must be 16-byte aligned");
   return hip_status(dsa::launch_warmup_forward((const uint16_t*)q, (const uint16_t*)kv, lse, B, n_q, n_kv, sm_scale,
                                                scores, ld_scores, target, ld_target, loss, (hipStream_t)stream),
@@ -394,7 +418,8 @@ dsa_status_t dsa_masked_mha_attn(const void* q, const void* k, const void* v, co
   if (B > 65535 || (long long)((n_q + 127) / 128) * H > 0x7FFFFFFFLL)
     return fail(DSA_ERR_UNSUPPORTED, "masked_mha: grid too large");
   if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "masked_mha: null q, k, v, idx or out");
-  if (!std::isfinite(sm_scale)) return fail(DSA_ERR_INVALID_ARG, "masked_mha: sm_scale must be finite");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "masked_mha: sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
   if (!(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(out, 16)))
     return fail(DSA_ERR_INVALID_ARG, "masked_mha: q, k, v and out must be 16-byte aligned");
   const size_t need = dsa_masked_mha_workspace_size(B, n_q, n_kv);
@@ -430,6 +455,81 @@ dsa_status_t dsa_forward_decode(const void* q_i, const float* q_i_scale, const v
                                 size_t ws_bytes, void* stream) {
   return forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, B, 1, n_kv, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype,
                  attn_dtype, out, lse, idx_out, workspace, ws_bytes, stream);
+}
+
+
+// ---------------------------------------------------------------------------------------- decode stages
+dsa_status_t dsa_indexer_scores_decode(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                       const float* w, int B, int n_kv, int H_I, int d_I, dsa_dtype_t dtype,
+                                       float* scores, int64_t ld_scores, void* stream) {
+  return dsa_indexer_scores(q, q_scale, k, k_scale, w, B, 1, n_kv, H_I, d_I, dtype, scores, ld_scores, stream);
+}
+
+size_t dsa_topk_decode_workspace_size(int B, int n_kv, int k) { return dsa_topk_workspace_size(B, 1, n_kv, k); }
+
+dsa_status_t dsa_topk_decode(const float* scores, int64_t ld_scores, int B, int n_kv, int k, int32_t* idx,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return dsa_topk(scores, ld_scores, B, 1, n_kv, k, idx, workspace, ws_bytes, stream);
+}
+
+size_t dsa_sparse_mla_attn_decode_workspace_size(int B, int n_kv, int H, int d_qk, int d_v, int k,
+                                                 dsa_dtype_t dtype) {
+  return dsa_sparse_mla_attn_workspace_size(B, 1, n_kv, H, d_qk, d_v, k, dtype);
+}
+
+dsa_status_t dsa_sparse_mla_attn_decode(const void* q, const void* kv, const int32_t* idx, int B, int n_kv, int H,
+                                        int d_qk, int d_v, int k, float sm_scale, dsa_dtype_t dtype, void* out,
+                                        float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  return dsa_sparse_mla_attn(q, kv, idx, B, 1, n_kv, H, d_qk, d_v, k, sm_scale, dtype, out, lse, workspace, ws_bytes,
+                             stream);
+}
+
+// ---------------------------------------------------------------------------------------- masked MHA mode forward
+size_t dsa_forward_prefill_masked_mha_workspace_size(int B, int n_q, int n_kv, int k_sel) {
+  MhaFwdLayout L;
+  if (plan_forward_mha(B, n_q, n_kv, k_sel, &L) != DSA_OK) return 0;
+  return L.total;
+}
+
+dsa_status_t dsa_forward_prefill_masked_mha(const void* q_i, const float* q_i_scale, const void* k_i,
+                                            const float* k_i_scale, const float* w, const void* q, const void* k,
+                                            const void* v, int B, int n_q, int n_kv, int H_I, int d_I, int H,
+                                            int d_qk, int d_v, int k_sel, float sm_scale, dsa_dtype_t idx_dtype,
+                                            dsa_dtype_t attn_dtype, void* out, float* lse, int32_t* idx_out,
+                                            void* workspace, size_t ws_bytes, void* stream_) {
+  MhaFwdLayout L;
+  dsa_status_t st = plan_forward_mha(B, n_q, n_kv, k_sel, &L);
+  if (st != DSA_OK) return st;
+  if (attn_dtype != DSA_BF16 || d_qk != 192 || d_v != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "forward_mha: attention supports bf16 with d_qk=192, d_v=128 (got dtype %d, %d, %d)",
+                (int)attn_dtype, d_qk, d_v);
+  if (H < 1) return fail(DSA_ERR_INVALID_ARG, "forward_mha: H must be positive");
+  if (B > 65535 || (long long)((n_q + 127) / 128) * H > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "forward_mha: grid too large");
+  if (!q || !k || !v || !out) return fail(DSA_ERR_INVALID_ARG, "forward_mha: null q, k, v or out");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "forward_mha: sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (!(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(out, 16)))
+    return fail(DSA_ERR_INVALID_ARG, "forward_mha: q, k, v and out must be 16-byte aligned");
+  if (!workspace) return fail(DSA_ERR_WORKSPACE, "forward_mha: workspace of %zu bytes required", L.total);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_WORKSPACE, "forward_mha: workspace must be 256-byte aligned");
+  if (ws_bytes < L.total) return fail(DSA_ERR_WORKSPACE, "forward_mha: workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* ws = (char*)workspace;
+  float* scores = (float*)ws;
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(ws + L.off_idx);
+  bool fast_idx = false;
+  st = check_indexer(q_i, q_i_scale, k_i, k_i_scale, w, B, n_q, n_kv, H_I, d_I, idx_dtype, scores, L.ld, &fast_idx);
+  if (st != DSA_OK) return st;
+  st = check_topk(scores, L.ld, B, n_q, n_kv, k_sel, idx);
+  if (st != DSA_OK) return st;
+  hipStream_t stream = (hipStream_t)stream_;
+  st = run_indexer(q_i, q_i_scale, k_i, k_i_scale, w, B, n_q, n_kv, H_I, d_I, idx_dtype, scores, L.ld, fast_idx, stream);
+  if (st != DSA_OK) return st;
+  st = hip_status(dsa::launch_topk(scores, L.ld, B, n_q, n_kv, k_sel, idx, L.topk, ws + L.off_topk, stream), "dsa_topk");
+  if (st != DSA_OK) return st;
+  return hip_status(dsa::launch_masked_mha((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, B, n_q, n_kv,
+                                           H, k_sel, sm_scale, (uint16_t*)out, lse, (uint32_t*)(ws + L.off_mask), stream),
+                    "dsa_forward_prefill_masked_mha");
 }
 
 }  // extern "C"

@@ -72,14 +72,16 @@ hipError_t launch_indexer_fp8(const uint8_t* q, const float* q_scale, const uint
                               const float* w, int B, int n_q, int n_kv, float* scores, int64_t ld,
                               int keys_per_wave, hipStream_t stream);
 
-// Top-k launch plan: one LDS-resident pass per row, two stages (chunk candidates in a workspace, then
-// a merge) for rows too long or too few, or a kernel that re-reads long rows from memory.
+// Top-k launch plan: one LDS-resident pass per row; for few long rows, threshold candidates per chunk
+// and an exact merge per row; two stages (each chunk's top k in a workspace, then a merge) for rows too
+// long or too few otherwise; or a kernel that re-reads long rows from memory.
 struct TopkPlan {
-  enum Mode { kSingle = 0, kTwoStage = 1, kUncached = 2 };
+  enum Mode { kSingle = 0, kTwoStage = 1, kUncached = 2, kCandidates = 3 };
   int mode;
-  int chunk;     // keys per chunk (two stages)
+  int chunk;     // keys per chunk (two stages, candidates)
   int n_chunks;
-  size_t ws;     // workspace bytes (two stages), else 0
+  int t_lo;      // candidates: keys a chunk keeps at least
+  size_t ws;     // workspace bytes (two stages, candidates), else 0
 };
 TopkPlan plan_topk(int B, int n_q, int n_kv, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv, int k, int32_t* idx,

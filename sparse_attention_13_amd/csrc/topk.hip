@@ -24,6 +24,8 @@
 // order is position order and the stage-two compaction keeps both the tie rule and the sorted output.
 // Rows the two stages cannot take (k too large for the LDS budget) use a kernel that re-reads the row
 // from memory in every pass.
+#include <atomic>
+
 #include "dsa_internal.h"
 
 #include <algorithm>
@@ -703,27 +705,21 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   for (int j = tid; j < k; j += kTkThreads) out_idx[j] = (int)stage[j];
 }
 
-// Fallback for rows the LDS-resident kernels cannot take: every pass re-reads the row from memory.
-__global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* __restrict__ scores, int64_t ld,
-                                                                   int n_q, int n_kv, int k,
-                                                                   int32_t* __restrict__ idx) {
-  extern __shared__ unsigned int lds[];
-  unsigned int* hist = lds;
-  unsigned int* misc = lds + kHistWords;
-  unsigned int* tot = misc + 64;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int t = n_q - 1 - (int)blockIdx.x;
-  const int b = blockIdx.y;
-  const int n = n_kv - n_q + t + 1;
-  const size_t rowid = (size_t)b * n_q + t;
-  const float* row = scores + rowid * ld;
-  int32_t* out = idx + rowid * (size_t)k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = (i < n) ? i : -1;
-    return;
-  }
+// ------------------------------------------------------------------------------------------------
+// Selection that re-reads its keys in every pass (from memory or LDS), for rows no resident kernel
+// holds.  key_at(i) returns the order-preserving key of entry i (0 <= i < n), pos_at(i) the position
+// written for it.  Both steps are called by every thread of a 512-thread workgroup; hist, misc and tot
+// are its LDS scratch (kHistWords, 64 and 256 words).
+// ------------------------------------------------------------------------------------------------
+struct TauK {
+  unsigned int tau;  // the k-th largest key
+  int k_rem;         // how many keys equal to tau are taken (the lowest entries win)
+};
+
+template <typename KeyAt>
+__device__ __forceinline__ TauK select_tau(int n, int k, unsigned int* hist, unsigned int* misc, unsigned int* tot,
+                                           KeyAt key_at) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned int prefix = 0u;
   int k_rem = k;
   unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
@@ -733,14 +729,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
     for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
     __syncthreads();
     for (int base = 0; base < n; base += kTkThreads * kLoadUnroll) {
-      float v[kLoadUnroll];
+      unsigned int v[kLoadUnroll];
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; u++) v[u] = row[min(base + u * kTkThreads + tid, n - 1)];
+      for (int u = 0; u < kLoadUnroll; u++) v[u] = key_at(min(base + u * kTkThreads + tid, n - 1));
 #pragma unroll
       for (int u = 0; u < kLoadUnroll; u++) {
         const int i = base + u * kTkThreads + tid;
-        const unsigned int key = score_key(v[u]);
-        if (i < n && (pass == 0 || (key >> (shift + 8)) == prefix)) atomicAdd(&h[(key >> shift) & 255u], 1u);
+        if (i < n && (pass == 0 || (v[u] >> (shift + 8)) == prefix)) atomicAdd(&h[(v[u] >> shift) & 255u], 1u);
       }
     }
     __syncthreads();
@@ -749,7 +744,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
     k_rem -= (int)misc[1];
     __syncthreads();
   }
-  const unsigned int tau = prefix;
+  return TauK{prefix, k_rem};
+}
+
+// Ordered write of the selection fixed by (tau, k_rem): every wave owns a contiguous segment of the
+// entries, a scan over the waves' counts gives each its output offset, and ballots order the lanes.
+template <typename KeyAt, typename PosAt>
+__device__ __forceinline__ void select_write(int n, int k, TauK tk, int32_t* __restrict__ out, unsigned int* misc,
+                                             KeyAt key_at, PosAt pos_at) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned int tau = tk.tau;
+  const int k_rem = tk.k_rem;
   const int seg = ((n + kTkWaves * 64 - 1) / (kTkWaves * 64)) * 64;
   const int s0 = wave * seg;
   const int s1 = min(n, s0 + seg);
@@ -757,9 +762,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
   for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
     unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) key[u] = __float_as_uint(row[min(i0 + 64 * u + lane, s1 - 1)]);
-#pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) key[u] = score_key(__uint_as_float(key[u]));
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = key_at(min(i0 + 64 * u + lane, s1 - 1));
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
@@ -784,9 +787,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
   for (int i0 = s0; i0 < s1; i0 += 64 * kLdsUnroll) {
     unsigned int key[kLdsUnroll];
 #pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) key[u] = __float_as_uint(row[min(i0 + 64 * u + lane, s1 - 1)]);
-#pragma unroll
-    for (int u = 0; u < kLdsUnroll; u++) key[u] = score_key(__uint_as_float(key[u]));
+    for (int u = 0; u < kLdsUnroll; u++) key[u] = key_at(min(i0 + 64 * u + lane, s1 - 1));
 #pragma unroll
     for (int u = 0; u < kLdsUnroll; u++) {
       const int i = i0 + 64 * u + lane;
@@ -797,10 +798,278 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
       const bool sel = g || (e && erank < (unsigned int)k_rem);
       const unsigned long long bs = __ballot(sel);
       const unsigned int opos = p_run + lanes_below(bs);
-      if (sel && opos < (unsigned int)k) out[opos] = i;
+      if (sel && opos < (unsigned int)k) out[opos] = pos_at(i);
       e_run += __popcll(be);
       p_run += __popcll(bs);
     }
+  }
+}
+
+// Fallback for rows the LDS-resident kernels cannot take: every pass re-reads the row from memory.
+__global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                   int n_q, int n_kv, int k,
+                                                                   int32_t* __restrict__ idx) {
+  extern __shared__ unsigned int lds[];
+  unsigned int* hist = lds;
+  unsigned int* misc = lds + kHistWords;
+  unsigned int* tot = misc + 64;
+  const int tid = threadIdx.x;
+  const int t = n_q - 1 - (int)blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = n_kv - n_q + t + 1;
+  const size_t rowid = (size_t)b * n_q + t;
+  const float* row = scores + rowid * ld;
+  int32_t* out = idx + rowid * (size_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  auto key_at = [&](int i) { return score_key(row[i]); };
+  auto pos_at = [](int i) { return i; };
+  const TauK tk = select_tau(n, k, hist, misc, tot, key_at);
+  select_write(n, k, tk, out, misc, key_at, pos_at);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Few long rows (decode): threshold candidates per chunk, then one exact merge per row.
+//
+// Stage one cuts each row into chunks of at most kCandChunk keys (one 256-thread workgroup each, the
+// keys in registers) and keeps, per chunk, every key at or above a threshold theta_c: the radix digits
+// are fixed from the top, as in a select of the chunk's top t_lo keys, but only until the keys at or
+// above the current digit prefix number at most kCandCap (usually after two digits).  So a chunk keeps
+// between t_lo and kCandCap keys, in ascending position, and every key it drops is below theta_c.
+// t_lo is twice a chunk's expected share of the row's top k plus a margin.
+// Stage two (one workgroup per row) gathers the row's candidates into LDS (chunk after chunk, so in
+// position order) and selects their top k exactly: tau and the number of keys equal to tau to take.
+// That is the row's selection exactly when tau >= theta_c for every chunk: each dropped key is then
+// below tau, and every key equal to tau is a candidate.  Otherwise (a chunk holding much of the row's
+// top k, or more than kCandCap keys tied at one value) the workgroup selects from the row's scores in
+// memory instead.
+// ------------------------------------------------------------------------------------------------
+constexpr int kCandThreads = 256;
+constexpr int kCandChunk = 8192;    // keys per chunk at most: 32 per thread
+constexpr int kCandPerThread = kCandChunk / kCandThreads;
+constexpr int kCandCap = 1024;      // candidates a chunk keeps at most
+constexpr int kMergeCand = 16384;   // candidates of a row at most (n_chunks * kCandCap)
+
+struct CandArgs {
+  const float* scores;
+  int64_t ld;
+  int n_q, n_kv, k;
+  int chunk, n_chunks, t_lo;
+  uint32_t* ckey;  // [rows][n_chunks][kCandCap]
+  int32_t* cpos;   // [rows][n_chunks][kCandCap]
+  int32_t* chdr;   // [rows][n_chunks][2]: candidate count (-1: more than kCandCap tied), theta_c
+  int32_t* idx;    // [rows][k]
+};
+
+template <bool VEC4>
+__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
+  __shared__ unsigned int hist[kHistWords];
+  __shared__ unsigned int misc[64];
+  __shared__ unsigned int tot[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int t = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n = a.n_kv - a.n_q + t + 1;  // causal row length
+  const size_t rowid = (size_t)b * a.n_q + t;
+  const int lo = c * a.chunk;
+  const int m = min(n, lo + a.chunk) - lo;  // keys of this chunk (<= 0 past the row's end)
+  const size_t slot = rowid * a.n_chunks + c;
+  uint32_t* okey = a.ckey + slot * kCandCap;
+  int32_t* opos = a.cpos + slot * kCandCap;
+  const float* srow = a.scores + rowid * a.ld + lo;
+  if (n <= a.k) return;  // the merge keeps the whole row
+  if (m <= a.t_lo) {  // the whole chunk is candidates (none past the row's end)
+    for (int i = tid; i < max(m, 0); i += kCandThreads) {
+      okey[i] = score_key(srow[i]);
+      opos[i] = lo + i;
+    }
+    if (tid == 0) {
+      a.chdr[2 * slot] = max(m, 0);
+      a.chdr[2 * slot + 1] = 0;
+    }
+    return;
+  }
+
+  // keys in registers: wave w owns entries [w*seg, w*seg + seg), lane l holds 4 consecutive keys of
+  // each 256-key block u at w*seg + 256u + 4l (every load issued before any is used, indexes clamped
+  // into the chunk; keys at or past m are masked below)
+  const int seg = ((m + 4 * 256 - 1) / (4 * 256)) * 256;  // multiple of 256, <= kCandChunk / 4
+  const int w0 = wave * seg;
+  u32x4 kk[kCandPerThread / 4];
+  if (VEC4) {
+    const int last4 = ((m + 3) >> 2) - 1;  // the row's allocation holds whole 16-byte groups (ld % 4 == 0)
+#pragma unroll
+    for (int u = 0; u < kCandPerThread / 4; u++) {
+      const int j = min((w0 + 256 * u + 4 * lane) >> 2, last4);
+      kk[u] = __builtin_bit_cast(u32x4, reinterpret_cast<const float4*>(srow)[j]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kCandPerThread / 4; u++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) kk[u][e] = __float_as_uint(srow[min(w0 + 256 * u + 4 * lane + e, m - 1)]);
+  }
+  unsigned int valid = 0;  // bit 4u+e: entry (u, e) lies in the wave's segment and the chunk
+#pragma unroll
+  for (int u = 0; u < kCandPerThread / 4; u++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int i = w0 + 256 * u + 4 * lane + e;
+      kk[u][e] = score_key(__uint_as_float(kk[u][e]));
+      valid |= (256 * u < seg && i < m) ? 1u << (4 * u + e) : 0u;
+    }
+
+  // digits from the top until the keys at or above the prefix number at most kCandCap
+  unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
+  unsigned int prefix = 0u, above = 0u, n_ge = 0u;
+  int shift = 24;
+  bool overflow = true;
+#pragma unroll 1
+  for (int d = 0; d < 4; d++) {
+    shift = 24 - 8 * d;
+    for (int i = tid; i < kHistWords; i += kCandThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCandPerThread / 4; u++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const unsigned int key = kk[u][e];
+        const bool on = ((valid >> (4 * u + e)) & 1u) && (d == 0 || (key >> (shift + 8)) == prefix);
+        atomicAdd(&h[on ? (key >> shift) & 255u : 256u], 1u);
+      }
+    __syncthreads();
+    if (tid < 256) {
+      unsigned int sum = 0;
+#pragma unroll
+      for (int cp = 0; cp < kHistCopies; cp++) sum += hist[cp * kHistStride + tid];
+      tot[tid] = sum;
+    }
+    __syncthreads();
+    scan_digit(tot, misc, a.t_lo - (int)above, wave, lane);  // misc[0] = digit, misc[1] = keys above its bin
+    const unsigned int dig = misc[0];
+    n_ge = above + misc[1] + tot[dig];
+    prefix = (prefix << 8) | dig;
+    above += misc[1];
+    __syncthreads();
+    if (n_ge <= (unsigned int)kCandCap) {
+      overflow = false;
+      break;
+    }
+  }
+  const unsigned int theta = overflow ? 0u : prefix << shift;  // candidates: keys >= theta
+  if (overflow) {
+    if (tid == 0) {
+      a.chdr[2 * slot] = -1;
+      a.chdr[2 * slot + 1] = 0;
+    }
+    return;
+  }
+
+  // ordered compaction of the keys >= theta: per-wave counts, a scan over the four waves, then
+  // ballots in position order inside each wave
+  unsigned int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kCandPerThread / 4; u++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) mine += (((valid >> (4 * u + e)) & 1u) && kk[u][e] >= theta) ? 1u : 0u;
+  const unsigned int wtot = wave_sum(mine);
+  if (lane == 0) misc[8 + wave] = wtot;
+  __syncthreads();
+  unsigned int run = 0;
+  for (int w2 = 0; w2 < wave; w2++) run += misc[8 + w2];
+#pragma unroll
+  for (int u = 0; u < kCandPerThread / 4; u++) {
+    unsigned int sm = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) sm |= (((valid >> (4 * u + e)) & 1u) && kk[u][e] >= theta) ? 1u << e : 0u;
+    unsigned int before, total;
+    lane_scan3((unsigned int)__popc(sm), &before, &total);
+    unsigned int o = run + before;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      if ((sm >> e) & 1u) {
+        okey[o] = kk[u][e];
+        opos[o] = lo + w0 + 256 * u + 4 * lane + e;
+        o++;
+      }
+    }
+    run += total;
+  }
+  if (tid == 0) {
+    a.chdr[2 * slot] = (int)n_ge;
+    a.chdr[2 * slot + 1] = (int)theta;
+  }
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(CandArgs a) {
+  extern __shared__ unsigned int lds[];
+  unsigned int* hist = lds;
+  unsigned int* misc = lds + kHistWords;
+  unsigned int* tot = misc + 64;
+  unsigned int* ck = tot + 256;                       // [kMergeCand] candidate keys
+  int* cp = reinterpret_cast<int*>(ck + kMergeCand);  // [kMergeCand] their positions
+  __shared__ int off_l[64];            // per chunk: offset of its candidates (n_chunks <= 64)
+  __shared__ unsigned int row_l[3];    // total candidates, fallback flag, the largest threshold
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n = a.n_kv - a.n_q + t + 1;
+  const size_t rowid = (size_t)b * a.n_q + t;
+  int32_t* out = a.idx + rowid * (size_t)a.k;
+  if (n <= a.k) {
+    for (int i = tid; i < a.k; i += kTkThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+  const int32_t* rh = a.chdr + rowid * a.n_chunks * 2;
+  if (tid == 0) {
+    unsigned int off = 0, bad = 0, th = 0;
+    for (int c = 0; c < a.n_chunks; c++) {
+      const int cnt = rh[2 * c];
+      off_l[c] = (int)off;
+      if (cnt < 0) {
+        bad = 1;
+      } else {
+        off += (unsigned int)cnt;
+        if (cnt > 0) th = max(th, (unsigned int)rh[2 * c + 1]);
+      }
+    }
+    row_l[0] = off;
+    row_l[1] = (bad || off < (unsigned int)a.k || off > (unsigned int)kMergeCand) ? 1u : 0u;
+    row_l[2] = th;
+  }
+  __syncthreads();
+  const float* row = a.scores + rowid * a.ld;
+  auto row_key = [&](int i) { return score_key(row[i]); };
+  auto row_pos = [](int i) { return i; };
+  const int m = (int)row_l[0];
+  if (row_l[1]) {  // a chunk kept too many tied keys, or the candidates are fewer than k: the row itself
+    const TauK tk = select_tau(n, a.k, hist, misc, tot, row_key);
+    select_write(n, a.k, tk, out, misc, row_key, row_pos);
+    return;
+  }
+  const unsigned int theta_max = row_l[2];
+  // gather the candidates, chunk after chunk
+  for (int c = 0; c < a.n_chunks; c++) {
+    const int cnt = rh[2 * c];
+    const int off = off_l[c];
+    const size_t slot = rowid * a.n_chunks + c;
+    for (int i = tid; i < cnt; i += kTkThreads) {
+      ck[off + i] = a.ckey[slot * kCandCap + i];
+      cp[off + i] = a.cpos[slot * kCandCap + i];
+    }
+  }
+  __syncthreads();
+  auto c_key = [&](int i) { return ck[i]; };
+  auto c_pos = [&](int i) { return cp[i]; };
+  const TauK tk = select_tau(m, a.k, hist, misc, tot, c_key);
+  if (tk.tau >= theta_max) {
+    select_write(m, a.k, tk, out, misc, c_key, c_pos);
+  } else {  // some chunk may hold keys at or above tau that it dropped
+    const TauK tr = select_tau(n, a.k, hist, misc, tot, row_key);
+    select_write(n, a.k, tr, out, misc, row_key, row_pos);
   }
 }
 
@@ -811,11 +1080,34 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// More than 64 KiB of dynamic LDS needs an explicit opt-in, once per kernel.
+// More than 64 KiB of dynamic LDS needs an explicit opt-in, per kernel and device.  The outcome is
+// remembered per device (a race between two threads only repeats the idempotent call).
+constexpr int kMaxDevices = 64;
+
 template <int SRC, int DST>
 hipError_t allow_full_lds() {
-  static const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<SRC, DST>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytesMax);
+  static std::atomic<int> done[kMaxDevices];  // 0: not yet, 1: opted in on that device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)topk_select_kernel<SRC, DST>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytesMax);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev].store(1, std::memory_order_release);
+  return e;
+}
+
+size_t merge_lds_bytes() { return (size_t)(kHistWords + kMiscWords + 2 * kMergeCand) * 4; }
+
+hipError_t allow_full_lds_merge() {
+  static std::atomic<int> done[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)merge_lds_bytes());
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev].store(1, std::memory_order_release);
   return e;
 }
 
@@ -829,8 +1121,26 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
   p.mode = TopkPlan::kSingle;
   p.chunk = n_kv;
   p.n_chunks = 1;
+  p.t_lo = 0;
   p.ws = 0;
   if (k < 1 || n_kv <= k) return p;  // every row keeps all of its keys (k < 1 is rejected by the caller)
+  if (rows < 256) {
+    // few long rows: threshold candidates per chunk when a chunk's expected share of the row's top k is
+    // small against the candidate capacity, with chunks as short as the merge's capacity allows
+    for (int chunk = 2048; chunk <= kCandChunk; chunk *= 2) {
+      const int n_chunks = (n_kv + chunk - 1) / chunk;
+      const long long share = ((long long)k * chunk + n_kv - 1) / n_kv;
+      const long long t_lo = 2 * share + 128;
+      if (n_chunks < 2 || n_chunks * kCandCap > kMergeCand || t_lo > 3 * kCandCap / 4) continue;
+      p.mode = TopkPlan::kCandidates;
+      p.chunk = chunk;
+      p.n_chunks = n_chunks;
+      p.t_lo = (int)t_lo;
+      const size_t slots = (size_t)rows * n_chunks;
+      p.ws = 2 * align256(slots * kCandCap * 4) + align256(slots * 2 * 4);
+      return p;
+    }
+  }
   int want = 1;
   if (n_kv > kKeyCap) want = (n_kv + kKeyCap - 1) / kKeyCap;
   if (rows < 256) {
@@ -866,6 +1176,32 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   a.idx = idx;
   // rows start on 16-byte boundaries when the base is aligned and ld is a multiple of 4
   const bool rows16 = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (ld & 3) == 0;
+  if (p.mode == TopkPlan::kCandidates) {
+    hipError_t e = allow_full_lds_merge();
+    if (e != hipSuccess) return e;
+    const size_t slots = (size_t)B * n_q * p.n_chunks;
+    CandArgs c;
+    c.scores = scores;
+    c.ld = ld;
+    c.n_q = n_q;
+    c.n_kv = n_kv;
+    c.k = k;
+    c.chunk = p.chunk;
+    c.n_chunks = p.n_chunks;
+    c.t_lo = p.t_lo;
+    c.ckey = (uint32_t*)workspace;
+    c.cpos = (int32_t*)((char*)workspace + align256(slots * kCandCap * 4));
+    c.chdr = (int32_t*)((char*)workspace + 2 * align256(slots * kCandCap * 4));
+    c.idx = idx;
+    if (rows16)
+      hipLaunchKernelGGL(topk_cand_kernel<true>, dim3(p.n_chunks, n_q, B), dim3(kCandThreads), 0, stream, c);
+    else
+      hipLaunchKernelGGL(topk_cand_kernel<false>, dim3(p.n_chunks, n_q, B), dim3(kCandThreads), 0, stream, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(n_q, B), dim3(kTkThreads), merge_lds_bytes(), stream, c);
+    return hipGetLastError();
+  }
   if (p.mode == TopkPlan::kUncached) {
     hipLaunchKernelGGL(topk_uncached_kernel, dim3(n_q, B), dim3(kTkThreads), lds_bytes(0), stream, scores, ld, n_q,
                        n_kv, k, idx);

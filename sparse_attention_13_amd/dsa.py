@@ -47,6 +47,14 @@ SIGNATURES = {
     "dsa_sparse_kl_loss": ([_P, _I64, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "dsa_mla_absorb_q": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P], _I),
     "dsa_mla_out_proj": ([_P, _P, _P, _I, _I, _I, _I, _I, _P], _I),
+    "dsa_indexer_scores_decode": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
+    "dsa_topk_decode": ([_P, _I64, _I, _I, _I, _P, _P, _SZ, _P], _I),
+    "dsa_topk_decode_workspace_size": ([_I, _I, _I], _SZ),
+    "dsa_sparse_mla_attn_decode": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _SZ, _P], _I),
+    "dsa_sparse_mla_attn_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
+    "dsa_forward_prefill_masked_mha": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                        _I, _P, _P, _P, _P, _SZ, _P], _I),
+    "dsa_forward_prefill_masked_mha_workspace_size": ([_I, _I, _I, _I], _SZ),
 }
 
 _lib = None
@@ -337,4 +345,81 @@ def forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, k: int, d_v: int, sm_scale
                                    _ptr(kv), B, n_q, n_kv, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), idt, adt,
                                    _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace), wsz, _stream(stream))
     _check(st)
+    return out, lse, idx_out
+
+
+# ---------------------------------------------------------------------------------------------- decode stages
+
+def indexer_scores_decode(q, q_scale, k, k_scale, w, scores, stream=None):
+    """Decode form of indexer_scores: q [B, H_I, d_I], w [B, H_I], k [B, n_kv, d_I], scores [B, ld] f32."""
+    _dev(q, q_scale, k, k_scale, w, scores)
+    B, H_I, d_I = q.shape
+    n_kv = k.shape[1]
+    _check(lib().dsa_indexer_scores_decode(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), B, n_kv, H_I, d_I,
+                                           _dtype_code(q), _ptr(scores), scores.shape[-1], _stream(stream)))
+    return scores
+
+
+def topk_decode(scores, n_kv: int, k: int, idx=None, workspace=None, stream=None):
+    """Decode form of topk: scores [B, ld] f32 -> idx [B, k] int32."""
+    _dev(scores, idx, workspace)
+    B, ld = scores.shape
+    if idx is None:
+        idx = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    ws = int(lib().dsa_topk_decode_workspace_size(B, n_kv, k))
+    if ws and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=scores.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_topk_decode(_ptr(scores), ld, B, n_kv, k, _ptr(idx), _ptr(workspace), wsz, _stream(stream)))
+    return idx
+
+
+def sparse_mla_attn_decode(q, kv, idx, d_v: int, sm_scale: float, out=None, lse=None, workspace=None, stream=None):
+    """Decode form of sparse_mla_attn: q [B, H, d_qk], kv [B, n_kv, d_qk], idx [B, k] -> out [B, H, d_v], lse [B, H]."""
+    _dev(q, kv, idx, out, lse, workspace)
+    B, H, d_qk = q.shape
+    n_kv = kv.shape[1]
+    k = idx.shape[-1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = int(lib().dsa_sparse_mla_attn_decode_workspace_size(B, n_kv, H, d_qk, d_v, k, dt))
+    if ws and (workspace is None or workspace.numel() * workspace.element_size() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().dsa_sparse_mla_attn_decode(_ptr(q), _ptr(kv), _ptr(idx), B, n_kv, H, d_qk, d_v, k, float(sm_scale),
+                                            dt, _ptr(out), _ptr(lse), _ptr(workspace), wsz, _stream(stream)))
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------------------- masked MHA mode forward
+
+def forward_masked_mha_workspace_size(B, n_q, n_kv, k_sel) -> int:
+    return int(lib().dsa_forward_prefill_masked_mha_workspace_size(B, n_q, n_kv, k_sel))
+
+
+def forward_masked_mha(q_i, q_i_scale, k_i, k_i_scale, w, q, k, v, k_sel: int, sm_scale: float, out=None, lse=None,
+                       idx_out=None, workspace=None, stream=None):
+    """Indexer -> top-k -> masked MHA mode on one stream.  q_i [B, n_q, H_I, d_I], w [B, n_q, H_I],
+    k_i [B, n_kv, d_I]; q [B, n_q, H, 192], k [B, n_kv, H, 192], v [B, n_kv, H, 128] bf16.
+    Returns (out [B, n_q, H, 128], lse [B, n_q, H], idx_out)."""
+    _dev(q_i, q_i_scale, k_i, k_i_scale, w, q, k, v, out, lse, idx_out, workspace)
+    B, n_q, H_I, d_I = q_i.shape
+    H, d_qk = q.shape[2], q.shape[3]
+    d_v = v.shape[3]
+    n_kv = k_i.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    ws = forward_masked_mha_workspace_size(B, n_q, n_kv, k_sel)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    wsz = workspace.numel() * workspace.element_size()
+    _check(lib().dsa_forward_prefill_masked_mha(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w),
+                                                _ptr(q), _ptr(k), _ptr(v), B, n_q, n_kv, H_I, d_I, H, d_qk, d_v, k_sel,
+                                                float(sm_scale), _dtype_code(q_i), _dtype_code(q), _ptr(out),
+                                                _ptr(lse), _ptr(idx_out), _ptr(workspace), wsz, _stream(stream)))
     return out, lse, idx_out

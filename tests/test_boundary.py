@@ -39,7 +39,10 @@ def test_header_declares_the_path():
               "dsa_forward_workspace_size", "dsa_sparse_mla_attn_workspace_size", "dsa_status_string",
               "dsa_last_error", "dsa_version", "dsa_masked_mha_attn", "dsa_masked_mha_workspace_size",
               "dsa_mla_absorb_q", "dsa_mla_out_proj", "dsa_warmup_loss", "dsa_warmup_indexer_backward",
-              "dsa_sparse_mla_backward", "dsa_sparse_mla_backward_workspace_size", "dsa_sparse_kl_loss"]:
+              "dsa_sparse_mla_backward", "dsa_sparse_mla_backward_workspace_size", "dsa_sparse_kl_loss",
+              "dsa_indexer_scores_decode", "dsa_topk_decode", "dsa_topk_decode_workspace_size",
+              "dsa_sparse_mla_attn_decode", "dsa_sparse_mla_attn_decode_workspace_size",
+              "dsa_forward_prefill_masked_mha", "dsa_forward_prefill_masked_mha_workspace_size"]:
         assert n in names
 
 
@@ -74,17 +77,30 @@ def test_topk_validation(L):
     assert L.dsa_topk(FAKE, 10, 70000, 1, 10, 4, FAKE2, None, 0, None) == DSA_ERR_UNSUPPORTED  # grid limit
 
 
+def test_topk_candidate_plan_workspace(L):
+    """Few long rows take the threshold-candidate plan: per (row, chunk of 8192 keys) room for 1024 candidate
+    keys and positions, and a two-word header; 256-byte aligned regions."""
+    up = lambda x: (x + 255) // 256 * 256
+    slots = 64 * 16
+    assert L.dsa_topk_workspace_size(64, 1, 131072, 2048) == 2 * up(slots * 1024 * 4) + up(slots * 2 * 4)
+    assert L.dsa_topk_decode_workspace_size(64, 131072, 2048) == L.dsa_topk_workspace_size(64, 1, 131072, 2048)
+    # 40000 keys: chunks of 4096 (ten chunks); 5000 keys: a chunk's share of the top k is too large for the plan
+    assert L.dsa_topk_workspace_size(1, 3, 40000, 2048) == 2 * up(3 * 10 * 1024 * 4) + up(3 * 10 * 2 * 4)
+    assert L.dsa_topk_workspace_size(1, 64, 5000, 2048) != 2 * up(64 * 3 * 1024 * 4) + up(64 * 3 * 2 * 4)
+
+
 def test_topk_workspace(L):
     from sparse_attention_13_amd.dsa import DSA_ERR_WORKSPACE
     # many rows that fit the LDS-resident kernel: no workspace
     assert L.dsa_topk_workspace_size(1, 32768, 32768, 2048) == 0
     assert L.dsa_topk_workspace_size(1, 10, 10, 2048) == 0  # every row keeps all keys
     assert L.dsa_topk_workspace_size(1, 10, 5, 4) == 0      # invalid: n_q > n_kv
-    # few long rows: two stages, candidates (key + position) of every chunk; 64 rows of 131072 keys
-    # split into 4 chunks each (256 chunk workgroups, one round on 256 CUs)
-    ws = L.dsa_topk_workspace_size(64, 1, 131072, 2048)
-    assert ws == 2 * 64 * 4 * 2048 * 4
+    # few long rows with a chunk's share of the top k too large for threshold candidates: two stages, the
+    # top k (key + position) of every chunk; 64 rows of 40000 keys with k = 4096 in 2 chunks of 20224
+    assert L.dsa_topk_workspace_size(64, 1, 40000, 4096) == 2 * 64 * 2 * 4096 * 4
+    ws = L.dsa_topk_workspace_size(64, 1, 131072, 2048)  # threshold candidates (see the test above)
     big = ctypes.c_void_p(0x40000)
+    assert ws > 0
     assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, None, 0, None) == DSA_ERR_WORKSPACE
     assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, big, ws - 1, None) == DSA_ERR_WORKSPACE
     assert L.dsa_topk(FAKE, 131072, 64, 1, 131072, 2048, FAKE2, ctypes.c_void_p(0x40010), ws, None) \
@@ -294,6 +310,94 @@ def test_forward_validation(L):
              DSA_BF16, FAKE2, None, None, ctypes.c_void_p(0x40000), 1 << 30, None]
     assert L.dsa_forward_decode(*dargs) == DSA_ERR_INVALID_ARG  # k = 0
     assert L.dsa_forward_workspace_size(1, 10, 5, 128, 576, 512, k, DSA_BF16) == 0  # n_q > n_kv: invalid
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.04, -0.0, float("-inf")])
+def test_softmax_scale_must_be_positive(L, scale):
+    """Every entry point that takes sm_scale rejects a zero or negative one before anything is enqueued (the
+    kernels take the running max of the unscaled dot products, so a negative scale would pick the minimum)."""
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_F32, DSA_FP8_E4M3
+    big = ctypes.c_void_p(0x40000)
+    assert L.dsa_sparse_mla_attn(FAKE, FAKE, FAKE, 1, 1, 10, 8, 80, 64, 8, scale, DSA_F32, FAKE2, None, None, 0,
+                                 None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_attn(FAKE, FAKE, FAKE, 1, 600, 1000, 128, 576, 512, 8, scale, DSA_BF16, FAKE2, None, None,
+                                 0, None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_attn_decode(FAKE, FAKE, FAKE, 1, 1000, 128, 576, 512, 8, scale, DSA_BF16, FAKE2, None,
+                                        big, 1 << 30, None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_masked_mha_attn(FAKE, FAKE, FAKE, FAKE, 1, 100, 1000, 16, 192, 128, 64, scale, DSA_BF16, FAKE2, None,
+                                 big, 1 << 30, None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_warmup_loss(FAKE, FAKE, FAKE, 1, 64, 100, 128, 576, scale, DSA_BF16, FAKE2, 100, FAKE2, 100, FAKE2,
+                             None) == DSA_ERR_INVALID_ARG
+    ws = L.dsa_sparse_mla_backward_workspace_size(1, 64, 100, 128, 576, 512, 32, DSA_BF16)
+    assert L.dsa_sparse_mla_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 128, 576, 512, 32, scale,
+                                     DSA_BF16, FAKE2, FAKE2, None, big, ws, None) == DSA_ERR_INVALID_ARG
+    ws = L.dsa_forward_workspace_size(1, 64, 100, 128, 576, 512, 32, DSA_BF16)
+    assert L.dsa_forward_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 64, 128, 128, 576, 512, 32,
+                                 scale, DSA_FP8_E4M3, DSA_BF16, FAKE2, None, None, big, ws, None) == DSA_ERR_INVALID_ARG
+    ws = L.dsa_forward_workspace_size(2, 1, 100, 128, 576, 512, 32, DSA_BF16)
+    assert L.dsa_forward_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 100, 64, 128, 128, 576, 512, 32, scale,
+                                DSA_FP8_E4M3, DSA_BF16, FAKE2, None, None, big, ws, None) == DSA_ERR_INVALID_ARG
+    ws = L.dsa_forward_prefill_masked_mha_workspace_size(1, 64, 100, 32)
+    assert L.dsa_forward_prefill_masked_mha(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 100, 64, 128, 16,
+                                            192, 128, 32, scale, DSA_FP8_E4M3, DSA_BF16, FAKE2, None, None, big, ws,
+                                            None) == DSA_ERR_INVALID_ARG
+    assert b"sm_scale" in L.dsa_last_error()
+
+
+def test_decode_stage_entry_points(L):
+    """The decode stage calls take the general calls' n_q = 1 plan: same workspace sizes, same validation."""
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_WORKSPACE, DSA_FP8_E4M3
+    for B, S in [(64, 131072), (4, 9000), (1, 100)]:
+        assert L.dsa_topk_decode_workspace_size(B, S, 2048) == L.dsa_topk_workspace_size(B, 1, S, 2048)
+        assert (L.dsa_sparse_mla_attn_decode_workspace_size(B, S, 128, 576, 512, 2048, DSA_BF16)
+                == L.dsa_sparse_mla_attn_workspace_size(B, 1, S, 128, 576, 512, 2048, DSA_BF16))
+    assert L.dsa_topk_decode_workspace_size(64, 131072, 2048) > 0
+    assert L.dsa_indexer_scores_decode(None, FAKE, FAKE, FAKE, FAKE, 2, 100, 64, 128, DSA_FP8_E4M3, FAKE2, 100,
+                                       None) == DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_scores_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 100, 64, 128, DSA_FP8_E4M3, FAKE2, 99,
+                                       None) == DSA_ERR_INVALID_ARG  # ld < n_kv
+    ws = L.dsa_topk_decode_workspace_size(64, 131072, 2048)
+    assert L.dsa_topk_decode(FAKE, 131072, 64, 131072, 2048, FAKE2, None, 0, None) == DSA_ERR_WORKSPACE
+    assert L.dsa_topk_decode(FAKE, 131072, 64, 131072, 2048, FAKE2, ctypes.c_void_p(0x40000), ws - 1,
+                             None) == DSA_ERR_WORKSPACE
+    assert L.dsa_topk_decode(FAKE, 131072, 64, 131072, 0, FAKE2, None, 0, None) == DSA_ERR_INVALID_ARG
+    ws = L.dsa_sparse_mla_attn_decode_workspace_size(64, 131072, 128, 576, 512, 2048, DSA_BF16)
+    assert ws > 0
+    assert L.dsa_sparse_mla_attn_decode(FAKE, FAKE, FAKE, 64, 131072, 128, 576, 512, 2048, 0.04, DSA_BF16, FAKE2,
+                                        None, None, 0, None) == DSA_ERR_WORKSPACE
+
+
+def test_forward_masked_mha_validation(L):
+    from sparse_attention_13_amd.dsa import (DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE,
+                                             DSA_F32, DSA_FP8_E4M3)
+    n_q, n_kv, k = 64, 1000, 32
+    ws = L.dsa_forward_prefill_masked_mha_workspace_size(1, n_q, n_kv, k)
+    up = lambda x: (x + 255) // 256 * 256
+    # score rows (ld = n_kv rounded up to 64), the selection, the top-k candidates (64 rows are split in two
+    # stages), the selection bitmask (two words per 64 keys)
+    assert ws == up(n_q * 1024 * 4) + up(n_q * k * 4) + up(L.dsa_topk_workspace_size(1, n_q, n_kv, k)) + up(n_q * 32 * 4)
+    assert L.dsa_forward_prefill_masked_mha_workspace_size(1, n_kv + 1, n_kv, k) == 0   # n_q > n_kv
+    assert L.dsa_forward_prefill_masked_mha_workspace_size(1, 1, (1 << 19) + 1, k) == 0
+    big = ctypes.c_void_p(0x40000)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, n_q, n_kv, 64, 128, 16, 192, 128, k, 0.07, DSA_FP8_E4M3,
+          DSA_BF16, FAKE2, None, None, big, ws, None]
+    f = L.dsa_forward_prefill_masked_mha
+    a = list(ok); a[24] = ws - 1
+    assert f(*a) == DSA_ERR_WORKSPACE
+    a = list(ok); a[23] = ctypes.c_void_p(0x40040)
+    assert f(*a) == DSA_ERR_WORKSPACE
+    a = list(ok); a[14] = 576
+    assert f(*a) == DSA_ERR_UNSUPPORTED                              # MHA form only: d_qk 192
+    a = list(ok); a[19] = DSA_F32
+    assert f(*a) == DSA_ERR_UNSUPPORTED
+    a = list(ok); a[6] = None
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # null k
+    a = list(ok); a[0] = None
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # null indexer query
+    a = list(ok); a[5] = ctypes.c_void_p(0x10002)
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # misaligned q
+    a = list(ok); a[16] = 0
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # k_sel = 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -70,8 +70,9 @@ def test_indexer_tiny_f32(orc, dsa):
     g = np32(scores)[0]
     pos = np.arange(L, dtype=np.int64)
     o, mag, absmag = orc.indexer(np32(x["q_i"]), np32(x["w"]), np32(x["k_i"]), pos, ld=ld, with_mag=True)
-    e_mag, e_rel, n = parity.indexer_errors(g, o, mag, absmag, pos)
-    assert e_mag <= 1.0, (e_mag, e_rel)
+    rep = parity.indexer_report(g, o, mag, absmag, pos)
+    print("indexer tiny f32:", rep)
+    parity.assert_indexer(rep, "tiny")
     for t in range(L):
         assert np.all(np.isnan(g[t, t + 1:])), "entries beyond the query position must stay untouched"
 
@@ -87,8 +88,9 @@ def test_indexer_fp8_vs_oracle(orc, dsa, B, L, n_q, needles):
     pos = np.arange(L - n_q, L, dtype=np.int64)
     for b, xb in enumerate(x["per_seq"]):
         o, mag, absmag = orc.indexer(deq_q(xb), np32(xb["w"]), deq_k(xb), pos, ld=ld, with_mag=True)
-        e_mag, e_rel, n = parity.indexer_errors(g[b], o, mag, absmag, pos)
-        assert e_mag <= 1.0, (b, e_mag, e_rel)
+        rep = parity.indexer_report(g[b], o, mag, absmag, pos)
+        print(f"indexer fp8 B={B} L={L} n_q={n_q} seq {b}:", rep)
+        parity.assert_indexer(rep, b)
         for r, p in enumerate(pos):
             assert np.all(np.isnan(g[b, r, p + 1:]))
 
@@ -112,8 +114,9 @@ def test_indexer_fp8_decode_many_sequences(orc, dsa, pad_ld):
         xb = {"q8": q8[b], "q_scale": qs[b], "k8": k8[b], "k_scale": ks[b]}
         o, mag, absmag = orc.indexer(deq_q(xb), np32(w[b]), deq_k(xb), pos, ld=ld, with_mag=True)
         gb = np32(scores[b])
-        e_mag, e_rel, n = parity.indexer_errors(gb, o, mag, absmag, pos)
-        assert e_mag <= 1.0, (b, e_mag, e_rel)
+        rep = parity.indexer_report(gb, o, mag, absmag, pos)
+        print(f"indexer decode seq {b}:", rep)
+        parity.assert_indexer(rep, b)
         assert np.all(np.isnan(gb[0, S:])), "entries past the row's keys must stay untouched"
 
 
@@ -217,6 +220,50 @@ def test_topk_long_rows_many_rows_bit_exact(orc, dsa):
         assert np.array_equal(gi[r], oi[r]), r
 
 
+def test_topk_candidates_plan_bit_exact(orc, dsa):
+    """Few long rows take the threshold-candidate plan (chunks of 8192 keys keep the keys above a per-chunk
+    threshold, one merge per row).  Bit-exact with the oracle on identical scores for rows where the
+    candidates cover the selection and for rows where they cannot (the merge then selects from the row
+    itself): the top k crowded into one chunk, a monotone row, long runs of ties, all-equal rows, signed
+    zeros, denormals, infinities; every row has a ragged causal end and NaN past it (never read)."""
+    n_kv, n_q, k = 131072, 12, 2048
+    ld = n_kv + 64
+    gen = np.random.default_rng(17)
+    s = gen.standard_normal((1, n_q, ld)).astype(np.float32)
+    s[0, 1, 5 * 8192: 5 * 8192 + 1500] += 8.0                               # most of the top k in one chunk
+    s[0, 2] = np.arange(ld, dtype=np.float32)                               # monotone: the top k in the last chunk
+    s[0, 3] = 0.75                                                          # all equal
+    s[0, 4] = gen.choice(np.array([-1.0, 0.0, 2.0, 2.0, 7.0], np.float32), ld)  # long runs of ties
+    s[0, 5] = np.where(gen.random(ld) < 0.5, -0.0, 0.0)                    # signed zeros only
+    s[0, 6] = (gen.standard_normal(ld) * 1e-39).astype(np.float32)          # denormals
+    s[0, 7, ::2] = -np.inf                                                  # -inf mixed in
+    s[0, 8] = np.round(s[0, 8] * 1000) / 1000                               # ties at every value, across chunks
+    s[0, 9, gen.choice(n_kv - n_q, 2048, replace=False)] += 20.0            # planted keys spread over the row
+    s[0, 10, 1000:1200] = np.inf                                            # +inf run
+    pos = np.arange(n_kv - n_q, n_kv, dtype=np.int64)
+    for r, p in enumerate(pos):
+        s[0, r, p + 1:] = np.nan
+    idx = dsa.topk(torch.from_numpy(s).to(DEV), n_kv, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    oi, _ = orc.topk(s[0], pos, k)
+    for r in range(n_q):
+        assert np.array_equal(gi[r], oi[r]), r
+
+
+@pytest.mark.parametrize("B,S", [(64, 131072), (7, 50000)])
+def test_topk_decode_entry_point(orc, dsa, B, S):
+    """dsa_topk_decode on decode-shaped score rows equals the oracle bit for bit."""
+    gen = np.random.default_rng(B + S)
+    s = gen.standard_normal((B, S)).astype(np.float32)
+    idx = dsa.topk_decode(torch.from_numpy(s).to(DEV), S, 2048)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    for b in range(0, B, max(1, B // 8)):
+        oi, _ = orc.topk(s[b:b + 1], np.array([S - 1], np.int64), 2048)
+        assert np.array_equal(gi[b], oi[0]), b
+
+
 # ------------------------------------------------------------------------------------------ attention
 
 def _rand_idx(gen, n_kv, k, n_valid, interleave=False):
@@ -271,9 +318,13 @@ def test_attention_bf16_one_workgroup_per_query(orc, dsa):
 
 
 def test_attention_bf16_peaked(orc, dsa):
+    """One selected row dominates every head's softmax (z about 12 above the rest): the running max is
+    set by that row and the lazy rescale has P up to 2^8 before it fires.  Same bounds as every other
+    case (the log-sum-exp within LSE_ABS)."""
     ratio, mx, lse_err = _attn_case(orc, dsa, B=1, n_q=2, n_kv=1000, k=256, valid_counts=[200, 37],
                                     interleave=False, seed=4, peaked=True)
-    assert ratio <= 1.0 and lse_err <= 50 * parity.LSE_ABS, (ratio, mx, lse_err)
+    print(f"peaked: ratio {ratio:.3g} max abs {mx:.3g} lse err {lse_err:.3g}")
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
 
 
 def test_attention_f32_tiny(orc, dsa):
@@ -306,26 +357,36 @@ def test_forward_tiny_f32_all_rows(orc, dsa):
     gi = idx_out.cpu().numpy()[0]
     ok, exact = parity.topk_band_match(gi, res["idx"], res["scores"], res["kth"], pos)
     assert ok == L, (ok, exact)
-    n = attention_on_oracle_selection(orc, np32(x["q"]), np32(x["kv"]), gi, res["idx"], np32(out)[0], np32(lse)[0],
-                                      x["d_v"], x["sm_scale"], abs_tol=1e-5)
-    assert n >= L // 2, n
+    n, _, mx, lse_err = attention_on_oracle_selection(orc, np32(x["q"]), np32(x["kv"]), gi, res["idx"], np32(out)[0],
+                                                      np32(lse)[0], x["d_v"], x["sm_scale"], abs_tol=1e-5)
+    print(f"[tiny] {L} rows: identical selections {exact}, attention compared {n} (max abs {mx:.3g}, lse {lse_err:.3g})")
+    assert n >= math.ceil(MIN_IDENTICAL * L), n
 
 
 def attention_on_oracle_selection(orc, q_rows, kv, gi, oi, out_rows, lse_rows, d_v, sm, abs_tol=None):
     """Attention parity on the rows where the GPU's selection equals the oracle's, computed by the oracle on
     its own selection (the oracle never takes an input from the GPU).  Rows whose selection exchanged
     near-ties at the k-th score are judged by the band rule only; the attention kernel itself is checked on
-    host-drawn selections.  Returns the number of rows compared."""
+    host-drawn selections at the same sizes.  Returns (rows compared, worst allclose ratio, max abs error,
+    max lse error)."""
     same = np.array([np.array_equal(gi[r], oi[r]) for r in range(len(oi))], dtype=bool)
+    ratio = mx = lse_err = 0.0
     if same.any():
         o_out, o_lse = orc.sparse_attn(q_rows[same], kv, oi[same], d_v, sm)
         if abs_tol is not None:
-            assert np.abs(out_rows[same] - o_out).max() <= abs_tol
-            assert np.abs(lse_rows[same] - o_lse).max() <= abs_tol
+            mx = float(np.abs(out_rows[same] - o_out).max())
+            lse_err = float(np.abs(lse_rows[same] - o_lse).max())
+            assert mx <= abs_tol and lse_err <= abs_tol, (mx, lse_err)
         else:
             ratio, mx, lse_err = parity.attention_errors(out_rows[same], o_out, lse_rows[same], o_lse)
             assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
-    return int(same.sum())
+    return int(same.sum()), ratio, mx, lse_err
+
+
+# Share of the sampled rows whose selection must equal the oracle's exactly (so that their attention is
+# compared with the oracle's own): an exchange needs two scores within the fp32 rounding of the sum
+# (about 1e-6 relative) at the k-th position, which the seeded workloads meet in well under 1% of rows.
+MIN_IDENTICAL = 0.9
 
 
 def _sample_rows(n_q, L, k, n, gen):
@@ -340,8 +401,9 @@ def _sample_rows(n_q, L, k, n, gen):
     return np.array(sorted(cand), dtype=np.int64)
 
 
-def check_forward_rows(orc, x, gpu_idx, gpu_out, gpu_lse, rows, L, n_q, k):
-    """Band-rule selection parity on `rows`, attention parity on the GPU's own selection."""
+def check_forward_rows(orc, x, gpu_idx, gpu_out, gpu_lse, rows, L, n_q, k, what=""):
+    """Band-rule selection parity on `rows`, attention parity on the rows whose selection is identical.
+    Asserts that at least MIN_IDENTICAL of the rows had their attention compared; prints the counts."""
     pos = (L - n_q + rows).astype(np.int64)
     q_i = deq_q(x, torch.from_numpy(rows).to(x["q8"].device))
     w = np32(x["w"][torch.from_numpy(rows).to(x["w"].device)])
@@ -351,10 +413,14 @@ def check_forward_rows(orc, x, gpu_idx, gpu_out, gpu_lse, rows, L, n_q, k):
     gi = gpu_idx[rows]
     parity.assert_idx_wellformed(gi, pos, k)
     ok, exact = parity.topk_band_match(gi, oi, sc, kth, pos)
-    assert ok == len(rows), (ok, exact, len(rows))
     qb = bf16_np(x["q"][torch.from_numpy(rows).to(x["q"].device)])
     kvb = bf16_np(x["kv"])
-    attention_on_oracle_selection(orc, qb, kvb, gi, oi, gpu_out[rows], gpu_lse[rows], 512, 1.0 / math.sqrt(576))
+    n_att, ratio, mx, lse_err = attention_on_oracle_selection(orc, qb, kvb, gi, oi, gpu_out[rows], gpu_lse[rows],
+                                                              512, 1.0 / math.sqrt(576))
+    print(f"[{what}] rows {len(rows)}: selection band-ok {ok}, identical {exact}, attention compared {n_att} "
+          f"(worst ratio {ratio:.3g}, max abs {mx:.3g}, lse err {lse_err:.3g})", flush=True)
+    assert ok == len(rows), (ok, exact, len(rows))
+    assert n_att >= math.ceil(MIN_IDENTICAL * len(rows)), (n_att, len(rows))
     return exact, oi, sc
 
 
@@ -379,7 +445,7 @@ def test_forward_prefill_small_all_rows_selection(orc, dsa):
     ok, exact = parity.topk_band_match(gi, oi, sc, kth, pos)
     assert ok == L, (ok, exact)
     rows = _sample_rows(L, L, k, 24, np.random.default_rng(0))
-    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k, "prefill 2600")
 
 
 def test_decode_equals_last_prefill_row(orc, dsa):
@@ -408,6 +474,7 @@ def test_forward_decode_vs_oracle(orc, dsa, B, S):
     torch.cuda.synchronize()
     gi, go, gl = idx.cpu().numpy()[:, 0], np32(out), np32(lse)
     pos = np.array([S - 1], np.int64)
+    n_att = 0
     for b in range(B):
         q_i = orc.dequant_e4m3(synth.u8(x["q8"][b:b + 1]), x["q_scale"][b:b + 1].cpu().numpy())
         k_i = orc.dequant_e4m3(synth.u8(x["k8"][b]), x["k_scale"][b].cpu().numpy())
@@ -415,20 +482,43 @@ def test_forward_decode_vs_oracle(orc, dsa, B, S):
         oi, kth = orc.topk(sc, pos, k)
         ok, _ = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
         assert ok == 1, b
-        attention_on_oracle_selection(orc, bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], oi,
-                                      go[b:b + 1], gl[b:b + 1], 512, x["sm_scale"])
+        n_att += attention_on_oracle_selection(orc, bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], oi,
+                                               go[b:b + 1], gl[b:b + 1], 512, x["sm_scale"])[0]
+    print(f"[decode {B}x{S}] sequences {B}: attention compared {n_att}")
+    assert n_att >= math.ceil(MIN_IDENTICAL * B), n_att
 
 
 # ------------------------------------------------------------------------------------------ full-size workloads
 
+def full_indexer_rows(orc, dsa, x, rows, L, n_q, what):
+    """The indexer stage alone over the whole workload in its forward launch configuration (scores
+    [1, n_q, ld], ld padded to 64 as the forward pads it), then complete score rows compared with the
+    oracle, every causal entry."""
+    ld = (L + 63) // 64 * 64
+    scores = torch.empty((1, n_q, ld), dtype=torch.float32, device=DEV)
+    dsa.indexer_scores(x["q8"][None], x["q_scale"][None], x["k8"][None], x["k_scale"][None], x["w"][None], scores)
+    torch.cuda.synchronize()
+    rsel = torch.from_numpy(rows).to(DEV)
+    g = np32(scores[0, rsel])
+    del scores
+    torch.cuda.empty_cache()
+    pos = (L - n_q + rows).astype(np.int64)
+    o, mag, absmag = orc.indexer(deq_q(x, rsel), np32(x["w"][rsel]), deq_k(x), pos, ld=ld, with_mag=True)
+    rep = parity.indexer_report(g, o, mag, absmag, pos)
+    print(f"[{what}] indexer, {len(rows)} full rows ({rep['n']} entries): {rep}", flush=True)
+    parity.assert_indexer(rep, what)
+    return rep
+
+
 def test_full_prefill_8k(orc, dsa):
     L, k = 8192, 2048
     x = synth.prefill(L, seed=0, device=DEV, n_needles=64, needle_layout="random")
+    full_indexer_rows(orc, dsa, x, np.array([0, 2047, 4096, L - 1], np.int64), L, L, "prefill 8K")
     gi, go, gl = run_prefill(dsa, x, k)
     pos = np.arange(L, dtype=np.int64)
     parity.assert_idx_wellformed(gi, pos, k)
-    rows = _sample_rows(L, L, k, 40, np.random.default_rng(1))
-    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+    rows = _sample_rows(L, L, k, 48, np.random.default_rng(1))
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k, "prefill 8K")
     # needle recall (sanity statistic): planted keys are selected by every later query
     needles = x["needles"].numpy()
     late = gi[-64:]
@@ -439,32 +529,56 @@ def test_full_prefill_8k(orc, dsa):
 def test_full_prefill_32k(orc, dsa):
     L, k = 32768, 2048
     x = synth.prefill(L, seed=0, device=DEV, n_needles=256, needle_layout="random")
+    full_indexer_rows(orc, dsa, x, np.array([5, 2047, 16000, L - 2, L - 1], np.int64), L, L, "prefill 32K")
     gi, go, gl = run_prefill(dsa, x, k)
     pos = np.arange(L, dtype=np.int64)
     parity.assert_idx_wellformed(gi, pos, k)
-    rows = _sample_rows(L, L, k, 24, np.random.default_rng(2))
-    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k)
+    rows = _sample_rows(L, L, k, 48, np.random.default_rng(2))
+    check_forward_rows(orc, x, gi, go, gl, rows, L, L, k, "prefill 32K")
 
 
 def test_full_decode_64x128k(orc, dsa):
     B, S, k = 64, 131072, 2048
     x = synth.decode(B, S, seed=0, device=DEV)
+    # the indexer stage alone: full 131072-key rows of four sequences against the oracle
+    ld = (S + 63) // 64 * 64
+    scores = torch.empty((B, 1, ld), dtype=torch.float32, device=DEV)
+    dsa.indexer_scores(x["q8"][:, None], x["q_scale"][:, None], x["k8"], x["k_scale"], x["w"][:, None], scores)
+    torch.cuda.synchronize()
+    pos = np.array([S - 1], np.int64)
+    for b in (0, 31, 63):
+        xb = {"q8": x["q8"][b:b + 1], "q_scale": x["q_scale"][b:b + 1], "k8": x["k8"][b], "k_scale": x["k_scale"][b]}
+        o, mag, absmag = orc.indexer(deq_q(xb), np32(x["w"][b:b + 1]), deq_k(xb), pos, ld=ld, with_mag=True)
+        rep = parity.indexer_report(np32(scores[b]), o, mag, absmag, pos)
+        print(f"[decode 64x128K] indexer, sequence {b}, full row: {rep}", flush=True)
+        parity.assert_indexer(rep, b)
+    del scores
+    torch.cuda.empty_cache()
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
     out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
                               x["sm_scale"], decode=True, idx_out=idx)
     torch.cuda.synchronize()
     gi, go, gl = idx.cpu().numpy()[:, 0], np32(out), np32(lse)
     parity.assert_idx_wellformed(gi, np.full(B, S - 1, np.int64), k)
-    pos = np.array([S - 1], np.int64)
-    for b in (0, 17, 63):
+    seqs = (0, 9, 17, 30, 41, 52, 60, 63)
+    n_ok = n_exact = n_att = 0
+    worst = (0.0, 0.0, 0.0)
+    for b in seqs:
         q_i = orc.dequant_e4m3(synth.u8(x["q8"][b:b + 1]), x["q_scale"][b:b + 1].cpu().numpy())
         k_i = orc.dequant_e4m3(synth.u8(x["k8"][b]), x["k_scale"][b].cpu().numpy())
         sc = orc.indexer(q_i, np32(x["w"][b:b + 1]), k_i, pos, ld=S)
         oi, kth = orc.topk(sc, pos, k)
-        ok, _ = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
-        assert ok == 1, b
-        attention_on_oracle_selection(orc, bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], oi,
-                                      go[b:b + 1], gl[b:b + 1], 512, x["sm_scale"])
+        ok, exact = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
+        n_ok += ok
+        n_exact += exact
+        n, *w = attention_on_oracle_selection(orc, bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], oi,
+                                              go[b:b + 1], gl[b:b + 1], 512, x["sm_scale"])
+        n_att += n
+        worst = tuple(max(u, v) for u, v in zip(worst, w))
+    print(f"[decode 64x128K] sequences {len(seqs)}: selection band-ok {n_ok}, identical {n_exact}, attention "
+          f"compared {n_att} (worst ratio {worst[0]:.3g}, max abs {worst[1]:.3g}, lse err {worst[2]:.3g})", flush=True)
+    assert n_ok == len(seqs)
+    assert n_att >= math.ceil(MIN_IDENTICAL * len(seqs)), n_att
 
 
 def test_full_chunked_128k_last_chunks(orc, dsa):
@@ -491,8 +605,51 @@ def test_full_chunked_128k_last_chunks(orc, dsa):
     torch.cuda.synchronize()
     assert np.array_equal(np.concatenate([i_a.cpu().numpy()[0], i_b.cpu().numpy()[0]]), gi)
     assert np.array_equal(np.concatenate([np32(o_a)[0], np32(o_b)[0]]), go)
-    rows = np.array(sorted(set([0, 1, C - 1] + list(np.random.default_rng(3).choice(C, 9, replace=False)))),
+    rows = np.array(sorted(set([0, 1, C - 1] + list(np.random.default_rng(3).choice(C, 17, replace=False)))),
                     dtype=np.int64)
     xs = {kk: x[kk] for kk in ["k8", "k_scale", "kv"]}
     xs.update({kk: x[kk][last] for kk in ["q8", "q_scale", "w", "q"]})
-    check_forward_rows(orc, xs, gi, go, gl, rows, L, C, k)
+    check_forward_rows(orc, xs, gi, go, gl, rows, L, C, k, "chunked 128K, last chunk")
+
+
+# ------------------------------------------------------------------------------------------ full-size attention
+# The attention kernel at the headline sizes on host-drawn top-k-shaped selections (synth.selection), so
+# every sampled row is compared with the oracle whatever the indexer selects: the unsplit path (>= 512
+# query rows, one workgroup per query, every row past position 2047 with a full 2048-entry selection, i.e.
+# all 64 steps of 32 rows with the lazy rescale), and the split decode path (64 sequences x 131072 keys).
+
+def test_attention_full_32k_host_selection(orc, dsa):
+    L, k = 32768, 2048
+    x = synth.prefill(L, seed=3, device=DEV)
+    sel = synth.selection(L, L, k, seed=7)
+    idx = torch.from_numpy(sel).to(DEV)
+    out, lse = dsa.sparse_mla_attn(x["q"][None], x["kv"][None], idx, 512, x["sm_scale"])
+    torch.cuda.synchronize()
+    rows = _sample_rows(L, L, k, 40, np.random.default_rng(4))
+    rsel = torch.from_numpy(rows).to(DEV)
+    go, gl = np32(out[0, rsel]), np32(lse[0, rsel])
+    o_out, o_lse = orc.sparse_attn(bf16_np(x["q"][rsel]), bf16_np(x["kv"]), sel[0][rows], 512, x["sm_scale"])
+    ratio, mx, lse_err = parity.attention_errors(go, o_out, gl, o_lse)
+    full = int(((sel[0][rows] >= 0).sum(axis=1) == k).sum())
+    print(f"[attention 32K host selection] rows {len(rows)} ({full} with {k} entries): worst ratio {ratio:.3g}, "
+          f"max abs {mx:.3g}, lse err {lse_err:.3g}", flush=True)
+    assert full >= len(rows) // 2
+    assert ratio <= 1.0 and lse_err <= parity.LSE_ABS, (ratio, mx, lse_err)
+
+
+def test_attention_full_decode_64x128k_host_selection(orc, dsa):
+    B, S, k = 64, 131072, 2048
+    x = synth.decode(B, S, seed=5, device=DEV)
+    sel = synth.selection(S, 1, k, seed=9, B=B)  # [B, 1, k]
+    idx = torch.from_numpy(sel).to(DEV)
+    out, lse = dsa.sparse_mla_attn(x["q"][:, None], x["kv"], idx, 512, x["sm_scale"])
+    torch.cuda.synchronize()
+    worst = (0.0, 0.0, 0.0)
+    seqs = (0, 5, 22, 37, 50, 63)
+    for b in seqs:
+        o_out, o_lse = orc.sparse_attn(bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), sel[b], 512, x["sm_scale"])
+        r = parity.attention_errors(np32(out[b]), o_out, np32(lse[b]), o_lse)
+        worst = tuple(max(u, v) for u, v in zip(worst, r))
+    print(f"[attention decode 64x128K host selection] sequences {len(seqs)}: worst ratio {worst[0]:.3g}, "
+          f"max abs {worst[1]:.3g}, lse err {worst[2]:.3g}", flush=True)
+    assert worst[0] <= 1.0 and worst[2] <= parity.LSE_ABS, worst
