@@ -92,8 +92,8 @@ hipError_t launch_attn_generic(const float* q, const float* kv, const int32_t* i
                                hipStream_t stream);
 
 // bf16 matrix-core sparse MLA, H = 128, d_qk = 576, d_v = 512.  n_split > 1 splits each query's
-// selection into n_split contiguous parts whose partial results go to `partial` (fp32) and are
-// merged by a second kernel.
+// selection into n_split contiguous parts whose partial results go to `partial` (normalised O in bf16,
+// then the parts' log-sum-exp in fp32) and are merged by a second kernel.
 // MQA-mode projections (bf16, H heads): q_mqa [rows][H][576] from q_mha [rows][H][192] and w_ukt [H][512][128];
 // o [rows][H][128] from o_lat [rows][H][512] and w_uv [H][128][512].
 hipError_t launch_mla_absorb_q(const uint16_t* q_mha, const uint16_t* w_ukt, uint16_t* q_mqa, int rows, int H,

@@ -368,7 +368,7 @@ __device__ __forceinline__ bool pipeline_step(int it, int n_steps, int e_n, cons
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int n_q, int n_kv, int k, float sm_scale, int n_split, int per_split, uint16_t* __restrict__ out,
-                float* __restrict__ lse, float* __restrict__ part, float* __restrict__ part_lse) {
+                float* __restrict__ lse, uint16_t* __restrict__ part, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -466,87 +466,56 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     m_l[32 * wave + lane] = m_run;
   }
   __syncthreads();
-  if (n_split == 1) {
-    // O goes out through LDS (the tiles are free after the last step): 64 heads at a time are written
-    // as bf16 rows of 1040 B, then every wave stores 16 whole 1 KiB head rows, 16 bytes per lane, instead
-    // of 8-byte pieces spread over 32 rows per instruction
-    char* stg = smem + kOffBuf;
-    constexpr int kStgRow = 1040;
-    static_assert(64 * kStgRow <= kNBuf * kTileBytes, "staging fits in the tiles");
+  // O goes out through LDS (the tiles are free after the last step): 64 heads at a time are written as
+  // bf16 rows of 1040 B, then every wave stores 16 whole 1 KiB head rows, 16 bytes per lane, instead of
+  // 8-byte pieces spread over 32 rows per instruction.  A split part writes its normalised partial O (bf16)
+  // and its log-sum-exp to the partial buffers, the merge kernel combines them.
+  uint16_t* obase = n_split == 1 ? out + row * kH * kDV : part + ((row * n_split + split) * kH) * kDV;
+  char* stg = smem + kOffBuf;
+  constexpr int kStgRow = 1040;
+  static_assert(64 * kStgRow <= kNBuf * kTileBytes, "staging fits in the tiles");
 #pragma unroll
-    for (int pass = 0; pass < 2; pass++) {
+  for (int pass = 0; pass < 2; pass++) {
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        const int hb = 2 * pass + hh;
-        const float lh = l_l[32 * hb + (lane & 31)];
-        const float inv = lh > 0.f ? 1.f / lh : 0.f;
-        char* rowp = stg + (32 * hh + (lane & 31)) * kStgRow + (128 * wave + 4 * (lane >> 5)) * 2;
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-          for (int qd = 0; qd < 4; qd++) {
-            u32x2 v;
-            v[0] = pack_bf16x2(o[db][hb][4 * qd + 0] * inv, o[db][hb][4 * qd + 1] * inv);
-            v[1] = pack_bf16x2(o[db][hb][4 * qd + 2] * inv, o[db][hb][4 * qd + 3] * inv);
-            *(u32x2*)(rowp + (32 * db + 8 * qd) * 2) = v;
-          }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int hl = 16 * wave + r;
-        const u32x4 v = *(const u32x4*)(stg + hl * kStgRow + lane * 16);
-        *(u32x4*)(out + (row * kH + 64 * pass + hl) * kDV + 8 * lane) = v;
-      }
-      __syncthreads();
-    }
-    if (lse && lane < 32) {
-      const float lh = l_run;
-      lse[row * kH + 32 * wave + lane] = lh > 0.f ? (m_run + log2f(lh)) * kLn2 : -INFINITY;
-    }
-  } else {
-    // partial result of this split: normalised O (fp32) and its log-sum-exp.  Through LDS as in the
-    // single-split case: 32 heads at a time as fp32 rows of 2064 B, then every wave stores 8 whole
-    // 2 KiB head rows, 16 bytes per lane and instruction
-    char* stg = smem + kOffBuf;
-    constexpr int kStgRowF = 2064;
-    static_assert(32 * kStgRowF <= kNBuf * kTileBytes, "staging fits in the tiles");
-    float* pbase = part + ((row * n_split + split) * kH) * kDV;
-#pragma unroll
-    for (int hb = 0; hb < 4; hb++) {
+    for (int hh = 0; hh < 2; hh++) {
+      const int hb = 2 * pass + hh;
       const float lh = l_l[32 * hb + (lane & 31)];
       const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      char* rowp = stg + (lane & 31) * kStgRowF + (128 * wave + 4 * (lane >> 5)) * 4;
+      char* rowp = stg + (32 * hh + (lane & 31)) * kStgRow + (128 * wave + 4 * (lane >> 5)) * 2;
 #pragma unroll
       for (int db = 0; db < 4; db++)
 #pragma unroll
         for (int qd = 0; qd < 4; qd++) {
-          const v4f v = {o[db][hb][4 * qd] * inv, o[db][hb][4 * qd + 1] * inv, o[db][hb][4 * qd + 2] * inv,
-                         o[db][hb][4 * qd + 3] * inv};
-          *(v4f*)(rowp + (32 * db + 8 * qd) * 4) = v;
+          u32x2 v;
+          v[0] = pack_bf16x2(o[db][hb][4 * qd + 0] * inv, o[db][hb][4 * qd + 1] * inv);
+          v[1] = pack_bf16x2(o[db][hb][4 * qd + 2] * inv, o[db][hb][4 * qd + 3] * inv);
+          *(u32x2*)(rowp + (32 * db + 8 * qd) * 2) = v;
         }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 8; r++) {
-        const int hl = 8 * wave + r;
-        float* dst = pbase + (size_t)(32 * hb + hl) * kDV;
-        const char* src = stg + hl * kStgRowF;
-        *(v4f*)(dst + 4 * lane) = *(const v4f*)(src + 16 * lane);
-        *(v4f*)(dst + 256 + 4 * lane) = *(const v4f*)(src + 1024 + 16 * lane);
-      }
-      __syncthreads();
     }
-    if (lane < 32) {
-      const float lh = l_run;
-      part_lse[(row * n_split + split) * kH + 32 * wave + lane] = lh > 0.f ? (m_run + log2f(lh)) * kLn2 : -INFINITY;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int hl = 16 * wave + r;
+      const u32x4 v = *(const u32x4*)(stg + hl * kStgRow + lane * 16);
+      *(u32x4*)(obase + (64 * pass + hl) * kDV + 8 * lane) = v;
+    }
+    __syncthreads();
+  }
+  if (lane < 32) {
+    const float lh = l_run;
+    const float lv = lh > 0.f ? (m_run + log2f(lh)) * kLn2 : -INFINITY;
+    if (n_split == 1) {
+      if (lse) lse[row * kH + 32 * wave + lane] = lv;
+    } else {
+      part_lse[(row * n_split + split) * kH + 32 * wave + lane] = lv;
     }
   }
 }
 
 // Merge the n_split partial results of each (query, head): lse = log sum exp(lse_j),
-// out = sum_j exp(lse_j - lse) * O_j.  One wave per (query, head), 4 heads per workgroup; lane l
-// holds output columns 4l..4l+3 and 256+4l..256+4l+3 (two 16-byte loads per part).
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part,
+// out = sum_j exp(lse_j - lse) * O_j.  One wave per (query, head), 4 heads per workgroup; lane l holds
+// output columns 8l..8l+7 (one 16-byte load of bf16 partial per part), accumulated in fp32.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part,
                                                           const float* __restrict__ part_lse, int n_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int wave = threadIdx.x >> 6;
@@ -557,31 +526,37 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   float mx = -INFINITY;
   for (int j = 0; j < n_split; j++) mx = fmaxf(mx, pl[(size_t)j * kH]);
   float wsum = 0.f;
-  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
     for (int j = 0; j < n_split; j++) {
       const float lj = pl[(size_t)j * kH];
       if (lj == -INFINITY) continue;  // a part without valid entries contributes nothing (wave-uniform)
       const float wj = __expf(lj - mx);
-      const v4f* pj = reinterpret_cast<const v4f*>(part + ((row * n_split + j) * kH + h) * kDV);
-      const v4f x0 = pj[lane], x1 = pj[64 + lane];
+      const u32x4 x = *reinterpret_cast<const u32x4*>(part + ((row * n_split + j) * kH + h) * kDV + 8 * lane);
       wsum += wj;
-      a0 += wj * x0;
-      a1 += wj * x1;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        acc[2 * q] += wj * __uint_as_float(x[q] << 16);
+        acc[2 * q + 1] += wj * __uint_as_float(x[q] & 0xFFFF0000u);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* op = out + (row * kH + h) * kDV;
-  const u32x2 o0 = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv)};
-  const u32x2 o1 = {pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
-  reinterpret_cast<u32x2*>(op)[lane] = o0;
-  reinterpret_cast<u32x2*>(op)[64 + lane] = o1;
+  const u32x4 o = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4*>(out + (row * kH + h) * kDV + 8 * lane) = o;
   if (lse && lane == 0) lse[row * kH + h] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+}
+
+// Split-k partials: normalised O of every part (bf16), then the parts' log-sum-exp (fp32), each region
+// 256-byte aligned.
+size_t mla_partial_o_bytes(int B, int n_q, int n_split) {
+  return (((size_t)B * n_q * n_split * kH * kDV * sizeof(uint16_t)) + 255) / 256 * 256;
 }
 
 size_t mla_bf16_workspace_bytes(int B, int n_q, int n_split) {
   if (n_split <= 1) return 0;
-  return (size_t)B * n_q * n_split * kH * (kDV + 1) * sizeof(float);  // O parts, then lse parts
+  return mla_partial_o_bytes(B, n_q, n_split) + (((size_t)B * n_q * n_split * kH * sizeof(float)) + 255) / 256 * 256;
 }
 
 int mla_bf16_pick_split(int B, int n_q, int k) {
@@ -604,13 +579,13 @@ hipError_t launch_mla_bf16(const uint16_t* q, const uint16_t* kv, const int32_t*
   int per_split = (k + n_split - 1) / n_split;
   per_split = ((per_split + kNB - 1) / kNB) * kNB;
   dim3 grid(n_q * n_split, B);
-  float* part = (float*)partial;
-  float* part_lse = part ? part + (size_t)B * n_q * n_split * kH * kDV : nullptr;
+  uint16_t* part = (uint16_t*)partial;
+  float* part_lse = part ? (float*)((char*)partial + mla_partial_o_bytes(B, n_q, n_split)) : nullptr;
   hipLaunchKernelGGL(mla_bf16_kernel, grid, dim3(256), 0, stream, q, kv, idx, n_q, n_kv, k, sm_scale, n_split,
                      per_split, out, lse, part, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(n_q * (kH / 4), B), dim3(256), 0, stream, (const float*)part,
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(n_q * (kH / 4), B), dim3(256), 0, stream, (const uint16_t*)part,
                      (const float*)part_lse, n_split, out, lse);
   return hipGetLastError();
 }

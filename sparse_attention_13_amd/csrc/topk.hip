@@ -29,6 +29,7 @@
 #include "dsa_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dsa {
 
@@ -834,11 +835,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_uncached_kernel(const float* 
 // Few long rows (decode): threshold candidates per chunk, then one exact merge per row.
 //
 // Stage one cuts each row into chunks of at most kCandChunk keys (one 256-thread workgroup each, the
-// keys in registers) and keeps, per chunk, every key at or above a threshold theta_c: the radix digits
-// are fixed from the top, as in a select of the chunk's top t_lo keys, but only until the keys at or
-// above the current digit prefix number at most kCandCap (usually after two digits).  So a chunk keeps
-// between t_lo and kCandCap keys, in ascending position, and every key it drops is below theta_c.
-// t_lo is twice a chunk's expected share of the row's top k plus a margin.
+// keys in registers) and keeps, per chunk, every key at or above a threshold theta_c: digits of 12, 12
+// and 8 bits are fixed from the top, as in a select of the chunk's top t_lo keys, but only until the
+// keys at or above the current prefix number at most 2 t_lo (usually after the first digit: sign,
+// exponent and three mantissa bits).  So a chunk keeps between t_lo and kCandCap keys, in ascending
+// position, and every key it drops is below theta_c.  t_lo is a chunk's expected share of the row's
+// top k plus six standard deviations of it and a margin.
 // Stage two (one workgroup per row) gathers the row's candidates into LDS (chunk after chunk, so in
 // position order) and selects their top k exactly: tau and the number of keys equal to tau to take.
 // That is the row's selection exactly when tau >= theta_c for every chunk: each dropped key is then
@@ -865,9 +867,9 @@ struct CandArgs {
 
 template <bool VEC4>
 __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
-  __shared__ unsigned int hist[kHistWords];
-  __shared__ unsigned int misc[64];
-  __shared__ unsigned int tot[256];
+  __shared__ __attribute__((aligned(16))) unsigned int hist[4096];
+  __shared__ unsigned int wsum[8];
+  __shared__ unsigned int res[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
   const int t = blockIdx.y;
@@ -922,41 +924,85 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
       valid |= (256 * u < seg && i < m) ? 1u << (4 * u + e) : 0u;
     }
 
-  // digits from the top until the keys at or above the prefix number at most kCandCap
-  unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
+  // digits from the top (12, 12, 8 bits) until the keys at or above the prefix number at most
+  // 2 t_lo (at most kCandCap after the last digit, else the chunk reports an overflow)
+  const unsigned int t_stop = min(2u * (unsigned int)a.t_lo, (unsigned int)kCandCap);
   unsigned int prefix = 0u, above = 0u, n_ge = 0u;
-  int shift = 24;
+  int shift = 20;
   bool overflow = true;
-#pragma unroll 1
-  for (int d = 0; d < 4; d++) {
-    shift = 24 - 8 * d;
-    for (int i = tid; i < kHistWords; i += kCandThreads) hist[i] = 0u;
+  // One digit: histogram of the keys on the prefix (key >> PSHIFT == prefix), then the bin where the count
+  // from the top, plus `above`, reaches t_lo.  Thread t owns the NB/256 consecutive bins from NB/256 * t
+  // and holds their counts in registers; a suffix scan over the threads gives the count above each range.
+  auto digit = [&](auto nb_c, auto shift_c, auto pshift_c, bool first) {
+    constexpr int NB = decltype(nb_c)::value, SH = decltype(shift_c)::value, PSH = decltype(pshift_c)::value;
+    constexpr int PER = NB / kCandThreads;  // 16 or 1
+#pragma unroll
+    for (int i = 0; i < PER; i++) hist[PER * tid + i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kCandPerThread / 4; u++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const unsigned int key = kk[u][e];
-        const bool on = ((valid >> (4 * u + e)) & 1u) && (d == 0 || (key >> (shift + 8)) == prefix);
-        atomicAdd(&h[on ? (key >> shift) & 255u : 256u], 1u);
+        const bool on = ((valid >> (4 * u + e)) & 1u) && (first || (key >> PSH) == prefix);
+        if (on) atomicAdd(&hist[(key >> SH) & (unsigned int)(NB - 1)], 1u);
       }
     __syncthreads();
-    if (tid < 256) {
-      unsigned int sum = 0;
+    unsigned int cnt[PER];
+    if constexpr (PER == 16) {
 #pragma unroll
-      for (int cp = 0; cp < kHistCopies; cp++) sum += hist[cp * kHistStride + tid];
-      tot[tid] = sum;
+      for (int q = 0; q < 4; q++) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(hist + PER * tid + 4 * q);
+        cnt[4 * q] = v[0]; cnt[4 * q + 1] = v[1]; cnt[4 * q + 2] = v[2]; cnt[4 * q + 3] = v[3];
+      }
+    } else {
+      cnt[0] = hist[tid];
+    }
+    unsigned int mine = 0;
+#pragma unroll
+    for (int j = 0; j < PER; j++) mine += cnt[j];
+    const unsigned int wsuf = suffix_sum(mine, lane);  // within the wave: bins >= PER * tid
+    if (lane == 0) wsum[wave] = wsuf;
+    __syncthreads();
+    unsigned int higher = 0;  // keys in the waves above this one
+#pragma unroll
+    for (int w2 = 1; w2 < kCandThreads / 64; w2++) higher += (w2 > wave) ? wsum[w2] : 0u;
+    unsigned int run = above + higher + (wsuf - mine);  // keys in bins above this thread's range
+    const unsigned int need = (unsigned int)a.t_lo;
+    if (run < need && run + mine >= need) {
+      bool found = false;
+#pragma unroll
+      for (int j = PER - 1; j >= 0; j--) {
+        if (!found && run + cnt[j] >= need) {
+          res[0] = (unsigned int)(PER * tid + j);
+          res[1] = run;           // keys above the bin
+          res[2] = run + cnt[j];  // keys at or above the bin
+          found = true;
+        }
+        run += cnt[j];
+      }
     }
     __syncthreads();
-    scan_digit(tot, misc, a.t_lo - (int)above, wave, lane);  // misc[0] = digit, misc[1] = keys above its bin
-    const unsigned int dig = misc[0];
-    n_ge = above + misc[1] + tot[dig];
-    prefix = (prefix << 8) | dig;
-    above += misc[1];
-    __syncthreads();
-    if (n_ge <= (unsigned int)kCandCap) {
+    const unsigned int dig = res[0];
+    above = res[1];
+    n_ge = res[2];
+    prefix = first ? dig : ((prefix << (PSH - SH)) | dig);
+    shift = SH;
+    __syncthreads();  // hist and res are rewritten by the next digit
+  };
+  digit(std::integral_constant<int, 4096>(), std::integral_constant<int, 20>(), std::integral_constant<int, 32>(),
+        true);
+  if (n_ge <= t_stop) {
+    overflow = false;
+  } else {
+    digit(std::integral_constant<int, 4096>(), std::integral_constant<int, 8>(), std::integral_constant<int, 20>(),
+          false);
+    if (n_ge <= t_stop) {
       overflow = false;
-      break;
+    } else {
+      digit(std::integral_constant<int, 256>(), std::integral_constant<int, 0>(), std::integral_constant<int, 8>(),
+            false);
+      overflow = n_ge > (unsigned int)kCandCap;
     }
   }
   const unsigned int theta = overflow ? 0u : prefix << shift;  // candidates: keys >= theta
@@ -970,16 +1016,16 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
 
   // ordered compaction of the keys >= theta: per-wave counts, a scan over the four waves, then
   // ballots in position order inside each wave
-  unsigned int mine = 0;
+  unsigned int cnt_mine = 0;
 #pragma unroll
   for (int u = 0; u < kCandPerThread / 4; u++)
 #pragma unroll
-    for (int e = 0; e < 4; e++) mine += (((valid >> (4 * u + e)) & 1u) && kk[u][e] >= theta) ? 1u : 0u;
-  const unsigned int wtot = wave_sum(mine);
-  if (lane == 0) misc[8 + wave] = wtot;
+    for (int e = 0; e < 4; e++) cnt_mine += (((valid >> (4 * u + e)) & 1u) && kk[u][e] >= theta) ? 1u : 0u;
+  const unsigned int wtot = wave_sum(cnt_mine);
+  if (lane == 0) wsum[4 + wave] = wtot;
   __syncthreads();
-  unsigned int run = 0;
-  for (int w2 = 0; w2 < wave; w2++) run += misc[8 + w2];
+  unsigned int orun = 0;
+  for (int w2 = 0; w2 < wave; w2++) orun += wsum[4 + w2];
 #pragma unroll
   for (int u = 0; u < kCandPerThread / 4; u++) {
     unsigned int sm = 0;
@@ -987,7 +1033,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
     for (int e = 0; e < 4; e++) sm |= (((valid >> (4 * u + e)) & 1u) && kk[u][e] >= theta) ? 1u << e : 0u;
     unsigned int before, total;
     lane_scan3((unsigned int)__popc(sm), &before, &total);
-    unsigned int o = run + before;
+    unsigned int o = orun + before;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       if ((sm >> e) & 1u) {
@@ -996,7 +1042,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(CandArgs a) {
         o++;
       }
     }
-    run += total;
+    orun += total;
   }
   if (tid == 0) {
     a.chdr[2 * slot] = (int)n_ge;
@@ -1012,8 +1058,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(CandArgs a) {
   unsigned int* ck = tot + 256;                       // [kMergeCand] candidate keys
   int* cp = reinterpret_cast<int*>(ck + kMergeCand);  // [kMergeCand] their positions
   __shared__ int off_l[64];            // per chunk: offset of its candidates (n_chunks <= 64)
+  __shared__ int cnt_l[64];            // per chunk: its candidate count
   __shared__ unsigned int row_l[3];    // total candidates, fallback flag, the largest threshold
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   const int b = blockIdx.y;
   const int n = a.n_kv - a.n_q + t + 1;
@@ -1024,21 +1071,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(CandArgs a) {
     return;
   }
   const int32_t* rh = a.chdr + rowid * a.n_chunks * 2;
-  if (tid == 0) {
-    unsigned int off = 0, bad = 0, th = 0;
-    for (int c = 0; c < a.n_chunks; c++) {
-      const int cnt = rh[2 * c];
-      off_l[c] = (int)off;
-      if (cnt < 0) {
-        bad = 1;
-      } else {
-        off += (unsigned int)cnt;
-        if (cnt > 0) th = max(th, (unsigned int)rh[2 * c + 1]);
-      }
+  if (wave == 0) {  // one lane per chunk (n_chunks <= 64): offsets by a wave scan, the largest threshold
+    const bool has = lane < a.n_chunks;
+    const int cnt = has ? rh[2 * lane] : 0;
+    const unsigned int th = (has && cnt > 0) ? (unsigned int)rh[2 * lane + 1] : 0u;
+    const unsigned int c = cnt > 0 ? (unsigned int)cnt : 0u;
+    unsigned int incl = c;  // inclusive prefix sum over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-    row_l[0] = off;
-    row_l[1] = (bad || off < (unsigned int)a.k || off > (unsigned int)kMergeCand) ? 1u : 0u;
-    row_l[2] = th;
+    unsigned int mx = th;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (unsigned int)__shfl_xor(mx, off, 64));
+    const bool bad = __ballot(has && cnt < 0) != 0ull;
+    if (has) {
+      off_l[lane] = (int)(incl - c);
+      cnt_l[lane] = (int)c;
+    }
+    if (lane == 63) {
+      row_l[0] = incl;
+      row_l[1] = (bad || incl < (unsigned int)a.k || incl > (unsigned int)kMergeCand) ? 1u : 0u;
+      row_l[2] = mx;
+    }
   }
   __syncthreads();
   const float* row = a.scores + rowid * a.ld;
@@ -1051,14 +1107,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(CandArgs a) {
     return;
   }
   const unsigned int theta_max = row_l[2];
-  // gather the candidates, chunk after chunk
-  for (int c = 0; c < a.n_chunks; c++) {
-    const int cnt = rh[2 * c];
+  // gather the candidates, chunk after chunk: wave w copies chunks w, w + 8, ..., each lane loading all of
+  // its (at most kCandCap / 64) entries of a chunk before storing any
+  for (int c = wave; c < a.n_chunks; c += kTkWaves) {
+    const int cnt = cnt_l[c];
     const int off = off_l[c];
     const size_t slot = rowid * a.n_chunks + c;
-    for (int i = tid; i < cnt; i += kTkThreads) {
-      ck[off + i] = a.ckey[slot * kCandCap + i];
-      cp[off + i] = a.cpos[slot * kCandCap + i];
+    const uint32_t* sk = a.ckey + slot * kCandCap;
+    const int32_t* sp = a.cpos + slot * kCandCap;
+    constexpr int kPer = kCandCap / 64;
+    uint32_t kv_[kPer];
+    int32_t pv_[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const int i = min(lane + 64 * u, kCandCap - 1);  // in the slot's bounds; entries at or past cnt are dropped
+      kv_[u] = sk[i];
+      pv_[u] = sp[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+      const int i = lane + 64 * u;
+      if (i < cnt) {
+        ck[off + i] = kv_[u];
+        cp[off + i] = pv_[u];
+      }
     }
   }
   __syncthreads();
@@ -1129,9 +1201,13 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
     // small against the candidate capacity, with chunks as short as the merge's capacity allows
     for (int chunk = 2048; chunk <= kCandChunk; chunk *= 2) {
       const int n_chunks = (n_kv + chunk - 1) / chunk;
+      // t_lo: a chunk's expected share of the row's top k plus six standard deviations of it and a margin,
+      // so that a chunk of independent scores holds more than t_lo of the row's top k essentially never
       const long long share = ((long long)k * chunk + n_kv - 1) / n_kv;
-      const long long t_lo = 2 * share + 128;
-      if (n_chunks < 2 || n_chunks * kCandCap > kMergeCand || t_lo > 3 * kCandCap / 4) continue;
+      long long sd = 1;
+      while (sd * sd < share) sd++;
+      const long long t_lo = share + 6 * sd + 32;
+      if (n_chunks < 2 || n_chunks * kCandCap > kMergeCand || 2 * t_lo > kCandCap) continue;
       p.mode = TopkPlan::kCandidates;
       p.chunk = chunk;
       p.n_chunks = n_chunks;
