@@ -33,8 +33,9 @@
  *   finite and > 0 (the scores are multiplied by it inside the exponent); anything else returns
  *   DSA_ERR_INVALID_ARG with nothing enqueued.
  * Threading.  All entry points are reentrant.  Mutable global state: the thread-local error text,
- *   and a per-device record that the top-k kernels' opt-in to the full 160 KiB of LDS was made
- *   (an idempotent runtime call; two threads racing on it only repeat it).
+ *   a per-device record that the top-k kernels' opt-in to the full 160 KiB of LDS was made (an
+ *   idempotent runtime call; two threads racing on it only repeat it), and the per-device address of
+ *   the fixed scratch array of dsa_forward_decode_noalloc (looked up once per device, under a lock).
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -341,6 +342,25 @@ dsa_status_t dsa_forward_prefill_masked_mha(const void* q_i, const float* q_i_sc
                                             dsa_dtype_t attn_dtype, void* out, float* lse, int32_t* idx_out,
                                             void* workspace, size_t ws_bytes, void* stream);
 size_t dsa_forward_prefill_masked_mha_workspace_size(int B, int n_q, int n_kv, int k_sel);
+
+/* ------------------------------------------------------------------------------------------------
+ * dsa_forward_decode_noalloc -- dsa_forward_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments
+ * and result as dsa_forward_decode without the workspace: the call's intermediates (score rows, the
+ * selection unless idx_out is given, top-k candidates, split-k partials) live in a fixed device array of
+ * dsa_forward_decode_noalloc_max_bytes() bytes (128 MiB) that the library holds on each device it runs
+ * on until the process ends; nothing is allocated or freed by the call.  A shape whose intermediates
+ * need more (dsa_forward_workspace_size(B, 1, n_kv, ...) above the limit; 64 sequences of 131072
+ * tokens fit) returns DSA_ERR_UNSUPPORTED with nothing enqueued.  All calls on one device share that
+ * device's array: calls that may overlap on one device (several streams or threads) race and must be
+ * ordered by the caller.  No part of the array needs to start at zero.
+ * ------------------------------------------------------------------------------------------------ */
+dsa_status_t dsa_forward_decode_noalloc(const void* q_i, const float* q_i_scale, const void* k_i,
+                                        const float* k_i_scale, const float* w, const void* q, const void* kv,
+                                        int B, int n_kv, int H_I, int d_I, int H, int d_qk, int d_v, int k,
+                                        float sm_scale, dsa_dtype_t idx_dtype, dsa_dtype_t attn_dtype,
+                                        void* out, float* lse, int32_t* idx_out, void* stream);
+size_t dsa_forward_decode_noalloc_max_bytes(void);
 
 #ifdef __cplusplus
 }

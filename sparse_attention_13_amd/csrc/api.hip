@@ -1,9 +1,11 @@
 // api.hip -- the C ABI declared in include/dsa.h: argument validation, kernel selection, workspace
 // layout.  Nothing here allocates, frees or synchronises; every failure is reported before any work
 // is enqueued.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "dsa_internal.h"
@@ -228,6 +230,47 @@ dsa_status_t plan_forward_mha(int B, int n_q, int n_kv, int k_sel, MhaFwdLayout*
   L->off_mask = L->off_topk + align_up(L->topk.ws, 256);
   L->total = L->off_mask + align_up((size_t)B * n_q * dsa::mha_mask_words(n_kv) * 4, 256);
   return DSA_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Device scratch of the allocation-free decode entry point.  Each device holds its own copy of the
+// array from module load until the process ends.  Host code never passes the array's name to a kernel
+// (in host code it is only a stand-in): the per-device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+// ------------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// The calling thread's current device's scratch address (nullptr, with the error text set, on failure).
+void* device_scratch(dsa_status_t* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = fail(DSA_ERR_HIP, "forward_decode_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    *st = fail(DSA_ERR_UNSUPPORTED, "forward_decode_noalloc: device %d beyond the %d devices served", dev,
+               kMaxScratchDevices);
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    *st = fail(DSA_ERR_HIP, "forward_decode_noalloc: hipGetSymbolAddress of the scratch array failed: %s",
+               hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -530,6 +573,35 @@ dsa_status_t dsa_forward_prefill_masked_mha(const void* q_i, const float* q_i_sc
   return hip_status(dsa::launch_masked_mha((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, B, n_q, n_kv,
                                            H, k_sel, sm_scale, (uint16_t*)out, lse, (uint32_t*)(ws + L.off_mask), stream),
                     "dsa_forward_prefill_masked_mha");
+}
+
+// ---------------------------------------------------------------------------------------- allocation-free decode
+size_t dsa_forward_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+dsa_status_t dsa_forward_decode_noalloc(const void* q_i, const float* q_i_scale, const void* k_i,
+                                        const float* k_i_scale, const float* w, const void* q, const void* kv, int B,
+                                        int n_kv, int H_I, int d_I, int H, int d_qk, int d_v, int k, float sm_scale,
+                                        dsa_dtype_t idx_dtype, dsa_dtype_t attn_dtype, void* out, float* lse,
+                                        int32_t* idx_out, void* stream) {
+  FwdLayout L;
+  dsa_status_t st = plan_forward(B, 1, n_kv, H, d_qk, d_v, k, attn_dtype, &L);
+  if (st != DSA_OK) return st;
+  if (L.total > kScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "forward_decode_noalloc: this call needs %zu bytes of scratch, beyond the fixed %zu bytes (fewer "
+                "sequences or a shorter context, or dsa_forward_decode with a workspace)",
+                L.total, kScratchBytes);
+  // Argument errors come before the scratch lookup, so they read DSA_ERR_INVALID_ARG on any machine; the
+  // full checks run again in forward().
+  if (!q_i || !k_i || !w || !q || !kv || !out)
+    return fail(DSA_ERR_INVALID_ARG, "forward_decode_noalloc: null q_i, k_i, w, q, kv or out");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "forward_decode_noalloc: sm_scale must be finite and > 0 (got %g)",
+                (double)sm_scale);
+  void* ws = device_scratch(&st);
+  if (!ws) return st;
+  return forward(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, B, 1, n_kv, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype,
+                 attn_dtype, out, lse, idx_out, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

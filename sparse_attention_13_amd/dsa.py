@@ -55,6 +55,9 @@ SIGNATURES = {
     "dsa_forward_prefill_masked_mha": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                         _I, _P, _P, _P, _P, _SZ, _P], _I),
     "dsa_forward_prefill_masked_mha_workspace_size": ([_I, _I, _I, _I], _SZ),
+    "dsa_forward_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P,
+                                    _P, _P], _I),
+    "dsa_forward_decode_noalloc_max_bytes": ([], _SZ),
 }
 
 _lib = None
@@ -422,4 +425,22 @@ def forward_masked_mha(q_i, q_i_scale, k_i, k_i_scale, w, q, k, v, k_sel: int, s
                                                 _ptr(q), _ptr(k), _ptr(v), B, n_q, n_kv, H_I, d_I, H, d_qk, d_v, k_sel,
                                                 float(sm_scale), _dtype_code(q_i), _dtype_code(q), _ptr(out),
                                                 _ptr(lse), _ptr(idx_out), _ptr(workspace), wsz, _stream(stream)))
+    return out, lse, idx_out
+
+
+# ---------------------------------------------------------------------------------------------- allocation-free decode
+
+def forward_decode_noalloc(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, k: int, d_v: int, sm_scale: float, out,
+                           lse=None, idx_out=None, stream=None):
+    """dsa_forward_decode without a workspace (the library's fixed device scratch): q_i [B, H_I, d_I],
+    w [B, H_I], q [B, H, d_qk], k_i [B, n_kv, d_I], kv [B, n_kv, d_qk]; out [B, H, d_v] and the optional
+    lse [B, H], idx_out [B, k] are the caller's.  Nothing is allocated."""
+    _dev(q_i, q_i_scale, k_i, k_i_scale, w, q, kv, out, lse, idx_out)
+    B, H_I, d_I = q_i.shape
+    H, d_qk = q.shape[1], q.shape[2]
+    n_kv = k_i.shape[1]
+    _check(lib().dsa_forward_decode_noalloc(_ptr(q_i), _ptr(q_i_scale), _ptr(k_i), _ptr(k_i_scale), _ptr(w), _ptr(q),
+                                            _ptr(kv), B, n_kv, H_I, d_I, H, d_qk, d_v, k, float(sm_scale),
+                                            _dtype_code(q_i), _dtype_code(q), _ptr(out), _ptr(lse), _ptr(idx_out),
+                                            _stream(stream)))
     return out, lse, idx_out

@@ -400,6 +400,25 @@ def test_forward_masked_mha_validation(L):
     assert f(*a) == DSA_ERR_INVALID_ARG                              # k_sel = 0
 
 
+def test_noalloc_decode_limits(L):
+    """The allocation-free decode call: a fixed 128 MiB scratch; shapes whose intermediates exceed it are
+    rejected before anything is enqueued, as are invalid arguments."""
+    from sparse_attention_13_amd.dsa import DSA_BF16, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_FP8_E4M3
+    assert L.dsa_forward_decode_noalloc_max_bytes() == 128 << 20
+    f = L.dsa_forward_decode_noalloc
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 131072, 64, 128, 128, 576, 512, 2048, 1.0 / 24, DSA_FP8_E4M3,
+            DSA_BF16, FAKE2, None, None, None]
+    assert L.dsa_forward_workspace_size(64, 1, 131072, 128, 576, 512, 2048, DSA_BF16) <= 128 << 20
+    a = list(args); a[7] = 160                                       # 160 sequences of 131072 tokens: too large
+    assert L.dsa_forward_workspace_size(160, 1, 131072, 128, 576, 512, 2048, DSA_BF16) > 128 << 20
+    assert f(*a) == DSA_ERR_UNSUPPORTED
+    assert b"scratch" in L.dsa_last_error()
+    a = list(args); a[14] = 0
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # k = 0
+    a = list(args); a[15] = -1.0
+    assert f(*a) == DSA_ERR_INVALID_ARG                              # scale
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from sparse_attention_13_amd import dsa
     monkeypatch.setattr(dsa, "_lib", None)
