@@ -241,6 +241,62 @@ struct PipeState {
   float l;  // running sum of exp2(. - m)
 };
 
+// ---- steady-state step helpers ----------------------------------------------------------------------
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// base + OFF in a register the compiler cannot fold or hoist: the transposing-read builtin takes no
+// immediate offset, and hoisted per-read addresses would cost a register each.
+template <int OFF>
+__device__ __forceinline__ unsigned int lds_add(unsigned int base) {
+  unsigned int a;
+  asm("v_add_u32 %0, %1, %2" : "=v"(a) : "i"(OFF), "v"(base));
+  return a;
+}
+// V^T fragment of d block DB (the two transposing reads of load_vfrags, through the builtin so the
+// compiler places the waits).  `base` is the LDS byte address of the half's first read.
+template <int DB>
+__device__ __forceinline__ v8bf vread(unsigned int base) {
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)lds_add<64 * DB>(base));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)lds_add<8576 + 64 * DB>(base));
+  const v8s c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(v8bf, c);
+}
+__device__ __forceinline__ v8bf vread_db(unsigned int base, int db) {
+  switch (db) {
+    case 0: return vread<0>(base);
+    case 1: return vread<1>(base);
+    case 2: return vread<2>(base);
+    default: return vread<3>(base);
+  }
+}
+
+// gather_copy for the steady state, the LDS-DMA load written in asm with an SGPR base and a 32-bit
+// lane offset.  Two reasons: the compiler treats a visible LDS-DMA load as leaving every later LDS
+// read of unknown completion order, so each of its LDS waits becomes a full drain (lgkmcnt(0)) until
+// the next vmcnt wait; and the SGPR base needs no per-copy 64-bit vector address arithmetic.  The
+// copy writes no register.  Its data is consumed only after this wave's vmcnt(0) and the step's
+// barrier; hiding it from the compiler's vmcnt bookkeeping is safe because vector-memory loads
+// complete in issue order and the only vmcnt wait in the loop is that full one.
+__device__ __forceinline__ void gather_copy_steady(const char* __restrict__ kvb, const GatherRows& g, int j,
+                                                   char* tile, int wave, int lane) {
+  if (j < 8) {
+    const int s = __builtin_amdgcn_readlane(g.a, j);
+    const char* rowp = kvb + (size_t)s * (kDQK * 2);
+    const unsigned int dst = (unsigned int)(uintptr_t)(lds_void*)(tile + (wave + 4 * j) * kRowA);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane * 16), "s"(rowp),
+                 "s"(dst)
+                 : "m0");
+  } else {
+    const int rb = 8 * wave + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rb >> 1) & 7);
+    const unsigned int off = (unsigned int)g.b * (kDQK * 2) + 1024 + chunk * 16;  // < 2^32: n_kv <= 2^21
+    const unsigned int dst = (unsigned int)(uintptr_t)(lds_void*)(tile + kTileA + wave * 1024);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kvb), "s"(dst)
+                 : "m0");
+  }
+}
+
 // One pipeline iteration (see the kernel): QK of step `it` (if DO_QK) with the copies of step it+1,
 // then PV of step it-1 (if DO_PV) interleaved with the softmax of step it, then one barrier.
 template <bool DO_QK, bool DO_PV>
@@ -365,6 +421,146 @@ __device__ __forceinline__ bool pipeline_step(int it, int n_steps, int e_n, cons
   return (rf[0] | rf[1] | rf[2] | rf[3]) != 0u;
 }
 
+// Bookkeeping carried from one steady step to the next: the rows whose copies the step issues and the
+// valid entries of the step's own rows, both read from the LDS selection a step ahead.
+struct StepCtx {
+  GatherRows g;        // rows of step it+1
+  unsigned int vmask;  // bit i: entry 32 it + i is valid
+};
+
+// The steady-state iteration (both QK of step `it` and PV of step it-1), scheduled by hand: the source
+// order is the issue order, fixed by scheduling barriers between units of one matrix-core op each.
+//   QK (36 ops): K fragments read five ops ahead; the nine copies of step it+1 one per fourth op; during
+//                the last twelve ops the P^T and V^T fragments of the PV's first half.
+//   PV (32 ops): first half d block by d block, second half head block by head block; the softmax of
+//                step it is spread over the first nineteen ops (max, rescale decision, then one
+//                exponential per op), the second half's fragments are read as the first half frees
+//                their registers, the next step's bookkeeping is read late and used later.
+// Numerically the same operations as the edge steps (pipeline_step), except that the row sum adds the
+// sixteen exponentials one by one.
+__device__ __forceinline__ bool pipeline_step_steady(int it, int e_n, const char* __restrict__ kvb, char* smem,
+                                                     const int* sel_l, const v8bf (&qf)[kDQK / 16], v16f (&o)[4][4],
+                                                     PipeState& st, StepCtx& cx, float c_scale, int wave, int lane) {
+  const int cur = it % kNBuf, prv = (it + kNBuf - 1) % kNBuf, nxt = (it + 1) % kNBuf;
+  const char* tile = smem + kOffBuf + cur * kTileBytes;
+  const char* ptile = smem + kOffBuf + prv * kTileBytes;
+  char* ntile = smem + kOffBuf + nxt * kTileBytes;
+  const int pp = (it + 1) & 1, pc = it & 1;
+  const u32x4* pl = (const u32x4*)(smem + kOffP + pp * kPBytes);
+  const int G = lane >> 4, jj = lane & 15;
+  const unsigned int vb0 = (unsigned int)(uintptr_t)(lds_void*)ptile + (4 * (G >> 1) + (jj >> 2)) * kRowA +
+                           (128 * wave + 16 * (G & 1) + 4 * (jj & 3)) * 2;
+  const unsigned int vb1 = vb0 + 16 * kRowA;
+  const GatherRows g = cx.g;
+  const unsigned int vmask = cx.vmask;
+
+  // ---- QK^T of step it
+  const char* kp = tile + (lane & 31) * kRowA + (lane >> 5) * 16;
+  const int rr = lane & 31;
+  const char* kb = tile + kTileA + rr * 128;
+  const int sw = (rr >> 1) & 7;
+  constexpr int kDepth = 5;
+  constexpr int kLead = 12;  // PV operands are read during the last kLead ops
+  v8bf kf[kDepth];
+#pragma unroll
+  for (int ks = 0; ks < kDepth; ks++) kf[ks] = *(const v8bf*)(kp + ks * 32);
+  v16f sacc;
+  v8bf pf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < kDQK / 16; ks++) {
+    if (ks == 0)
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(kf[0]), "v"(qf[0]));
+    else
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(kf[ks % kDepth]), "v"(qf[ks]));
+    const int nk = ks + kDepth;
+    if (nk < 32)
+      kf[ks % kDepth] = *(const v8bf*)(kp + nk * 32);
+    else if (nk < kDQK / 16)
+      kf[ks % kDepth] = *(const v8bf*)(kb + (((2 * (nk - 32) + (lane >> 5)) ^ sw) << 4));
+    if ((ks & 3) == 1) gather_copy_steady(kvb, g, ks >> 2, ntile, wave, lane);
+    const int lp = ks - (kDQK / 16 - kLead);
+    if (lp >= 0 && lp < 4) pf[lp] = __builtin_bit_cast(v8bf, pl[(lp * 2) * 64 + lane]);
+    if (lp >= 4 && lp < 8) vf[lp - 4] = vread_db(vb0, lp - 4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- PV of step it-1 with the softmax of step it
+  float alpha = 1.f, neg_m = 0.f, psum = 0.f, bm = 0.f, b01 = 0.f, pe = 0.f;
+  unsigned int pk[8];
+  int raw_a = 0, raw_b = 0, raw_v = 0;
+#pragma unroll
+  for (int u = 0; u < 32; u++) {
+    const int db = u < 16 ? (u >> 2) : (u & 3);
+    const int hb = u < 16 ? (u & 3) : ((u - 16) >> 2);
+    o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[hb], o[db][hb], 0, 0, 0);
+    if (u == 0) {
+      asm("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));  // the QK result is readable
+      if (vmask != 0xFFFFFFFFu) {  // some entries of the step are invalid (rare): their scores -> -inf
+        const unsigned int vm = vmask >> (4 * (lane >> 5));
+#pragma unroll
+        for (int r = 0; r < 16; r++) sacc[r] = ((vm >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -INFINITY;
+      }
+      b01 = fmaxf(fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]),
+                  fmaxf(fmaxf(sacc[3], sacc[4]), fmaxf(sacc[5], fmaxf(sacc[6], sacc[7]))));
+    } else if (u == 1) {
+      const float b23 = fmaxf(fmaxf(fmaxf(sacc[8], sacc[9]), sacc[10]),
+                              fmaxf(fmaxf(sacc[11], sacc[12]), fmaxf(sacc[13], fmaxf(sacc[14], sacc[15]))));
+      bm = xor32_max(fmaxf(b01, b23)) * c_scale;
+    } else if (u == 2) {
+      if (bm > st.m + kRescaleThreshold) {
+        alpha = __builtin_amdgcn_exp2f(st.m - bm);  // 0 when m = -inf
+        st.m = bm;
+      }
+      neg_m = (st.m == -INFINITY) ? 0.f : -st.m;
+    } else if (u >= 3 && u < 19) {
+      const int r = u - 3;
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c_scale, neg_m));
+      psum += p;
+      if (r & 1)
+        pk[r >> 1] = pack_bf16x2(pe, p);
+      else
+        pe = p;
+    }
+    if (u < 16) {
+      if ((u & 3) == 3 && u < 15) vf[db] = vread_db(vb1, db);  // second half, d block db
+      if (u >= 12) pf[hb] = __builtin_bit_cast(v8bf, pl[(hb * 2 + 1) * 64 + lane]);  // second half, head block hb
+      if (u == 15) vf[3] = vread<3>(vb1);
+    }
+    if (u == 19) {  // publish step it's P^T
+      u32x4* plw = (u32x4*)(smem + kOffP + pc * kPBytes);
+      plw[(wave * 2 + 0) * 64 + lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      plw[(wave * 2 + 1) * 64 + lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    }
+    if (u == 20) {
+      st.l = st.l * alpha + xor32_sum(psum);
+      // lanes l and l+32 hold the same head and store the same factor; every lane stores the same flag
+      ((float*)(smem + kOffAlpha))[kH * pc + 32 * wave + (lane & 31)] = alpha;
+      const unsigned long long any = __ballot(alpha != 1.f);
+      ((unsigned int*)(smem + kOffRFlag))[4 * pc + wave] = any ? 1u : 0u;
+    }
+    if (u == 21) {  // next step's bookkeeping: raw entries now, decisions at u = 29
+      const int e2 = (it + 2) * kNB, e1 = (it + 1) * kNB;
+      raw_a = sel_l[max(0, min(e2 + wave + 4 * (lane & 7), e_n - 1))];
+      raw_b = sel_l[max(0, min(e2 + 8 * wave + (lane >> 3), e_n - 1))];
+      raw_v = sel_l[max(0, min(e1 + lane, e_n - 1))];
+    }
+    if (u == 29) {
+      const int e2 = (it + 2) * kNB, e1 = (it + 1) * kNB;
+      const int ea = e2 + wave + 4 * (lane & 7), eb = e2 + 8 * wave + (lane >> 3);
+      cx.g.a = (ea < e_n && raw_a >= 0) ? raw_a : 0;
+      cx.g.b = (eb < e_n && raw_b >= 0) ? raw_b : 0;
+      cx.vmask = (unsigned int)(__ballot(lane < kNB && e1 + lane < e_n && raw_v >= 0) & 0xFFFFFFFFull);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // step it+1's rows have landed (this wave's copies), then meet: every wave's copies landed, step it's
+  // P^T is published and step it-1's tile is free
+  wait_vmcnt0();
+  lds_barrier();
+  const unsigned int* rf = (const unsigned int*)(smem + kOffRFlag) + 4 * pc;
+  return (rf[0] | rf[1] | rf[2] | rf[3]) != 0u;
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
                 int n_q, int n_kv, int k, float sm_scale, int n_split, int per_split, uint16_t* __restrict__ out,
@@ -447,10 +643,13 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   if (n_steps > 0) {
     pipeline_step<true, false>(0, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
     int it = 1;
+    StepCtx cx;
+    cx.g = gather_rows(sel_l, 2 * kNB, e_n, wave, lane);
+    cx.vmask = step_valid_mask(sel_l, kNB, e_n, lane);
     while (it < n_steps) {
       bool moved = false;
       for (; it < n_steps && !moved; it++)
-        moved = pipeline_step<true, true>(it, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
+        moved = pipeline_step_steady(it, e_n, kvb, smem, sel_l, qf, o, st, cx, c_scale, wave, lane);
       if (moved) rescale_o(o, (const float*)(smem + kOffAlpha) + kH * ((it - 1) & 1), lane);
     }
     pipeline_step<false, true>(n_steps, n_steps, e_n, kvb, smem, sel_l, qf, o, st, c_scale, wave, lane);
@@ -459,11 +658,14 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   l_run = st.l;
 
   // ---- epilogue: publish per-head (m, l), normalise, store
+  // The lane index again, from a fresh computation: carrying the early one through the loop made the
+  // compiler spill two lane-derived addresses to scratch.
+  const int le = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   float* l_l = (float*)(smem + kOffL);
   float* m_l = (float*)(smem + kOffM);
-  if (lane < 32) {
-    l_l[32 * wave + lane] = l_run;
-    m_l[32 * wave + lane] = m_run;
+  if (le < 32) {
+    l_l[32 * wave + le] = l_run;
+    m_l[32 * wave + le] = m_run;
   }
   __syncthreads();
   // O goes out through LDS (the tiles are free after the last step): 64 heads at a time are written as
@@ -479,9 +681,9 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
       const int hb = 2 * pass + hh;
-      const float lh = l_l[32 * hb + (lane & 31)];
+      const float lh = l_l[32 * hb + (le & 31)];
       const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      char* rowp = stg + (32 * hh + (lane & 31)) * kStgRow + (128 * wave + 4 * (lane >> 5)) * 2;
+      char* rowp = stg + (32 * hh + (le & 31)) * kStgRow + (128 * wave + 4 * (le >> 5)) * 2;
 #pragma unroll
       for (int db = 0; db < 4; db++)
 #pragma unroll
@@ -496,18 +698,18 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int hl = 16 * wave + r;
-      const u32x4 v = *(const u32x4*)(stg + hl * kStgRow + lane * 16);
-      *(u32x4*)(obase + (64 * pass + hl) * kDV + 8 * lane) = v;
+      const u32x4 v = *(const u32x4*)(stg + hl * kStgRow + le * 16);
+      *(u32x4*)(obase + (64 * pass + hl) * kDV + 8 * le) = v;
     }
     __syncthreads();
   }
-  if (lane < 32) {
+  if (le < 32) {
     const float lh = l_run;
     const float lv = lh > 0.f ? (m_run + log2f(lh)) * kLn2 : -INFINITY;
     if (n_split == 1) {
-      if (lse) lse[row * kH + 32 * wave + lane] = lv;
+      if (lse) lse[row * kH + 32 * wave + le] = lv;
     } else {
-      part_lse[(row * n_split + split) * kH + 32 * wave + lane] = lv;
+      part_lse[(row * n_split + split) * kH + 32 * wave + le] = lv;
     }
   }
 }
