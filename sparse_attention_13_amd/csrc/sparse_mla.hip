@@ -716,7 +716,10 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 
 // Merge the n_split partial results of each (query, head): lse = log sum exp(lse_j),
 // out = sum_j exp(lse_j - lse) * O_j.  One wave per (query, head), 4 heads per workgroup; lane l holds
-// output columns 8l..8l+7 (one 16-byte load of bf16 partial per part), accumulated in fp32.
+// output columns 8l..8l+7 (one 16-byte load of bf16 partial per part), accumulated in fp32.  The parts
+// go in groups of kCombineGroup whose loads are all issued before any is used (part indexes clamped
+// into range, weights of the extra slots zero): one memory round trip per group instead of one per part.
+constexpr int kCombineGroup = 8;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part,
                                                           const float* __restrict__ part_lse, int n_split,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -725,21 +728,63 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
   const size_t row = (size_t)blockIdx.y * (gridDim.x / (kH / 4)) + blockIdx.x / (kH / 4);
   const int h = (blockIdx.x % (kH / 4)) * 4 + wave;
   const float* pl = part_lse + row * n_split * kH + h;
-  float mx = -INFINITY;
-  for (int j = 0; j < n_split; j++) mx = fmaxf(mx, pl[(size_t)j * kH]);
   float wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    for (int j = 0; j < n_split; j++) {
-      const float lj = pl[(size_t)j * kH];
-      if (lj == -INFINITY) continue;  // a part without valid entries contributes nothing (wave-uniform)
-      const float wj = __expf(lj - mx);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(part + ((row * n_split + j) * kH + h) * kDV + 8 * lane);
-      wsum += wj;
+  float mx = -INFINITY;
+  if (n_split <= kCombineGroup) {
+    // the usual case (decode: 4 parts): every load of the row in one round trip
+    float l[kCombineGroup];
+    u32x4 x[kCombineGroup];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        acc[2 * q] += wj * __uint_as_float(x[q] << 16);
-        acc[2 * q + 1] += wj * __uint_as_float(x[q] & 0xFFFF0000u);
+    for (int j = 0; j < kCombineGroup; j++) {
+      const int jc = min(j, n_split - 1);
+      l[j] = pl[(size_t)jc * kH];
+      x[j] = *reinterpret_cast<const u32x4*>(part + ((row * n_split + jc) * kH + h) * kDV + 8 * lane);
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; j++) mx = fmaxf(mx, l[j]);
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kCombineGroup; j++) {
+        const float wj = (j < n_split && l[j] != -INFINITY) ? __expf(l[j] - mx) : 0.f;
+        wsum += wj;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          acc[2 * q] += wj * __uint_as_float(x[j][q] << 16);
+          acc[2 * q + 1] += wj * __uint_as_float(x[j][q] & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+    // more parts: the maximum first, then the weighted sum, a group of loads at a time
+    for (int j0 = 0; j0 < n_split; j0 += kCombineGroup) {
+      float l[kCombineGroup];
+#pragma unroll
+      for (int j = 0; j < kCombineGroup; j++) l[j] = pl[(size_t)min(j0 + j, n_split - 1) * kH];
+#pragma unroll
+      for (int j = 0; j < kCombineGroup; j++) mx = fmaxf(mx, l[j]);  // clamped slots repeat a real part
+    }
+    if (mx != -INFINITY) {
+      for (int j0 = 0; j0 < n_split; j0 += kCombineGroup) {
+        float l[kCombineGroup];
+        u32x4 x[kCombineGroup];
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; j++) {
+          const int jc = min(j0 + j, n_split - 1);
+          l[j] = pl[(size_t)jc * kH];
+          x[j] = *reinterpret_cast<const u32x4*>(part + ((row * n_split + jc) * kH + h) * kDV + 8 * lane);
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineGroup; j++) {
+          // a part without valid entries (lse = -inf) and the clamped slots contribute nothing
+          const float wj = (j0 + j < n_split && l[j] != -INFINITY) ? __expf(l[j] - mx) : 0.f;
+          wsum += wj;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            acc[2 * q] += wj * __uint_as_float(x[j][q] << 16);
+            acc[2 * q + 1] += wj * __uint_as_float(x[j][q] & 0xFFFF0000u);
+          }
+        }
       }
     }
   }
