@@ -580,27 +580,27 @@ mla_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
   int* misc = (int*)(smem + kOffMisc);
   int* sel_l = (int*)(smem + kOffSel);
 
+  // this workgroup's part of the selection -> LDS (invalid entries as -1), and its extent.  The
+  // selection's loads go first (all of a thread's at once, e_n <= kMaxSel = 8 x 256), then the Q
+  // fragments': loads complete in issue order, so the selection, which the first copies wait for,
+  // does not wait behind the 147 KB of Q.
+  if (tid == 0) misc[0] = -1;
+  int v[kMaxSel / 256];
+#pragma unroll
+  for (int u = 0; u < kMaxSel / 256; u++) {
+    const int e = tid + 256 * u;
+    v[u] = sel[min(e_begin + min(e, max(e_n - 1, 0)), k - 1)];  // clamped into the row; past e_n unused
+  }
   // Q^T fragments of this wave's 32 heads: lane holds head 32w + l%32, dims 16ks + 8(l/32) .. +8.
-  // Issued first, so that their latency overlaps that of the selection's loads below.
   v8bf qf[kDQK / 16];
   {
     const uint16_t* qh = q + (row * kH + 32 * wave + (lane & 31)) * kDQK + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < kDQK / 16; ks++) qf[ks] = *(const v8bf*)(qh + 16 * ks);
   }
-
-  // this workgroup's part of the selection -> LDS (invalid entries as -1), and its extent
-  if (tid == 0) misc[0] = -1;
   __syncthreads();
   {
-    // all of a thread's loads in flight at once (e_n <= kMaxSel = 8 x 256)
     int last = -1;
-    int v[kMaxSel / 256];
-#pragma unroll
-    for (int u = 0; u < kMaxSel / 256; u++) {
-      const int e = tid + 256 * u;
-      v[u] = e < e_n ? sel[e_begin + e] : -1;
-    }
 #pragma unroll
     for (int u = 0; u < kMaxSel / 256; u++) {
       const int e = tid + 256 * u;
