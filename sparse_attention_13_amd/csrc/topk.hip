@@ -16,9 +16,11 @@
 // with aligned starts keep their keys in registers instead (topk_reg_kernel): the workgroup then needs
 // only about 34 KB of LDS and two of them share a compute unit.
 //
-// Rows that are longer than kKeyCap, or too few to fill the GPU, run in two stages.  Stage one cuts
-// each row into chunks and selects the top k of every chunk as (key, position) candidates; stage two
-// selects the top k among a row's candidates.  Every member of the row's top k is in its own chunk's
+// Rows that are longer than one workgroup holds, or too few to fill the GPU, run in two stages.  Stage
+// one cuts each row into chunks (at most kRegKeys keys, selected by the register-resident kernel, when
+// the rows are 16-byte aligned and a chunk's top k fit its staging area; else at most kKeyCap, in LDS)
+// and selects the top k of every chunk as (key, position) candidates; stage two selects the top k among
+// a row's candidates.  Every member of the row's top k is in its own chunk's
 // top k (fewer than k keys of the row, hence of the chunk, beat it), so the result is exact.  The
 // candidates of a row are stored chunk after chunk, each chunk's in ascending position, so array
 // order is position order and the stage-two compaction keeps both the tie rule and the sorted output.
@@ -474,12 +476,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
 // registers instead of LDS.  Wave w owns the segment [w*segw, w*segw + segw) (segw a multiple of 256,
 // at most 16 blocks of 256); lane l holds keys 256u + 4l .. +3 of its wave's block u.  LDS keeps only
 // the histograms, the candidate list and the staged output (about 34 KB), so two workgroups share a
-// compute unit and one's barriers and memory waits overlap the other's passes.
+// compute unit and one's barriers and memory waits overlap the other's passes.  DST = kDstIdx selects
+// whole rows; DST = kDstCand is stage one of the two-stage plan for longer rows: blockIdx.z is the chunk
+// of `chunk` keys (a multiple of 256, at most kRegKeys), whose top k go out as keys and positions.
 constexpr int kRegBlocks = 16;
 constexpr int kRegKeys = kTkWaves * kRegBlocks * kSeg;  // 32768
 
+template <int DST>
 __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
-                                                                 int n_q, int n_kv, int k, int32_t* __restrict__ idx) {
+                                                                 int n_q, int n_kv, int k, int chunk, int n_chunks,
+                                                                 int32_t* __restrict__ idx, uint32_t* __restrict__ okey,
+                                                                 int32_t* __restrict__ opos) {
   __shared__ unsigned int hist[kHistWords];   // histograms; then the candidates' positions; then the output
   __shared__ unsigned int misc[kMiscWords];   // [64] scratch + [256] summed histogram
   __shared__ unsigned int ckey[kHistWords];   // the candidates' keys
@@ -488,14 +495,28 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   const int wave = tid >> 6;
   const int t = n_q - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y;
-  const int m = n_kv - n_q + t + 1;  // causal row length
+  const int n = n_kv - n_q + t + 1;  // causal row length
   const size_t rowid = (size_t)b * n_q + t;
-  int32_t* out_idx = idx + rowid * (size_t)k;
-  if (m <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out_idx[i] = (i < m) ? i : -1;
+  int32_t* out_idx = DST == kDstIdx ? idx + rowid * (size_t)k : nullptr;
+  if (n <= k) {  // the row keeps all of its keys; stage one leaves such rows to stage two
+    if (DST == kDstIdx)
+      for (int i = tid; i < k; i += kTkThreads) out_idx[i] = (i < n) ? i : -1;
     return;
   }
-  const float* srow = scores + rowid * ld;
+  const int lo = DST == kDstCand ? (int)blockIdx.z * chunk : 0;
+  const int m = DST == kDstCand ? min(n, lo + chunk) - lo : n;  // keys of this chunk (<= 0: past pos_t)
+  const size_t ostride = (size_t)n_chunks * k;
+  uint32_t* out_key = DST == kDstCand ? okey + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
+  int32_t* out_pos = DST == kDstCand ? opos + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
+  const float* srow = scores + rowid * ld + lo;
+  if (DST == kDstCand && m <= k) {  // the whole chunk is candidates (none when m <= 0); pad with key 0
+    for (int i = tid; i < k; i += kTkThreads) {
+      const bool v = i < m;
+      out_key[i] = v ? score_key(srow[i]) : 0u;
+      out_pos[i] = v ? lo + i : -1;
+    }
+    return;
+  }
   const int segw = ((m + kTkWaves * kSeg - 1) / (kTkWaves * kSeg)) * kSeg;  // <= kRegBlocks * kSeg
   const int s0 = wave * segw;
   const int s1 = min(m, s0 + segw);
@@ -664,7 +685,8 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   }
   unsigned int e_run = eq_before;
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
-  unsigned int* stage = hist;  // [k] positions (k <= kHistWords - 1; the last word is the dummy slot)
+  // [k] positions, then (candidate output) [k] keys; 2k <= kHistWords - 1: the last word is the dummy slot
+  unsigned int* stage = hist;
 #pragma unroll
   for (int u = 0; u < kRegBlocks; u++) {
     if (u < nb) {
@@ -697,13 +719,21 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
       for (int e = 0; e < 4; e++) {
         const bool sel = (sel_mask & (1u << e)) && op < (unsigned int)k;
         stage[sel ? op : kHistWords - 1] = (unsigned int)(i + e);
+        if (DST == kDstCand) stage[sel ? k + op : kHistWords - 1] = kr[u][e];
         op += (sel_mask >> e) & 1u;
       }
       p_run += s_total;
     }
   }
   __syncthreads();
-  for (int j = tid; j < k; j += kTkThreads) out_idx[j] = (int)stage[j];
+  for (int j = tid; j < k; j += kTkThreads) {
+    if (DST == kDstIdx) {
+      out_idx[j] = (int)stage[j];
+    } else {
+      out_key[j] = stage[k + j];
+      out_pos[j] = lo + (int)stage[j];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1217,8 +1247,11 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
       return p;
     }
   }
+  // chunks of at most kRegKeys keys when the register-resident kernel can stage a chunk's top k (keys and
+  // positions), else of at most the LDS row cache
+  const int cap = 2 * k < kHistWords ? kRegKeys : kKeyCap;
   int want = 1;
-  if (n_kv > kKeyCap) want = (n_kv + kKeyCap - 1) / kKeyCap;
+  if (n_kv > cap) want = (n_kv + cap - 1) / cap;
   if (rows < 256) {
     // too few rows to fill the GPU: split each into chunks of at least 4k keys, aiming at one
     // workgroup per CU (a large chunk's row cache leaves room for only one), so that all chunks run
@@ -1229,7 +1262,7 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
   if (want <= 1) return p;
   const int chunk = (int)((((long long)n_kv + want - 1) / want + kSeg - 1) / kSeg * kSeg);
   const int n_chunks = (n_kv + chunk - 1) / chunk;
-  if (n_chunks < 2 || chunk <= k || chunk > kKeyCap || (long long)n_chunks * k > kKeyCap) {
+  if (n_chunks < 2 || chunk <= k || chunk > cap || (long long)n_chunks * k > kKeyCap) {
     if (n_kv > kKeyCap) p.mode = TopkPlan::kUncached;
     return p;
   }
@@ -1284,7 +1317,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
     return hipGetLastError();
   }
   if (p.mode == TopkPlan::kSingle && rows16 && n_kv <= kRegKeys && k < kHistWords) {
-    hipLaunchKernelGGL(topk_reg_kernel, dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld, n_q, n_kv, k, idx);
+    hipLaunchKernelGGL(topk_reg_kernel<kDstIdx>, dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld, n_q, n_kv, k,
+                       n_kv, 1, idx, nullptr, nullptr);
     return hipGetLastError();
   }
   if (p.mode == TopkPlan::kSingle) {
@@ -1310,8 +1344,12 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   a.okey = ckey;
   a.opos = cpos;
   a.vec4 = rows16;  // chunk starts are multiples of 256 keys
-  hipLaunchKernelGGL((topk_select_kernel<kSrcScores, kDstCand>), dim3(n_q, B, p.n_chunks), dim3(kTkThreads),
-                     lds_bytes(p.chunk), stream, a);
+  if (rows16 && p.chunk <= kRegKeys && 2 * k < kHistWords)
+    hipLaunchKernelGGL(topk_reg_kernel<kDstCand>, dim3(n_q, B, p.n_chunks), dim3(kTkThreads), 0, stream, scores,
+                       ld, n_q, n_kv, k, p.chunk, p.n_chunks, nullptr, ckey, cpos);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<kSrcScores, kDstCand>), dim3(n_q, B, p.n_chunks), dim3(kTkThreads),
+                       lds_bytes(p.chunk), stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   TopkArgs c = a;

@@ -192,24 +192,48 @@ def test_topk_adversarial_rows(orc, dsa):
     assert gi[0].tolist() == list(range(k))
 
 
+def _bucket_row(gen, ld, m, n_bucket, spots=None):
+    """A row whose 2048-th largest key lies in a 16-bit key prefix (sign, exponent and 7 mantissa bits)
+    holding exactly n_bucket keys: 2048 - n_bucket keys well above it, n_bucket distinct values in
+    [1, 1 + 2^-7), every other key negative.  spots: the bucket's positions (default: random)."""
+    row = (-1.0 - np.abs(gen.standard_normal(ld))).astype(np.float32)
+    free = gen.permutation(m)
+    if spots is None:
+        spots = free[:n_bucket]
+    free = np.setdiff1d(free, spots)
+    row[spots] = (1.0 + np.arange(n_bucket) * 2.0 ** -22).astype(np.float32)
+    row[gen.choice(free, 2048 - n_bucket, replace=False)] = 100.0 + np.arange(2048 - n_bucket, dtype=np.float32)
+    return row
+
+
 def test_topk_long_rows_many_rows_bit_exact(orc, dsa):
     """Many rows of up to 32768 keys with aligned row starts (the register-resident kernel): whole
-    16-block wave segments, ragged row ends, and rows whose candidates overflow the list (ties)."""
+    16-block wave segments, ragged row ends, rows whose candidates (the keys on the k-th key's 16-bit
+    prefix) number a few hundred with ties on tau, exactly 512 (the most tau is found from in registers),
+    513, or 512 inside one wave's segment, and rows with thousands of candidates (ties)."""
     n_kv, n_q, k = 32768, 260, 2048
     ld = n_kv + 4
     gen = np.random.default_rng(11)
     s = gen.standard_normal((1, n_q, ld)).astype(np.float32)
     pos = np.arange(n_kv - n_q, n_kv, dtype=np.int64)
     for r in range(0, n_q, 13):
-        kind = (r // 13) % 4
+        kind = (r // 13) % 10
+        m = int(pos[r]) + 1
         if kind == 0:
             s[0, r] = 0.25                                                   # all equal
         elif kind == 1:
             s[0, r] = gen.choice(np.array([-2.0, 0.0, 3.0, 3.0], np.float32), ld)  # long runs of ties
         elif kind == 2:
             s[0, r] = np.where(gen.random(ld) < 0.5, -0.0, 0.0)              # signed zeros
-        else:
+        elif kind == 3:
             s[0, r, ::2] = -np.inf                                           # -inf mixed in
+        elif kind in (4, 5, 6):
+            q = {4: 16.0, 5: 8.0, 6: 2.0}[kind]                              # ~250, ~550, ~2000 candidates
+            s[0, r] = np.round(s[0, r] * q) / q
+        elif kind in (7, 8):
+            s[0, r] = _bucket_row(gen, ld, m, 512 if kind == 7 else 513)
+        else:
+            s[0, r] = _bucket_row(gen, ld, m, 512, spots=np.arange(12288, 12288 + 512))  # wave 3's segment
     for r, p in enumerate(pos):
         s[0, r, p + 1:] = np.nan  # never to be read
     idx = dsa.topk(torch.from_numpy(s).to(DEV), n_kv, k)
@@ -218,6 +242,43 @@ def test_topk_long_rows_many_rows_bit_exact(orc, dsa):
     oi, _ = orc.topk(s[0], pos, k)
     for r in range(n_q):
         assert np.array_equal(gi[r], oi[r]), r
+
+
+@pytest.mark.parametrize("extra_ld", [0, 1])
+def test_topk_two_stage_all_row_lengths(orc, dsa, extra_ld):
+    """One causal prefill of 36000 queries in one call: rows longer than 32768 keys take two stages (chunks
+    of 18176 keys; aligned rows select their chunks in registers, unaligned ones in LDS).  Sampled rows
+    cover every chunk case: a second chunk wholly past the row's end, one holding at most k keys (exactly
+    k, k + 1), ragged tails, rows of at most k keys, and rows of ties, -inf and signed zeros; each is
+    compared with the oracle bit for bit."""
+    n, k = 36000, 2048
+    ld = n + extra_ld
+    g = torch.Generator(device=DEV)
+    g.manual_seed(23)
+    s = torch.randn((1, n, ld), generator=g, device=DEV)
+    rows = [0, 2047, 2048, 2049, 9000, 18175, 18176, 18177, 18176 + 2047, 18176 + 2048, 18176 + 2049, 20000,
+            25000, 30001, 32767, 32768, 35998, 35999]
+    special = {9000: "ties", 25000: "ninf", 30001: "zeros", 35999: "ties"}
+    gen = np.random.default_rng(29)
+    for t, kind in special.items():
+        if kind == "ties":
+            v = gen.choice(np.array([-1.0, 0.5, 0.5, 2.0], np.float32), ld)
+        elif kind == "ninf":
+            v = gen.standard_normal(ld).astype(np.float32)
+            v[::2] = -np.inf
+        else:
+            v = np.where(gen.random(ld) < 0.5, -0.0, 0.0).astype(np.float32)
+        s[0, t] = torch.from_numpy(v).to(DEV)
+    idx = dsa.topk(s, n, k)
+    torch.cuda.synchronize()
+    sel = torch.tensor(rows, device=DEV)
+    srows = s[0, sel].cpu().numpy()
+    gi = idx[0, sel].cpu().numpy()
+    del s, idx
+    torch.cuda.empty_cache()
+    oi, _ = orc.topk(srows, np.array(rows, np.int64), k)
+    for j, t in enumerate(rows):
+        assert np.array_equal(gi[j], oi[j]), t
 
 
 def test_topk_candidates_plan_bit_exact(orc, dsa):
