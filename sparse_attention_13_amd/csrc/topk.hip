@@ -13,12 +13,12 @@
 // One workgroup (8 waves) selects from up to kKeyCap keys held in LDS: the first pass reads them from
 // memory (kLoadUnroll independent 16-byte loads per thread in flight), every later pass and the
 // compaction read LDS in 16-byte pieces, kLdsUnroll per lane in flight.  Rows of at most 32768 keys
-// with aligned starts keep their keys in registers instead (topk_reg_kernel): the workgroup then needs
-// only about 34 KB of LDS and two of them share a compute unit.
+// keep their keys in registers instead (topk_reg_kernel): the workgroup then needs only about 34 KB of
+// LDS and two of them share a compute unit.
 //
 // Rows that are longer than one workgroup holds, or too few to fill the GPU, run in two stages.  Stage
 // one cuts each row into chunks (at most kRegKeys keys, selected by the register-resident kernel, when
-// the rows are 16-byte aligned and a chunk's top k fit its staging area; else at most kKeyCap, in LDS)
+// a chunk's top k fit its staging area; else at most kKeyCap, in LDS)
 // and selects the top k of every chunk as (key, position) candidates; stage two selects the top k among
 // a row's candidates.  Every member of the row's top k is in its own chunk's
 // top k (fewer than k keys of the row, hence of the chunk, beat it), so the result is exact.  The
@@ -472,9 +472,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
   }
 }
 
-// Rows of at most kRegKeys keys with 16-byte aligned starts: the same select, with every key held in
+// Rows of at most kRegKeys keys: the same select, with every key held in
 // registers instead of LDS.  Wave w owns the segment [w*segw, w*segw + segw) (segw a multiple of 256,
-// at most 16 blocks of 256); lane l holds keys 256u + 4l .. +3 of its wave's block u.  LDS keeps only
+// at most 16 blocks of 256); lane l holds keys 256u + 64e + l (e = 0..3) of its wave's block u, so row
+// order is (u, e, lane) and one ballot per key vector ranks keys in the compaction.  LDS keeps only
 // the histograms, the candidate list and the staged output (about 34 KB), so two workgroups share a
 // compute unit and one's barriers and memory waits overlap the other's passes.  DST = kDstIdx selects
 // whole rows; DST = kDstCand is stage one of the two-stage plan for longer rows: blockIdx.z is the chunk
@@ -527,29 +528,26 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   unsigned int* h = hist + (lane & (kHistCopies - 1)) * kHistStride;
   for (int i = tid; i < kHistWords; i += kTkThreads) hist[i] = 0u;
   u32x4 kr[kRegBlocks];
-  {
-    const int last4 = (m - 1) & ~3;
 #pragma unroll
-    for (int u = 0; u < kRegBlocks; u++) {
-      if (u < nb) {
-        const int i = min(s0 + kSeg * u + 4 * lane, last4);
-        kr[u] = __builtin_bit_cast(u32x4, *reinterpret_cast<const float4*>(srow + i));
-      } else {
-        kr[u] = (u32x4){0u, 0u, 0u, 0u};
-      }
+  for (int u = 0; u < kRegBlocks; u++) {
+    if (u < nb) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) kr[u][e] = __float_as_uint(srow[min(s0 + kSeg * u + 64 * e + lane, m - 1)]);
+    } else {
+      kr[u] = (u32x4){0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();  // histogram cleared
 #pragma unroll
   for (int u = 0; u < kRegBlocks; u++) {
     if (u < nb) {
-      const int i = s0 + kSeg * u + 4 * lane;
+      const int i = s0 + kSeg * u + lane;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         // positions past the segment (values from a clamped load) hold key 0 and are never counted:
-        // every later pass tests i + e < s1 again
+        // every later pass tests i + 64 * e < s1 again
         unsigned int key = 0u;
-        if (i + e < s1) {
+        if (i + 64 * e < s1) {
           key = score_key(__uint_as_float(kr[u][e]));
           atomicAdd(&h[key >> 24], 1u);
         }
@@ -573,10 +571,10 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
 #pragma unroll
       for (int u = 0; u < kRegBlocks; u++) {
         if (u < nb) {
-          const int i = s0 + kSeg * u + 4 * lane;
+          const int i = s0 + kSeg * u + lane;
 #pragma unroll
           for (int e = 0; e < 4; e++)
-            if (i + e < s1 && (kr[u][e] >> (shift + 8)) == prefix) atomicAdd(&h[(kr[u][e] >> shift) & 255u], 1u);
+            if (i + 64 * e < s1 && (kr[u][e] >> (shift + 8)) == prefix) atomicAdd(&h[(kr[u][e] >> shift) & 255u], 1u);
         }
       }
       __syncthreads();
@@ -597,11 +595,11 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
 #pragma unroll
   for (int u = 0; u < kRegBlocks; u++) {
     if (u < nb) {
-      const int i = s0 + kSeg * u + 4 * lane;
+      const int i = s0 + kSeg * u + lane;
       unsigned int cmask = 0;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const bool v = i + e < s1;
+        const bool v = i + 64 * e < s1;
         const unsigned int top = kr[u][e] >> 16;
         n_above += (v && top > prefix) ? 1u : 0u;
         cmask |= (v && top == prefix) ? 1u << e : 0u;
@@ -612,7 +610,7 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
         for (int e = 0; e < 4; e++) {
           if (cmask & (1u << e)) {
             if (slot < (unsigned int)kHistWords) {
-              clist[slot] = (unsigned int)(i + e);
+              clist[slot] = (unsigned int)(i + 64 * e);
               ckey[slot] = kr[u][e];
             }
             slot++;
@@ -658,10 +656,10 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
 #pragma unroll
     for (int u = 0; u < kRegBlocks; u++) {
       if (u < nb) {
-        const int i = s0 + kSeg * u + 4 * lane;
+        const int i = s0 + kSeg * u + lane;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const bool v = i + e < s1;
+          const bool v = i + 64 * e < s1;
           n_gt += (v && kr[u][e] > prefix) ? 1u : 0u;
           n_eq += (v && kr[u][e] == prefix) ? 1u : 0u;
         }
@@ -687,42 +685,28 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
   // [k] positions, then (candidate output) [k] keys; 2k <= kHistWords - 1: the last word is the dummy slot
   unsigned int* stage = hist;
+  // positions 256u + 64e + lane: row order is (u, e, lane), so one ballot per key vector ranks the keys
 #pragma unroll
   for (int u = 0; u < kRegBlocks; u++) {
     if (u < nb) {
-      const int i = s0 + kSeg * u + 4 * lane;
-      unsigned int eq_mask = 0, gt_mask = 0;
+      const int i = s0 + kSeg * u + lane;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const bool v = i + e < s1;
-        gt_mask |= (v && kr[u][e] > tau) ? (1u << e) : 0u;
-        eq_mask |= (v && kr[u][e] == tau) ? (1u << e) : 0u;
-      }
-      unsigned int sel_mask = gt_mask;
-      if (__ballot(eq_mask != 0) != 0) {  // keys equal to tau: the first k_rem of them in row order
-        unsigned int e_before, e_total;
-        lane_scan3((unsigned int)__popc(eq_mask), &e_before, &e_total);
-        unsigned int er = e_run + e_before;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          if (eq_mask & (1u << e)) {
-            if (er < (unsigned int)k_rem) sel_mask |= 1u << e;
-            er++;
-          }
+        const bool v = i + 64 * e < s1;
+        bool sel = v && kr[u][e] > tau;
+        const bool eq = v && kr[u][e] == tau;
+        const unsigned long long be = __ballot(eq);
+        if (be != 0ull) {  // keys equal to tau: the first k_rem of them in row order
+          sel = sel || (eq && e_run + lanes_below(be) < (unsigned int)k_rem);
+          e_run += (unsigned int)__popcll(be);
         }
-        e_run += e_total;
+        const unsigned long long bs = __ballot(sel);
+        const unsigned int op = p_run + lanes_below(bs);
+        const bool st = sel && op < (unsigned int)k;
+        stage[st ? op : kHistWords - 1] = (unsigned int)(i + 64 * e);
+        if (DST == kDstCand) stage[st ? k + op : kHistWords - 1] = kr[u][e];
+        p_run += (unsigned int)__popcll(bs);
       }
-      unsigned int s_before, s_total;
-      lane_scan3((unsigned int)__popc(sel_mask), &s_before, &s_total);
-      unsigned int op = p_run + s_before;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const bool sel = (sel_mask & (1u << e)) && op < (unsigned int)k;
-        stage[sel ? op : kHistWords - 1] = (unsigned int)(i + e);
-        if (DST == kDstCand) stage[sel ? k + op : kHistWords - 1] = kr[u][e];
-        op += (sel_mask >> e) & 1u;
-      }
-      p_run += s_total;
     }
   }
   __syncthreads();
@@ -1316,7 +1300,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
                        n_kv, k, idx);
     return hipGetLastError();
   }
-  if (p.mode == TopkPlan::kSingle && rows16 && n_kv <= kRegKeys && k < kHistWords) {
+  if (p.mode == TopkPlan::kSingle && n_kv <= kRegKeys && k < kHistWords) {
     hipLaunchKernelGGL(topk_reg_kernel<kDstIdx>, dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld, n_q, n_kv, k,
                        n_kv, 1, idx, nullptr, nullptr);
     return hipGetLastError();
@@ -1344,7 +1328,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   a.okey = ckey;
   a.opos = cpos;
   a.vec4 = rows16;  // chunk starts are multiples of 256 keys
-  if (rows16 && p.chunk <= kRegKeys && 2 * k < kHistWords)
+  if (p.chunk <= kRegKeys && 2 * k < kHistWords)
     hipLaunchKernelGGL(topk_reg_kernel<kDstCand>, dim3(n_q, B, p.n_chunks), dim3(kTkThreads), 0, stream, scores,
                        ld, n_q, n_kv, k, p.chunk, p.n_chunks, nullptr, ckey, cpos);
   else

@@ -247,7 +247,7 @@ def test_topk_long_rows_many_rows_bit_exact(orc, dsa):
 @pytest.mark.parametrize("extra_ld", [0, 1])
 def test_topk_two_stage_all_row_lengths(orc, dsa, extra_ld):
     """One causal prefill of 36000 queries in one call: rows longer than 32768 keys take two stages (chunks
-    of 18176 keys; aligned rows select their chunks in registers, unaligned ones in LDS).  Sampled rows
+    of 18176 keys selected in registers), with a row pitch that is and is not a multiple of 4.  Sampled rows
     cover every chunk case: a second chunk wholly past the row's end, one holding at most k keys (exactly
     k, k + 1), ragged tails, rows of at most k keys, and rows of ties, -inf and signed zeros; each is
     compared with the oracle bit for bit."""
