@@ -480,14 +480,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_select_kernel(TopkArgs a) {
 // compute unit and one's barriers and memory waits overlap the other's passes.  DST = kDstIdx selects
 // whole rows; DST = kDstCand is stage one of the two-stage plan for longer rows: blockIdx.z is the chunk
 // of `chunk` keys (a multiple of 256, at most kRegKeys), whose top k go out as keys and positions.
+// SRC = kSrcCand is stage two: the row is the n_in (key, position) candidates of stage one.
 constexpr int kRegBlocks = 16;
 constexpr int kRegKeys = kTkWaves * kRegBlocks * kSeg;  // 32768
 
-template <int DST>
+template <int SRC, int DST>
 __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __restrict__ scores, int64_t ld,
                                                                  int n_q, int n_kv, int k, int chunk, int n_chunks,
                                                                  int32_t* __restrict__ idx, uint32_t* __restrict__ okey,
-                                                                 int32_t* __restrict__ opos) {
+                                                                 int32_t* __restrict__ opos,
+                                                                 const uint32_t* __restrict__ ckey_in,
+                                                                 const int32_t* __restrict__ cpos_in, int n_in) {
   __shared__ unsigned int hist[kHistWords];   // histograms; then the candidates' positions; then the output
   __shared__ unsigned int misc[kMiscWords];   // [64] scratch + [256] summed histogram
   __shared__ unsigned int ckey[kHistWords];   // the candidates' keys
@@ -505,11 +508,14 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
     return;
   }
   const int lo = DST == kDstCand ? (int)blockIdx.z * chunk : 0;
-  const int m = DST == kDstCand ? min(n, lo + chunk) - lo : n;  // keys of this chunk (<= 0: past pos_t)
+  // keys of this row, chunk (<= 0: past pos_t) or candidate list
+  const int m = SRC == kSrcCand ? n_in : DST == kDstCand ? min(n, lo + chunk) - lo : n;
+  const uint32_t* crow = SRC == kSrcCand ? ckey_in + rowid * (size_t)n_in : nullptr;
+  const int32_t* cprow = SRC == kSrcCand ? cpos_in + rowid * (size_t)n_in : nullptr;
   const size_t ostride = (size_t)n_chunks * k;
   uint32_t* out_key = DST == kDstCand ? okey + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
   int32_t* out_pos = DST == kDstCand ? opos + rowid * ostride + (size_t)blockIdx.z * k : nullptr;
-  const float* srow = scores + rowid * ld + lo;
+  const float* srow = SRC == kSrcScores ? scores + rowid * ld + lo : nullptr;
   if (DST == kDstCand && m <= k) {  // the whole chunk is candidates (none when m <= 0); pad with key 0
     for (int i = tid; i < k; i += kTkThreads) {
       const bool v = i < m;
@@ -532,7 +538,10 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   for (int u = 0; u < kRegBlocks; u++) {
     if (u < nb) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) kr[u][e] = __float_as_uint(srow[min(s0 + kSeg * u + 64 * e + lane, m - 1)]);
+      for (int e = 0; e < 4; e++) {
+        const int i = min(s0 + kSeg * u + 64 * e + lane, m - 1);
+        kr[u][e] = SRC == kSrcCand ? crow[i] : __float_as_uint(srow[i]);
+      }
     } else {
       kr[u] = (u32x4){0u, 0u, 0u, 0u};
     }
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
         // every later pass tests i + 64 * e < s1 again
         unsigned int key = 0u;
         if (i + 64 * e < s1) {
-          key = score_key(__uint_as_float(kr[u][e]));
+          key = SRC == kSrcCand ? kr[u][e] : score_key(__uint_as_float(kr[u][e]));
           atomicAdd(&h[key >> 24], 1u);
         }
         kr[u][e] = key;
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   __syncthreads();
   for (int j = tid; j < k; j += kTkThreads) {
     if (DST == kDstIdx) {
-      out_idx[j] = (int)stage[j];
+      out_idx[j] = SRC == kSrcCand ? cprow[stage[j]] : (int)stage[j];
     } else {
       out_key[j] = stage[k + j];
       out_pos[j] = lo + (int)stage[j];
@@ -1301,8 +1310,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
     return hipGetLastError();
   }
   if (p.mode == TopkPlan::kSingle && n_kv <= kRegKeys && k < kHistWords) {
-    hipLaunchKernelGGL(topk_reg_kernel<kDstIdx>, dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld, n_q, n_kv, k,
-                       n_kv, 1, idx, nullptr, nullptr);
+    hipLaunchKernelGGL((topk_reg_kernel<kSrcScores, kDstIdx>), dim3(n_q, B), dim3(kTkThreads), 0, stream, scores, ld,
+                       n_q, n_kv, k, n_kv, 1, idx, nullptr, nullptr, nullptr, nullptr, 0);
     return hipGetLastError();
   }
   if (p.mode == TopkPlan::kSingle) {
@@ -1329,8 +1338,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   a.opos = cpos;
   a.vec4 = rows16;  // chunk starts are multiples of 256 keys
   if (p.chunk <= kRegKeys && 2 * k < kHistWords)
-    hipLaunchKernelGGL(topk_reg_kernel<kDstCand>, dim3(n_q, B, p.n_chunks), dim3(kTkThreads), 0, stream, scores,
-                       ld, n_q, n_kv, k, p.chunk, p.n_chunks, nullptr, ckey, cpos);
+    hipLaunchKernelGGL((topk_reg_kernel<kSrcScores, kDstCand>), dim3(n_q, B, p.n_chunks), dim3(kTkThreads), 0, stream,
+                       scores, ld, n_q, n_kv, k, p.chunk, p.n_chunks, nullptr, ckey, cpos, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((topk_select_kernel<kSrcScores, kDstCand>), dim3(n_q, B, p.n_chunks), dim3(kTkThreads),
                        lds_bytes(p.chunk), stream, a);
@@ -1343,8 +1352,12 @@ hipError_t launch_topk(const float* scores, int64_t ld, int B, int n_q, int n_kv
   c.vec4 = (c.n_cand & 3) == 0;  // the workspace is 256-byte aligned
   c.okey = nullptr;
   c.opos = nullptr;
-  hipLaunchKernelGGL((topk_select_kernel<kSrcCand, kDstIdx>), dim3(n_q, B, 1), dim3(kTkThreads),
-                     lds_bytes(c.n_cand), stream, c);
+  if (c.n_cand <= kRegKeys && k < kHistWords)
+    hipLaunchKernelGGL((topk_reg_kernel<kSrcCand, kDstIdx>), dim3(n_q, B), dim3(kTkThreads), 0, stream, nullptr, 0,
+                       n_q, n_kv, k, 0, 1, idx, nullptr, nullptr, ckey, cpos, c.n_cand);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<kSrcCand, kDstIdx>), dim3(n_q, B, 1), dim3(kTkThreads),
+                       lds_bytes(c.n_cand), stream, c);
   return hipGetLastError();
 }
 
