@@ -16,6 +16,8 @@
 // (one query per sequence): the row is split into chunks so that thousands of waves stream keys.
 #include "dsa_internal.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 // ------------------------------------------------------------------------------------------------
@@ -180,6 +182,40 @@ __device__ __forceinline__ void score_key_group(const KeyGroup& g, const v8i (&q
   }
 }
 
+// Decode key groups are read contiguously: load u of lane l brings bytes 16(l%8) .. +16 of key g0 + 8u + l/8,
+// so every wave-wide load covers 1 KiB of whole 128-byte rows (the operand layout, 32 bytes of one key per
+// lane, touches each row in half-line pieces and streams about 12 % slower).  Each 16-key block is then
+// turned into the matrix-core layout through a per-wave LDS slot: 16-byte chunk c of row r at chunk
+// c ^ ((r >> 1) & 7), so both the contiguous writes and the operand reads hit every bank once.
+struct RawGroup {
+  u32x4 r[8];
+  float ksc;
+};
+__device__ __forceinline__ void load_raw_group(const uint8_t* __restrict__ kb, const float* __restrict__ ksb, int g0,
+                                               int n_kv, int lane, RawGroup& g) {
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int s = min(g0 + 8 * u + (lane >> 3), n_kv - 1);
+    g.r[u] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)s * kDI + (lane & 7) * 16));
+  }
+  g.ksc = __builtin_nontemporal_load(ksb + min(g0 + lane, n_kv - 1));
+}
+// Blocks 2h and 2h+1 of a raw group into kf[2h], kf[2h+1] through the wave's 4 KiB slot `tr`.
+__device__ __forceinline__ void transpose_pair(const RawGroup& g, int h, char* tr, int lane, KeyGroup& kg) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {  // load 4h + q: rows 8q .. 8q+7 of the 32-row pair slot
+    const int r = 8 * q + (lane >> 3), c = lane & 7;
+    *(u32x4*)(tr + r * 128 + 16 * (c ^ ((r >> 1) & 7))) = g.r[4 * h + q];
+  }
+#pragma unroll
+  for (int jj = 0; jj < 2; jj++) {
+    const int r = 16 * jj + (lane & 15), c0 = 2 * (lane >> 4);
+    const u32x4 lo = *(const u32x4*)(tr + r * 128 + 16 * (c0 ^ ((r >> 1) & 7)));
+    const u32x4 hi = *(const u32x4*)(tr + r * 128 + 16 * ((c0 + 1) ^ ((r >> 1) & 7)));
+    kg.kf[2 * h + jj] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+}
+
 // One query per wave (decode) stages its scores in LDS and writes them out after its last key load.
 // Stores count in the same counter as loads and their acknowledgements come back slowly under a full
 // read stream, so a store issued per group holds every later wait for the next group's keys: the
@@ -212,6 +248,8 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   constexpr bool kStaged = QW == 1;  // chunk_keys <= kStageKeys then (checked by the launch)
   __shared__ float stage_all[kStaged ? 4 * kStageKeys : 1];
   float* stage = stage_all + (kStaged ? (threadIdx.x >> 6) * kStageKeys : 0);
+  __shared__ __attribute__((aligned(16))) char tr_all[kStaged ? 4 * 4096 : 16];  // decode: transpose slots
+  char* tr = tr_all + (kStaged ? (threadIdx.x >> 6) * 4096 : 0);
 
   const uint8_t* kb = k8 + (size_t)b * n_kv * kDI;
   const float* ksb = k_scale + (size_t)b * n_kv;
@@ -243,10 +281,15 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   // Key loads are unconditional (indexes are clamped into the row, so groups past the range re-read
   // in-bounds keys that are never scored): with no load skipped on any path, each wait below covers
   // exactly the group it needs.
-  KeyGroup ring[NB];
+  using Ring = typename std::conditional<kStaged, RawGroup, KeyGroup>::type;
+  auto load_group = [&](int g0, Ring& g) {
+    if constexpr (kStaged) load_raw_group(kb, ksb, g0, n_kv, lane, g);
+    else load_key_group<false>(kb, ksb, g0, n_kv, lane, g);
+  };
+  Ring ring[NB];
 #pragma unroll
   for (int p = 0; p < NB - 1; p++) {
-    load_key_group<QW == 1>(kb, ksb, s_begin + 64 * p, n_kv, lane, ring[p]);
+    load_group(s_begin + 64 * p, ring[p]);
     // in issue order, each group's scale right after its keys: the wait for a group's scale then
     // never covers the keys of the group after it
     __builtin_amdgcn_sched_barrier(0);
@@ -256,10 +299,14 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   // with no early exit (every slot index static, every wait exact); loads for group i + NB - 1 are
   // issued before group i is scored.  The last n_groups % NB groups are already in slots 0.. and are
   // scored after the loop.
-  auto score = [&](const KeyGroup& g, int g0) {
+  auto score = [&](const Ring& g, int g0) {
     if constexpr (kStaged) {
+      KeyGroup kg;
+      transpose_pair(g, 0, tr, lane, kg);
+      transpose_pair(g, 1, tr, lane, kg);
+      kg.ksc = g.ksc;
       float out[1];
-      key_group_scores<1>(g, qa, ww, out);
+      key_group_scores<1>(kg, qa, ww, out);
       stage[g0 - s_begin + lane] = out[0];  // < chunk_keys: groups start inside the chunk
     } else {
       score_key_group<QW>(g, qa, ww, g0, s_end, pos0, nq_here, lane, srow, ld);
@@ -271,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
 #pragma unroll
     for (int p = 0; p < NB; p++) {
       const int g0 = s_begin + 64 * (gi + p);
-      load_key_group<QW == 1>(kb, ksb, g0 + 64 * (NB - 1), n_kv, lane, ring[(p + NB - 1) % NB]);
+      load_group(g0 + 64 * (NB - 1), ring[(p + NB - 1) % NB]);
       score(ring[p], g0);
       __builtin_amdgcn_sched_barrier(0);  // one group at a time: no loads hoisted across groups
     }
