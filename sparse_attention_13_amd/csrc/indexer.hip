@@ -255,6 +255,23 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
   const float* ksb = k_scale + (size_t)b * n_kv;
   float* srow = scores + ((size_t)b * n_q + t0) * ld;
 
+  // Key loads are unconditional (indexes are clamped into the row, so groups past the range re-read
+  // in-bounds keys that are never scored): with no load skipped on any path, each wait below covers
+  // exactly the group it needs.
+  using Ring = typename std::conditional<kStaged, RawGroup, KeyGroup>::type;
+  auto load_group = [&](int g0, Ring& g) {
+    if constexpr (kStaged) load_raw_group(kb, ksb, g0, n_kv, lane, g);
+    else load_key_group<false>(kb, ksb, g0, n_kv, lane, g);
+  };
+  Ring ring[NB];
+#pragma unroll
+  for (int p = 0; p < NB - 1; p++) {
+    load_group(s_begin + 64 * p, ring[p]);
+    // in issue order, each group's scale right after its keys: the wait for a group's scale then
+    // never covers the keys of the group after it
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // A operands: row block mb holds heads 16*mb .. 16*mb+15; lane l supplies head 16*mb + l%16,
   // bytes 32*(l/16) .. +32 of that head's 128-byte query.
   v8i qa[QW][4];
@@ -274,26 +291,9 @@ __global__ __launch_bounds__(256, 2) void indexer_fp8_kernel(const uint8_t* __re
         ww[qi][mb][r] = w[qrow * kHI + h] * q_scale[qrow * kHI + h];
       }
   }
-  // The query side is complete before any key load is issued: the loop below then only ever waits for
-  // key groups, never (through the wait analysis' merge at the loop head) for everything in flight.
+  // One wait for the query side and the first key groups together (the key loads were issued first, so
+  // the two memory round trips overlap); the loop below then only ever waits for key groups.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
-  // Key loads are unconditional (indexes are clamped into the row, so groups past the range re-read
-  // in-bounds keys that are never scored): with no load skipped on any path, each wait below covers
-  // exactly the group it needs.
-  using Ring = typename std::conditional<kStaged, RawGroup, KeyGroup>::type;
-  auto load_group = [&](int g0, Ring& g) {
-    if constexpr (kStaged) load_raw_group(kb, ksb, g0, n_kv, lane, g);
-    else load_key_group<false>(kb, ksb, g0, n_kv, lane, g);
-  };
-  Ring ring[NB];
-#pragma unroll
-  for (int p = 0; p < NB - 1; p++) {
-    load_group(s_begin + 64 * p, ring[p]);
-    // in issue order, each group's scale right after its keys: the wait for a group's scale then
-    // never covers the keys of the group after it
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
   // Ring of NB key groups: group i lives in slot i % NB.  The main loop runs whole rounds of NB groups
   // with no early exit (every slot index static, every wait exact); loads for group i + NB - 1 are

@@ -549,6 +549,56 @@ def test_forward_decode_vs_oracle(orc, dsa, B, S):
     assert n_att >= math.ceil(MIN_IDENTICAL * B), n_att
 
 
+def _decode_with_patterns(B, S, seed):
+    """Decode inputs with sequences whose score rows stress the decode top-k: exact ties that overflow a
+    chunk's candidate slot, all-zero rows, non-positive rows, exact ties across chunks, and the top k
+    crowded into one chunk (so that the chunk thresholds cannot cover the selection)."""
+    x = synth.decode(B, S, seed=seed, device=DEV)
+    k8, ks, w = x["k8"], x["k_scale"], x["w"]
+    k8[1, 4096:8192] = k8[1, 4096]                 # 4096 identical keys: one chunk's slot overflows
+    ks[1, 4096:8192] = ks[1, 4096]
+    w[2] = 0.0                                     # every score 0: every chunk overflows
+    w[3] = -w[3].abs()                             # scores <= 0
+    k8[4, S // 2:S // 2 + 2048] = k8[4, :2048]     # exact ties between distant chunks
+    ks[4, S // 2:S // 2 + 2048] = ks[4, :2048]
+    ks[5, 1000:2500] *= 64.0                       # most of the top k inside one chunk
+    return x
+
+
+@pytest.mark.parametrize("B,S", [(64, 8191), (64, 32801), (64, 131072)])
+def test_forward_decode_matches_stage_calls(orc, dsa, B, S):
+    """dsa_forward_decode against the separate decode stage calls (indexer scores, dsa_topk_decode, sparse
+    attention) on the same inputs: scores, selection and attention output equal bit for bit, including the
+    patterned sequences (candidate-slot overflow from ties, all-zero and non-positive scores, ties across
+    chunks, the top k crowded into one chunk); the selection of those sequences is also checked against the
+    oracle's top-k on the GPU's scores."""
+    x = _decode_with_patterns(B, S, seed=300)
+    k = 2048
+    ld = (S + 63) // 64 * 64
+    ws = torch.empty(dsa.forward_workspace_size(B, 1, S, 128, 576, 512, k, dsa.DSA_BF16), dtype=torch.uint8,
+                     device=DEV)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
+                              x["sm_scale"], decode=True, idx_out=idx, workspace=ws)
+    sc_fwd = ws[:B * ld * 4].view(torch.float32).view(B, ld)[:, :S].clone()
+    sc = torch.empty((B, S), dtype=torch.float32, device=DEV)
+    dsa.indexer_scores_decode(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], sc)
+    idx_s = dsa.topk_decode(sc, S, k)
+    out_s, lse_s = dsa.sparse_mla_attn_decode(x["q"], x["kv"], idx_s, 512, x["sm_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(sc_fwd, sc)
+    gi, si = idx.cpu().numpy(), idx_s.cpu().numpy()
+    bad = [b for b in range(B) if not np.array_equal(gi[b], si[b])]
+    assert not bad, bad
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
+    sc_h = sc.cpu().numpy()
+    pos = np.array([S - 1], np.int64)
+    for b in (0, 1, 2, 3, 4, 5, B - 1):
+        oi, _ = orc.topk(sc_h[b:b + 1], pos, k)
+        assert np.array_equal(gi[b], oi[0]), b
+    print(f"[decode forward {B}x{S}] rows identical to the stage calls: {B}; oracle top-k rows: 7")
+
+
 # ------------------------------------------------------------------------------------------ full-size workloads
 
 def full_indexer_rows(orc, dsa, x, rows, L, n_q, what):
