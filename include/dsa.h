@@ -122,7 +122,7 @@ size_t dsa_topk_workspace_size(int B, int n_q, int n_kv, int k);
  * out [B][n_q][H][d_v] in `dtype`, lse [B][n_q][H] fp32 or NULL.  A row with no valid entry gets
  * out = 0 and lse = -inf.  sm_scale finite and > 0.
  * dtype = DSA_BF16: q, kv, out are bf16 (fp32 accumulation).  Fast path H = 128, d_qk = 576,
- *   d_v = 512 (CDNA4 bf16 matrix cores).
+ *   d_v = 512 (CDNA4 bf16 matrix cores), n_kv <= 2^21 (DSA_ERR_UNSUPPORTED otherwise).
  * dtype = DSA_F32: q, kv, out fp32 (generic kernel: H <= 64, d_qk <= 256, d_v <= d_qk).
  * workspace: device memory of at least dsa_sparse_mla_attn_workspace_size(...) bytes, 256-byte
  *   aligned (may be NULL when that size is 0).

@@ -114,6 +114,9 @@ dsa_status_t plan_attn(int B, int n_q, int n_kv, int H, int d_qk, int d_v, int k
   if (dtype == DSA_BF16) {
     if (!(H == 128 && d_qk == 576 && d_v == 512))
       return fail(DSA_ERR_UNSUPPORTED, "attn: bf16 supports H=128, d_qk=576, d_v=512 (got %d, %d, %d)", H, d_qk, d_v);
+    // the kernel's row gathers address the rope part of a row with a 32-bit byte offset from the sequence's
+    // base (row * 1152 + 1152 bytes at most), exact for every row below 2^21
+    if (n_kv > (1 << 21)) return fail(DSA_ERR_UNSUPPORTED, "attn: bf16 supports n_kv <= 2^21 (got %d)", n_kv);
     p->fast = true;
     p->n_split = dsa::mla_bf16_pick_split(B, n_q, k);
     p->ws = dsa::mla_bf16_workspace_bytes(B, n_q, p->n_split);

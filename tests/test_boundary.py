@@ -145,6 +145,11 @@ def test_attention_validation_and_workspace(L):
     assert f(*args) == DSA_ERR_WORKSPACE
     # many queries: no workspace needed
     assert L.dsa_sparse_mla_attn_workspace_size(1, 4096, 4096, 128, 576, 512, 2048, DSA_BF16) == 0
+    # the bf16 kernel takes at most 2^21 rows per sequence (its row offsets are 32-bit)
+    big = [FAKE, FAKE, FAKE, 1, 1, (1 << 21) + 1, 128, 576, 512, 2048, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
+    assert f(*big) == DSA_ERR_UNSUPPORTED
+    assert L.dsa_sparse_mla_attn_workspace_size(1, 1, (1 << 21) + 1, 128, 576, 512, 2048, DSA_BF16) == 0
+    assert L.dsa_sparse_mla_attn_workspace_size(1, 1, 1 << 21, 128, 576, 512, 2048, DSA_BF16) > 0
     bad = [FAKE, FAKE, None, 1, 1, 10, 128, 576, 512, 8, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
     assert f(*bad) == DSA_ERR_INVALID_ARG
     bad = [FAKE, FAKE, FAKE, 1, 1, 10, 64, 576, 512, 8, 0.04, DSA_BF16, FAKE2, None, None, 0, None]
