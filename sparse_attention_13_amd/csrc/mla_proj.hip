@@ -72,7 +72,7 @@ __device__ __forceinline__ void mma_step(const char* at, const char* wt, const i
 
 // C[m][n] = sum_k A[m][k] W[n][k] for one head; A row m at a + m*lda, W [N][K], C row m at c + m*ldc.
 // Optionally copies rope[m][0..n_rope) to c + m*ldc + N (blocks of column tile 0).
-__global__ __launch_bounds__(256) void proj_gemm_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t a_head,
+__global__ __launch_bounds__(256, 4) void proj_gemm_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t a_head,
                                                         const uint16_t* __restrict__ w, int64_t w_head,
                                                         uint16_t* __restrict__ c, int64_t ldc, int64_t c_head, int M,
                                                         int N, int K, const uint16_t* __restrict__ rope,
