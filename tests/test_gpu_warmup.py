@@ -161,3 +161,35 @@ def test_warmup_backward_full_8k(orc, dsa):
         wt = (dts > 0) * np.abs(gb[t, s])[:, None] * np.abs(w[t])
         bk = np.einsum("th,thd->d", wt.astype(np.float64), np.abs(qh[t]).astype(np.float64))
         assert np.all(np.abs(dk[0][s] - k_o[0]) <= 2.0 ** -20 * bk + 1e-30), s
+
+
+def test_warmup_backward_key_block_major_order(orc, dsa):
+    """Four sequences of 6144 queries over 6144 keys: the query codes (4 x 6144 x 8 KiB, 201 MB) pass the
+    size at which the dk kernel runs its workgroups key block by key block instead of part by part, with
+    the sequence as the third grid dimension.  dq and dw on sampled rows, dk on sampled keys of every
+    sequence (each as a one-key problem over the queries that see it).  Exact inputs as above."""
+    B, L = 4, 6144
+    xi = exact_indexer_inputs(B, L, L, seed=91)
+    g = torch.randint(-31, 32, (B, L, L), generator=torch.Generator().manual_seed(92)).float() / 1024.0
+    dq, dw, dk = run_backward(dsa, xi, g)
+    rows = np.array([0, 31, 1024, 4097, 6143])
+    for b in range(B):
+        qh = orc.dequant_e4m3(xi["q8"][b].numpy(), xi["qs"][b].numpy())
+        kh = orc.dequant_e4m3(xi["k8"][b].numpy(), xi["ks"][b].numpy())
+        w, gb = xi["w"][b].numpy(), g[b].numpy()
+        q_o, w_o, _ = orc.warmup_backward(qh[rows], w[rows], kh, gb[rows], rows.astype(np.int64))
+        d = np.matmul(qh[rows].astype(np.float64), kh.T.astype(np.float64))
+        on = (d > 0) * np.where(np.arange(L)[None, :] <= rows[:, None], np.abs(gb[rows]), 0.0)[:, None, :]
+        bq = np.matmul(on, np.abs(kh).astype(np.float64)) * np.abs(w[rows])[:, :, None]
+        bw = np.sum(on * np.maximum(d, 0), axis=2)
+        assert np.all(np.abs(dq[b][rows] - q_o) <= 2.0 ** -20 * bq + 1e-30), b
+        assert np.all(np.abs(dw[b][rows] - w_o) <= 2.0 ** -20 * bw + 1e-30), b
+        for s in (0, 255, 256, 3071, 6143):
+            t = np.arange(s, L)
+            _, _, k_o = orc.warmup_backward(qh[t], w[t], kh[s:s + 1], gb[t][:, s:s + 1].copy(),
+                                            np.zeros(len(t), np.int64))
+            dts = np.matmul(qh[t], kh[s])
+            wt = (dts > 0) * np.abs(gb[t, s])[:, None] * np.abs(w[t])
+            bk = np.einsum("th,thd->d", wt.astype(np.float64), np.abs(qh[t]).astype(np.float64))
+            assert np.all(np.abs(dk[b][s] - k_o[0]) <= 2.0 ** -20 * bk + 1e-30), (b, s)
+            assert np.abs(k_o).max() > 0
