@@ -257,7 +257,8 @@ dsa_status_t dsa_sparse_kl_loss(float* scores, int64_t ld_scores, const float* p
  * query), o_lat [rows][H][d_c] (its output), o [rows][H][d_v].  Weights are row-major with the
  * contraction dimension last: w_ukt [H][d_c][d_nope] (w_ukt[h][c][d] = W_UK,h[d][c]) and
  * w_uv [H][d_v][d_c].  bf16 in and out, fp32 accumulation; d_nope = 128, d_rope = 64, d_c = 512,
- * d_v = 128, any H.  All pointers 16-byte aligned.  Other shapes: DSA_ERR_UNSUPPORTED.
+ * d_v = 128, any H, rows <= 2^30 and at most 2^31 - 1 workgroups (rows / 128 * H * 4 for the absorption).
+ * All pointers 16-byte aligned.  Other shapes: DSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------------------------ */
 dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa, int rows, int H,
                               int d_nope, int d_rope, int d_c, dsa_dtype_t dtype, void* stream);

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -283,7 +284,11 @@ extern "C" {
 int dsa_version(void) { return 100; }
 
 const char* dsa_status_string(dsa_status_t s) {
-  switch (s) {
+  // A C caller may pass any int: read the bits as an int (a C++ load of an enum outside its range is
+  // undefined), then compare.
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case DSA_OK: return "DSA_OK";
     case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
     case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: no kernel for this dtype/shape";
@@ -421,8 +426,8 @@ dsa_status_t dsa_mla_absorb_q(const void* q_mha, const void* w_ukt, void* q_mqa,
   if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "absorb_q: rows and H must be positive");
   if (dtype != DSA_BF16 || d_nope != 128 || d_rope != 64 || d_c != 512)
     return fail(DSA_ERR_UNSUPPORTED, "absorb_q: supports bf16 with d_nope=128, d_rope=64, d_c=512");
-  if (((long long)(rows + 127) / 128 * H + 7) / 8 * 8 * 4 > 0x7FFFFFFFLL)
-    return fail(DSA_ERR_UNSUPPORTED, "absorb_q: grid too large");
+  if (rows > (1 << 30) || (((long long)rows + 127) / 128 * H + 7) / 8 * 8 * 4 > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "absorb_q: rows <= 2^30 and a grid below 2^31 workgroups");
   if (!q_mha || !w_ukt || !q_mqa) return fail(DSA_ERR_INVALID_ARG, "absorb_q: null pointer");
   if (!(aligned(q_mha, 16) && aligned(w_ukt, 16) && aligned(q_mqa, 16)))
     return fail(DSA_ERR_INVALID_ARG, "absorb_q: pointers must be 16-byte aligned");
@@ -436,8 +441,8 @@ dsa_status_t dsa_mla_out_proj(const void* o_lat, const void* w_uv, void* o, int 
   if (rows < 1 || H < 1) return fail(DSA_ERR_INVALID_ARG, "out_proj: rows and H must be positive");
   if (dtype != DSA_BF16 || d_c != 512 || d_v != 128)
     return fail(DSA_ERR_UNSUPPORTED, "out_proj: supports bf16 with d_c=512, d_v=128");
-  if (((long long)(rows + 127) / 128 * H + 7) / 8 * 8 > 0x7FFFFFFFLL)
-    return fail(DSA_ERR_UNSUPPORTED, "out_proj: grid too large");
+  if (rows > (1 << 30) || (((long long)rows + 127) / 128 * H + 7) / 8 * 8 > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "out_proj: rows <= 2^30 and a grid below 2^31 workgroups");
   if (!o_lat || !w_uv || !o) return fail(DSA_ERR_INVALID_ARG, "out_proj: null pointer");
   if (!(aligned(o_lat, 16) && aligned(w_uv, 16) && aligned(o, 16)))
     return fail(DSA_ERR_INVALID_ARG, "out_proj: pointers must be 16-byte aligned");

@@ -1223,7 +1223,7 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
     // few long rows: threshold candidates per chunk when a chunk's expected share of the row's top k is
     // small against the candidate capacity, with chunks as short as the merge's capacity allows
     for (int chunk = 2048; chunk <= kCandChunk; chunk *= 2) {
-      const int n_chunks = (n_kv + chunk - 1) / chunk;
+      const int n_chunks = (int)(((long long)n_kv + chunk - 1) / chunk);
       // t_lo: a chunk's expected share of the row's top k plus six standard deviations of it and a margin,
       // so that a chunk of independent scores holds more than t_lo of the row's top k essentially never
       const long long share = ((long long)k * chunk + n_kv - 1) / n_kv;
@@ -1244,7 +1244,7 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
   // positions), else of at most the LDS row cache
   const int cap = 2 * k < kHistWords ? kRegKeys : kKeyCap;
   int want = 1;
-  if (n_kv > cap) want = (n_kv + cap - 1) / cap;
+  if (n_kv > cap) want = (int)(((long long)n_kv + cap - 1) / cap);
   if (rows < 256) {
     // too few rows to fill the GPU: split each into chunks of at least 4k keys, aiming at one
     // workgroup per CU (a large chunk's row cache leaves room for only one), so that all chunks run
@@ -1254,7 +1254,7 @@ TopkPlan plan_topk(int B, int n_q, int n_kv, int k) {
   }
   if (want <= 1) return p;
   const int chunk = (int)((((long long)n_kv + want - 1) / want + kSeg - 1) / kSeg * kSeg);
-  const int n_chunks = (n_kv + chunk - 1) / chunk;
+  const int n_chunks = (int)(((long long)n_kv + chunk - 1) / chunk);
   if (n_chunks < 2 || chunk <= k || chunk > cap || (long long)n_chunks * k > kKeyCap) {
     if (n_kv > kKeyCap) p.mode = TopkPlan::kUncached;
     return p;

@@ -212,6 +212,8 @@ def test_projection_validation(L):
     assert o(FAKE, FAKE, ctypes.c_void_p(0x20002), 10, 128, 512, 128, DSA_BF16, None) == DSA_ERR_INVALID_ARG
     assert o(FAKE, FAKE, FAKE2, 2**31 - 1, 128, 512, 128, DSA_BF16, None) == DSA_ERR_UNSUPPORTED  # grid
     assert a(FAKE, FAKE, FAKE2, 2**30, 128, 128, 64, 512, DSA_BF16, None) == DSA_ERR_UNSUPPORTED    # grid
+    assert a(FAKE, FAKE, FAKE2, 2**31 - 1, 1, 128, 64, 512, DSA_BF16, None) == DSA_ERR_UNSUPPORTED  # rows
+    assert o(FAKE, FAKE, FAKE2, 2**30 + 1, 1, 512, 128, DSA_BF16, None) == DSA_ERR_UNSUPPORTED      # rows
 
 
 def test_warmup_validation(L):
