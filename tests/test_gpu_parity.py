@@ -549,6 +549,36 @@ def test_forward_decode_vs_oracle(orc, dsa, B, S):
     assert n_att >= math.ceil(MIN_IDENTICAL * B), n_att
 
 
+def _random_forward_cases(n, seed):
+    """Seeded shapes that walk the dispatch regimes of the forward: one query per sequence (decode plans),
+    2..7 queries (two-query indexer waves), 8..299 queries, and whole prefills; 1..2499 keys, k from 1 to
+    2048 (often above the row length), one to three sequences."""
+    gen = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        L = int(gen.integers(1, 2500))
+        n_q = [1, int(gen.integers(2, 8)), int(gen.integers(8, 300)), L][i % 4]
+        cases.append((int(gen.choice([1, 2, 3])), L, min(n_q, L), int(gen.choice([1, 5, 64, 333, 2048]))))
+    return cases
+
+
+@pytest.mark.parametrize("B,L,n_q,k", _random_forward_cases(12, 2024))
+def test_forward_random_shapes(orc, dsa, B, L, n_q, k):
+    """dsa_forward_prefill on random shapes against the oracle: every sequence's sampled rows (first,
+    last, around position k - 1, uniform others) by the band rule for the selection and elementwise for
+    the attention of the rows whose selection is identical."""
+    x = stack_prefill(B, L, n_q, seed=50 + L + 7 * k, n_needles=min(8, L // 64), with_mla=True)
+    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
+                              1.0 / math.sqrt(576), idx_out=idx)
+    torch.cuda.synchronize()
+    gi, go, gl = idx.cpu().numpy(), np32(out), np32(lse)
+    for b in range(B):
+        rows = _sample_rows(n_q, L, k, 12, np.random.default_rng(b))
+        check_forward_rows(orc, x["per_seq"][b], gi[b], go[b], gl[b], rows, L, n_q, k,
+                           f"random B={B} L={L} n_q={n_q} k={k} seq {b}")
+
+
 def _decode_with_patterns(B, S, seed):
     """Decode inputs with sequences whose score rows stress the decode top-k: exact ties that overflow a
     chunk's candidate slot, all-zero rows, non-positive rows, exact ties across chunks, and the top k
