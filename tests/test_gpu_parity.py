@@ -525,10 +525,10 @@ def test_decode_equals_last_prefill_row(orc, dsa):
     assert np.abs(np32(lse)[0] - gl_p[-1]).max() <= parity.LSE_ABS
 
 
-@pytest.mark.parametrize("B,S", [(4, 9000), (2, 40000)])
-def test_forward_decode_vs_oracle(orc, dsa, B, S):
-    x = synth.decode(B, S, seed=100, device=DEV)
-    k = 2048
+def _check_decode_forward(orc, dsa, B, S, k, seed):
+    """dsa_forward_decode for B sequences of S tokens against the oracle: each sequence's selection by the
+    band rule, and its attention elementwise when the selection is identical (at least 90% of them)."""
+    x = synth.decode(B, S, seed=seed, device=DEV)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
     out, lse, _ = dsa.forward(x["q8"], x["q_scale"], x["k8"], x["k_scale"], x["w"], x["q"], x["kv"], k, 512,
                               x["sm_scale"], decode=True, idx_out=idx)
@@ -541,12 +541,31 @@ def test_forward_decode_vs_oracle(orc, dsa, B, S):
         k_i = orc.dequant_e4m3(synth.u8(x["k8"][b]), x["k_scale"][b].cpu().numpy())
         sc = orc.indexer(q_i, np32(x["w"][b:b + 1]), k_i, pos, ld=S)
         oi, kth = orc.topk(sc, pos, k)
+        parity.assert_idx_wellformed(gi[b:b + 1], pos, k)
         ok, _ = parity.topk_band_match(gi[b:b + 1], oi, sc, kth, pos)
         assert ok == 1, b
         n_att += attention_on_oracle_selection(orc, bf16_np(x["q"][b:b + 1]), bf16_np(x["kv"][b]), gi[b:b + 1], oi,
                                                go[b:b + 1], gl[b:b + 1], 512, x["sm_scale"])[0]
-    print(f"[decode {B}x{S}] sequences {B}: attention compared {n_att}")
+    print(f"[decode {B}x{S} k={k}] sequences {B}: attention compared {n_att}", flush=True)
     assert n_att >= math.ceil(MIN_IDENTICAL * B), n_att
+
+
+@pytest.mark.parametrize("B,S", [(4, 9000), (2, 40000)])
+def test_forward_decode_vs_oracle(orc, dsa, B, S):
+    _check_decode_forward(orc, dsa, B, S, 2048, seed=100)
+
+
+def _random_decode_cases(n, seed):
+    """Seeded decode shapes: 1..8 sequences, 1..140000 tokens (log-uniform), k of 1, 100 or 2048: rows shorter
+    than k, the two-stage and the threshold-candidate top-k plans, split and unsplit attention."""
+    gen = np.random.default_rng(seed)
+    return [(int(gen.integers(1, 9)), int(np.exp(gen.uniform(0.0, np.log(140000.0)))) + 1,
+             int(gen.choice([1, 100, 2048]))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("B,S,k", _random_decode_cases(8, 77))
+def test_forward_decode_random_shapes(orc, dsa, B, S, k):
+    _check_decode_forward(orc, dsa, B, S, k, seed=300 + S)
 
 
 def _random_forward_cases(n, seed):
