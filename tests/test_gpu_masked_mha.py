@@ -112,3 +112,58 @@ def test_masked_mha_full_8k(orc, dsa):
     rows = np.array([0, 1, 63, 127, 128, 2047, 2048, 2049, 4095, 5000, 8064, 8191])
     check_rows(orc, m["q"], m["k"], m["v"], gi, out[0], lse[0], rows, m["sm_scale"], "8k")
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+# B, L, n_q, H, k_sel: a whole prefill of several key tiles, fewer queries than keys with k_sel above every
+# row's length, one query per sequence
+@pytest.mark.parametrize("B,L,n_q,H,k_sel", [(2, 700, 700, 4, 64), (1, 1500, 300, 2, 2048), (3, 200, 1, 3, 16)])
+def test_forward_masked_mha_vs_stage_calls_and_oracle(orc, dsa, B, L, n_q, H, k_sel):
+    """dsa_forward_prefill_masked_mha (indexer, top-k, masked MHA under the selection): its selection and
+    output equal, bit for bit, those of the stage calls on the same inputs; on sampled rows of every
+    sequence the selection matches the oracle's own (indexer and top-k on the dequantised codes) by the
+    band rule, and the output matches the MHA-form oracle attention over the oracle's selection on the rows
+    whose selections are identical."""
+    xi = [synth.prefill(L, seed=40 + b, device=DEV, n_q=n_q, n_needles=min(4, L // 64), with_mla=False)
+          for b in range(B)]
+    xm = [synth.mha_heads(L, seed=70 + b, device=DEV, n_q=n_q, H=H) for b in range(B)]
+    st = lambda xs, key: torch.stack([x[key] for x in xs]).contiguous()
+    q8, qs, k8, ks, w = st(xi, "q8"), st(xi, "q_scale"), st(xi, "k8"), st(xi, "k_scale"), st(xi, "w")
+    q, k, v = st(xm, "q"), st(xm, "k"), st(xm, "v")
+    sm_scale = 1.0 / math.sqrt(192)
+    idx = torch.empty((B, n_q, k_sel), dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.forward_masked_mha(q8, qs, k8, ks, w, q, k, v, k_sel, sm_scale, idx_out=idx)
+    scores = torch.empty((B, n_q, L), dtype=torch.float32, device=DEV)
+    dsa.indexer_scores(q8, qs, k8, ks, w, scores)
+    idx_s = dsa.topk(scores, L, k_sel)
+    out_s, lse_s = dsa.masked_mha_attn(q, k, v, idx_s, sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s)
+    assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
+    gi = idx.cpu().numpy()
+    n_cmp = n_rows = 0
+    for b in range(B):
+        rows = np.unique(np.concatenate([np.arange(min(3, n_q)), np.arange(max(0, n_q - 3), n_q),
+                                         np.random.default_rng(b).choice(n_q, size=min(6, n_q), replace=False)]))
+        pos = (L - n_q + rows).astype(np.int64)
+        tr = torch.as_tensor(rows, dtype=torch.long, device=DEV)
+        q_i = orc.dequant_e4m3(synth.u8(q8[b][tr]), qs[b][tr].cpu().numpy())
+        k_i = orc.dequant_e4m3(synth.u8(k8[b]), ks[b].cpu().numpy())
+        sc = orc.indexer(q_i, np32(w[b][tr]), k_i, pos, ld=L)
+        oi, kth = orc.topk(sc, pos, k_sel)
+        ok, _ = parity.topk_band_match(gi[b][rows], oi, sc, kth, pos)
+        assert ok == len(rows), (b, ok, len(rows))
+        same = np.array([np.array_equal(gi[b][r], oi[j]) for j, r in enumerate(rows)])
+        if same.any():
+            check_rows(orc, q[b], k[b], v[b], _rows_idx(oi, rows, n_q, k_sel), out[b], lse[b], rows[same],
+                       sm_scale, (b,))
+        n_cmp += int(same.sum())
+        n_rows += len(rows)
+    print(f"[forward masked MHA B={B} L={L} n_q={n_q} k_sel={k_sel}] rows {n_rows}: attention compared {n_cmp}")
+    assert n_cmp >= math.ceil(0.9 * n_rows), (n_cmp, n_rows)
+
+
+def _rows_idx(oi, rows, n_q, k_sel):
+    """An [n_q, k_sel] selection holding the oracle's own rows (other rows unused)."""
+    full = np.full((n_q, k_sel), -1, dtype=np.int32)
+    full[rows] = oi
+    return full
