@@ -694,29 +694,54 @@ __global__ __launch_bounds__(kTkThreads, 2) void topk_reg_kernel(const float* __
   unsigned int p_run = gt_before + min(eq_before, (unsigned int)k_rem);
   // [k] positions, then (candidate output) [k] keys; 2k <= kHistWords - 1: the last word is the dummy slot
   unsigned int* stage = hist;
-  // positions 256u + 64e + lane: row order is (u, e, lane), so one ballot per key vector ranks the keys
+  // Does this wave take any key equal to tau?  Only when it holds some and the waves before it have not
+  // used up the k_rem taken ones.  Usually not: then a key is selected exactly when it is above tau, and
+  // the loop below runs without the per-vector branch of the tie rule, so the compiler can overlap the
+  // ballot and store chains of neighbouring key vectors.
+  const bool eq_taken = __builtin_amdgcn_readfirstlane(misc[2 + kTkWaves + wave]) != 0u &&
+                        (unsigned int)__builtin_amdgcn_readfirstlane(eq_before) < (unsigned int)k_rem;
+  if (!eq_taken) {
 #pragma unroll
-  for (int u = 0; u < kRegBlocks; u++) {
-    if (u < nb) {
-      const int i = s0 + kSeg * u + lane;
+    for (int u = 0; u < kRegBlocks; u++) {
+      if (u < nb) {
+        const int i = s0 + kSeg * u + lane;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const bool v = i + 64 * e < s1;
-        bool sel = v && kr[u][e] > tau;
-        const bool eq = v && kr[u][e] == tau;
-        const unsigned long long be = __ballot(eq);
-        if (be != 0ull) {  // keys equal to tau: the first k_rem of them in row order
-          sel = sel || (eq && e_run + lanes_below(be) < (unsigned int)k_rem);
-          e_run += (unsigned int)__popcll(be);
+        for (int e = 0; e < 4; e++) {
+          const bool sel = i + 64 * e < s1 && kr[u][e] > tau;
+          const unsigned long long bs = __ballot(sel);
+          const unsigned int op = p_run + lanes_below(bs);
+          const bool st = sel && op < (unsigned int)k;
+          stage[st ? op : kHistWords - 1] = (unsigned int)(i + 64 * e);
+          if (DST == kDstCand) stage[st ? k + op : kHistWords - 1] = kr[u][e];
+          p_run += (unsigned int)__popcll(bs);
         }
-        const unsigned long long bs = __ballot(sel);
-        const unsigned int op = p_run + lanes_below(bs);
-        const bool st = sel && op < (unsigned int)k;
-        stage[st ? op : kHistWords - 1] = (unsigned int)(i + 64 * e);
-        if (DST == kDstCand) stage[st ? k + op : kHistWords - 1] = kr[u][e];
-        p_run += (unsigned int)__popcll(bs);
       }
     }
+  } else {
+    // positions 256u + 64e + lane: row order is (u, e, lane), so one ballot per key vector ranks the keys
+  #pragma unroll
+    for (int u = 0; u < kRegBlocks; u++) {
+      if (u < nb) {
+        const int i = s0 + kSeg * u + lane;
+  #pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const bool v = i + 64 * e < s1;
+          bool sel = v && kr[u][e] > tau;
+          const bool eq = v && kr[u][e] == tau;
+          const unsigned long long be = __ballot(eq);
+          if (be != 0ull) {  // keys equal to tau: the first k_rem of them in row order
+            sel = sel || (eq && e_run + lanes_below(be) < (unsigned int)k_rem);
+            e_run += (unsigned int)__popcll(be);
+          }
+          const unsigned long long bs = __ballot(sel);
+          const unsigned int op = p_run + lanes_below(bs);
+          const bool st = sel && op < (unsigned int)k;
+          stage[st ? op : kHistWords - 1] = (unsigned int)(i + 64 * e);
+          if (DST == kDstCand) stage[st ? k + op : kHistWords - 1] = kr[u][e];
+          p_run += (unsigned int)__popcll(bs);
+        }
+      }
+  }
   }
   __syncthreads();
   for (int j = tid; j < k; j += kTkThreads) {
